@@ -1,0 +1,264 @@
+"""Pins of the oracle's online-softmax attention (CPU only).
+
+What each test pins (method: "HiFA4: Training-Free 4-bit FlashAttention on
+Ascend HIF4 NPUs for LLM Inference", Abstract):
+  * exact mode (no quantisation) == textbook softmax attention, materialised in
+    numpy fp64, for causal / non-causal, GQA, ragged lengths, Sq != Sk, rows
+    with no visible key, and every key-tile width (so the online rescale is
+    pinned and P-frame bookkeeping cannot leak into the exact result);
+  * single key tile with MXFP4 P: closed form sum(P_hat V) / sum(P_hat) with a
+    block quantiser written here (P-Reordering: same P_hat in both sums);
+  * Smooth-QK: Q*s, K/s leaves exact attention unchanged (exact for powers of
+    two, to fp32 rounding otherwise);
+  * P-Reordering invariant: final key weights are >= 0, sum to 1, reproduce O,
+    and O lies in the per-channel hull of the visible V rows;
+  * the inconsistent normaliser scales each row coherently: O_naive =
+    O * l / l_naive, and l_naive is the plain sum of P;
+  * split-K + log-sum-exp merge == the unsplit result (exact mode) and == a
+    merge done here of separate per-chunk runs (MXFP4 mode);
+  * per-sequence lengths == slicing the cache; thread count does not change a
+    bit of the result; the row-subset mode returns the same rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def brute_attention(q, k, v, causal, sm_scale, kv_lens=None):
+    """softmax(Q K^T * sm_scale + mask) V, materialised, fp64."""
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    o = np.zeros_like(q)
+    lse = np.full((B, Hq, Sq), -np.inf)
+    for b in range(B):
+        L = Sk if kv_lens is None else int(kv_lens[b])
+        for h in range(Hq):
+            kk, vv = k[b, h // g, :L], v[b, h // g, :L]
+            s = q[b, h] @ kk.T * sm_scale
+            if causal:
+                i = np.arange(Sq)[:, None]
+                t = np.arange(L)[None, :]
+                s = np.where(t <= i + L - Sq, s, -np.inf)
+            for i in range(Sq):
+                row = s[i]
+                if not np.isfinite(row).any():
+                    continue
+                m = row.max()
+                p = np.exp(row - m)
+                o[b, h, i] = p @ vv / p.sum()
+                lse[b, h, i] = m + np.log(p.sum())
+    return o, lse
+
+
+def mx_quantize_rows_np(p):
+    """Block quantiser written for the test: 32 columns per block, aligned to 0."""
+    n, S = p.shape
+    nb = -(-S // 32)
+    pad = np.zeros((n, nb * 32))
+    pad[:, :S] = p
+    blk = pad.reshape(n, nb, 32)
+    amax = np.abs(blk).max(axis=-1, keepdims=True)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.where(amax > 0, np.clip(ex - 1 - 2, -127, 127), -127)
+    y = np.minimum(np.abs(blk) / np.exp2(e), 6.0)
+    dist = np.abs(y[..., None] - MAG)
+    best = dist.min(axis=-1, keepdims=True)
+    pref = np.where(dist == best, (np.arange(8) % 2) * 16 + np.arange(8), 99)
+    code = pref.argmin(axis=-1)
+    return (np.sign(blk) * MAG[code] * np.exp2(e)).reshape(n, nb * 32)[:, :S]
+
+
+CASES = [
+    # B, Hq, Hkv, Sq, Sk, d, causal
+    (1, 1, 1, 128, 128, 64, False),
+    (2, 4, 2, 70, 100, 32, True),
+    (1, 2, 1, 100, 40, 32, True),      # Sq > Sk: the first rows see no key
+    (1, 3, 3, 33, 161, 64, False),
+    (1, 2, 2, 1, 97, 32, True),        # decode-like
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("bc", [32, 64, 128, 4096])
+def test_exact_mode_equals_textbook_softmax(case, bc):
+    B, Hq, Hkv, Sq, Sk, d, causal = case
+    rng = np.random.default_rng(hash((case, bc)) % 2**32)
+    q = rng.standard_normal((B, Hq, Sq, d)) * 1.5
+    k = rng.standard_normal((B, Hkv, Sk, d))
+    v = rng.standard_normal((B, Hkv, Sk, d))
+    sm = 1.0 / np.sqrt(d)
+    r = oracle.attention(q, k, v, causal=causal, sm_scale=sm, bc=bc, quant_p=False)
+    o, lse = brute_attention(q, k, v, causal, sm)
+    np.testing.assert_allclose(r["o"], o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-12, atol=1e-12)
+    # the inconsistent normaliser coincides with the exact one without quantisation
+    np.testing.assert_allclose(r["o_naive"], o, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("Sk", [32, 75, 160])
+def test_single_tile_mxfp4_p_closed_form(Sk):
+    rng = np.random.default_rng(Sk)
+    Sq, d = 9, 64
+    q = rng.standard_normal((1, 1, Sq, d)) * 2
+    k = rng.standard_normal((1, 1, Sk, d))
+    v = rng.standard_normal((1, 1, Sk, d))
+    sm = 1.0 / np.sqrt(d)
+    r = oracle.attention(q, k, v, causal=False, sm_scale=sm, bc=4096, quant_p=True)
+    s = q[0, 0] @ k[0, 0].T * sm
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    ph = mx_quantize_rows_np(p)
+    o = ph @ v[0, 0] / ph.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(r["o"][0, 0], o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["l"][0, 0], ph.sum(axis=1), rtol=1e-13)
+    np.testing.assert_allclose(r["l_naive"][0, 0], p.sum(axis=1), rtol=1e-13)
+    np.testing.assert_allclose(r["lse"][0, 0], s.max(axis=1) + np.log(ph.sum(axis=1)), rtol=1e-13)
+    # P-Reordering is not the identity: quantisation changes the weights
+    assert np.abs(ph - p).max() > 1e-3
+
+
+@pytest.mark.parametrize("pow2", [True, False])
+def test_smooth_qk_invariance_exact(pow2):
+    rng = np.random.default_rng(5 + pow2)
+    B, Hq, Hkv, S, d = 1, 4, 2, 96, 64
+    q = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, S, d))
+    if pow2:
+        s = np.exp2(rng.integers(-4, 5, size=(Hkv, d))).astype(np.float32)
+    else:
+        s = np.exp(rng.uniform(-2, 2, size=(Hkv, d))).astype(np.float32)
+    _, _, qs = oracle.quantize_rows(q, s, divide=False, quantise=False)
+    _, _, ks = oracle.quantize_rows(k, s, divide=True, quantise=False)
+    r1 = oracle.attention(qs, ks, v, causal=True, bc=64, quant_p=False)
+    r0 = oracle.attention(q.astype(np.float64), k.astype(np.float64), v, causal=True, bc=64,
+                          quant_p=False)
+    tol = 1e-12 if pow2 else 2e-5
+    np.testing.assert_allclose(r1["o"], r0["o"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(r1["lse"], r0["lse"], rtol=tol, atol=tol)
+
+
+def _quantised_case(seed, B=1, Hq=2, Hkv=1, Sq=150, Sk=150, d=64, outliers=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, Sq, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, Sk, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, Sk, d)).astype(np.float32)
+    if outliers:
+        k[..., [3, 17]] *= 8
+    return oracle.quantize_qkv(q, k, v, None)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("bc", [32, 64])
+def test_p_reordering_convex_weights(causal, bc):
+    qq = _quantised_case(1)
+    r = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=bc,
+                         quant_p=True, want_weights=True)
+    w = r["w"]                                   # [B,Hq,Sq,Sk]
+    vd = qq["v_deq"]
+    Sq, Sk = w.shape[2], w.shape[3]
+    assert (w >= 0).all()
+    np.testing.assert_allclose(w.sum(-1), 1.0, rtol=0, atol=1e-12)
+    if causal:
+        vis = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None] + Sk - Sq
+        assert (w[..., ~vis] == 0).all()
+    o = np.einsum("bhqk,bkd->bhqd", w, vd[:, 0])
+    np.testing.assert_allclose(r["o"], o, rtol=1e-12, atol=1e-12)
+    for i in range(Sq):
+        nv = (i + 1) if causal else Sk
+        lo = vd[0, 0, :nv].min(axis=0)
+        hi = vd[0, 0, :nv].max(axis=0)
+        assert (r["o"][0, :, i] >= lo - 1e-12).all() and (r["o"][0, :, i] <= hi + 1e-12).all()
+
+
+def test_inconsistent_normaliser_is_coherent_row_scaling():
+    qq = _quantised_case(2, Sq=200, Sk=200)
+    r = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=64, quant_p=True)
+    np.testing.assert_allclose(r["o_naive"], r["o"] * (r["l"] / r["l_naive"])[..., None],
+                               rtol=1e-12, atol=1e-13)
+    # the scaling is not trivially 1
+    assert np.abs(r["l"] / r["l_naive"] - 1).max() > 1e-3
+
+
+def test_epsilon_bar_sign_on_synthetic_scores():
+    """Expected sign of the per-tile mismatch (net probability-mass loss).
+
+    The pages report that every measured tile of a real trace loses mass under
+    the inconsistent normaliser, median -0.064 (Abstract); that value needs the
+    trace and is unpinned here.  On N(0,1) data the sign must agree.
+    """
+    rng = np.random.default_rng(9)
+    B, H, S, d = 1, 2, 512, 128
+    q = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, S, d)).astype(np.float32)
+    qq = oracle.quantize_qkv(q, k, v, None)
+    r = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=64, br=128,
+                         quant_p=True, want_eps=True)
+    eps = r["eps_tile_mean"]
+    eps = eps[np.isfinite(eps)]
+    assert eps.size >= 40          # 2 heads x 20 causal (128-row x 64-key) tiles
+    assert (eps < 0).mean() > 0.9
+    assert -0.2 < np.median(eps) < 0
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 192])
+def test_split_k_exact_equals_unsplit(chunk):
+    rng = np.random.default_rng(chunk)
+    q = rng.standard_normal((2, 4, 1, 64))
+    k = rng.standard_normal((2, 2, 500, 64))
+    v = rng.standard_normal((2, 2, 500, 64))
+    lens = np.array([500, 333], dtype=np.int32)
+    a = oracle.attention(q, k, v, causal=True, bc=64, chunk=chunk, quant_p=False, kv_lens=lens)
+    b = oracle.attention(q, k, v, causal=True, bc=64, chunk=0, quant_p=False, kv_lens=lens)
+    np.testing.assert_allclose(a["o"], b["o"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(a["lse"], b["lse"], rtol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_split_k_mxfp4_equals_merge_of_chunk_runs(chunk):
+    qq = _quantised_case(4, B=1, Hq=4, Hkv=2, Sq=1, Sk=300)
+    q, k, v = qq["q_deq"], qq["k_deq"], qq["v_deq"]
+    a = oracle.attention(q, k, v, causal=False, bc=64, chunk=chunk, quant_p=True)
+    lses, outs = [], []
+    for c0 in range(0, 300, chunk):
+        c1 = min(300, c0 + chunk)
+        r = oracle.attention(q, k[:, :, c0:c1], v[:, :, c0:c1], causal=False, bc=64, quant_p=True)
+        lses.append(r["lse"])
+        outs.append(r["o"])
+    lse = np.logaddexp.reduce(np.stack(lses), axis=0)
+    o = sum(np.exp(l - lse)[..., None] * oc for l, oc in zip(lses, outs))
+    np.testing.assert_allclose(a["o"], o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(a["lse"], lse, rtol=1e-12)
+    # and splitting does change P_hat (the chunk frame), so it is a real parameter
+    un = oracle.attention(q, k, v, causal=False, bc=64, chunk=0, quant_p=True)
+    assert np.abs(un["o"] - a["o"]).max() > 0
+
+
+def test_kv_lens_equals_sliced_cache():
+    qq = _quantised_case(6, B=2, Hq=4, Hkv=2, Sq=3, Sk=260)
+    q, k, v = qq["q_deq"], qq["k_deq"], qq["v_deq"]
+    lens = np.array([260, 101], dtype=np.int32)
+    a = oracle.attention(q, k, v, causal=True, bc=64, chunk=128, quant_p=True, kv_lens=lens)
+    for b in range(2):
+        L = lens[b]
+        r = oracle.attention(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L], causal=True, bc=64,
+                             chunk=128, quant_p=True)
+        np.testing.assert_array_equal(a["o"][b], r["o"][0])
+        np.testing.assert_array_equal(a["lse"][b], r["lse"][0])
+
+
+def test_threads_and_row_subset_are_bitwise_stable():
+    qq = _quantised_case(8, B=1, Hq=4, Hkv=2, Sq=260, Sk=260)
+    q, k, v = qq["q_deq"], qq["k_deq"], qq["v_deq"]
+    a = oracle.attention(q, k, v, causal=True, bc=64, quant_p=True, nthreads=1)
+    b = oracle.attention(q, k, v, causal=True, bc=64, quant_p=True, nthreads=8)
+    for key in ("o", "lse", "o_naive", "l", "l_naive"):
+        np.testing.assert_array_equal(a[key], b[key])
+    rows = np.array([0, 5, 259, 260 + 77, 3 * 260 + 130])
+    c = oracle.attention(q, k, v, causal=True, bc=64, quant_p=True, rows=rows)
+    np.testing.assert_array_equal(c["o"], a["o"].reshape(-1, 64)[rows])
+    np.testing.assert_array_equal(c["lse"], a["lse"].reshape(-1)[rows])

@@ -1,0 +1,103 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each mutant is a copy of the oracle's C source with one planted mistake (a
+dropped term, a wrong sign, a swapped operand or index, a wrong constant),
+compiled with gcc into a temporary library.  The pin tests are then re-run
+against that library; at least one of them must fail.  Nothing here touches
+the HIP path.
+"""
+import os
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_attention as TA
+from tests import test_oracle_quant as TQ
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "hifa4_oracle.c")
+
+# (name, original text, planted text, occurrence index)
+MUTANTS = [
+    ("tie_to_odd_code", "c = (i % 2u == 0u) ? i : i + 1;", "c = (i % 2u == 0u) ? i + 1 : i;", 0),
+    ("scale_exponent_off_by_one", "e = ex - 1 - 2;", "e = ex - 2;", 0),
+    ("negative_zero_loses_sign", "unsigned sign = signbit(y) ? 8u : 0u;",
+     "unsigned sign = (y < 0) ? 8u : 0u;", 0),
+    ("smooth_direction_swapped", "v = divide ? v / s[j] : v * s[j];",
+     "v = divide ? v * s[j] : v / s[j];", 0),
+    ("qk_nibble_order_swapped", "(unsigned char)(blk[k] | (blk[k + 1] << 4))",
+     "(unsigned char)(blk[k + 1] | (blk[k] << 4))", 0),
+    ("v_nibble_order_swapped", "(unsigned char)(blk[k] | (blk[k + 1] << 4))",
+     "(unsigned char)(blk[k + 1] | (blk[k] << 4))", 1),
+    ("v_block_transposed", "codes[(blkrow * d + c) * 16 + k / 2]",
+     "codes[(blkrow * 16 + k / 2) * d + c]", 0),
+    ("alpha_sign_flipped", "double alpha = exp(m - m_new);", "double alpha = exp(m_new - m);", 0),
+    ("normaliser_from_unquantised_p", "l = alpha * l + sumPh;", "l = alpha * l + sumP;", 0),
+    ("numerator_from_unquantised_p", "double p = Ph[u];", "double p = P[u];", 0),
+    ("causal_not_bottom_right", "(long)i + L - c->Sq < last) last = (long)i + L - c->Sq;",
+     "(long)i < last) last = (long)i;", 0),
+    ("gqa_head_map_modulo", "const int g = h / (c->Hq / c->Hkv);", "const int g = h % c->Hkv;", 0),
+    ("p_not_quantised", "if (c->quant_p) {", "if (0) {", 0),
+    ("rescale_dropped", "for (int j = 0; j < d; j++) acc_c[j] *= alpha;", "", 0),
+    ("merge_weight_dropped", "lsum = a_old * lsum + a_new * l;", "lsum = a_old * lsum + l;", 0),
+    ("sm_scale_dropped", "s *= c->sm_scale;", "s *= 1.0;", 0),
+    ("lse_from_naive_sum", "J->lse[out] = M + log(lsum);", "J->lse[out] = M + log(lnsum);", 0),
+    ("p_block_misaligned", "for (long a0 = t0 - (t0 % 32); a0 < t1; a0 += 32)",
+     "for (long a0 = t0 - (t0 % 32) - 16; a0 < t1; a0 += 32)", 0),
+    ("v_tail_amax_over_padding", "col[k] = k < n ? (double)xh[(size_t)(t0 + k) * d + c] : 0.0;",
+     "col[k] = (double)xh[(size_t)((t0 + k) % S) * d + c];", 0),
+    ("dot_product_drops_last_channel", "for (int j = 0; j < d; j++) s += qr[j] * kr[j];",
+     "for (int j = 0; j < d - 1; j++) s += qr[j] * kr[j];", 0),
+]
+
+
+def _pin_checks():
+    """The pin tests, as plain callables (each raises on failure)."""
+    checks = [
+        TQ.test_e2m1_golden,
+        TQ.test_e2m1_sweep_against_brute_force,
+        TQ.test_quantize_rows_layout_and_smooth_direction,
+        TQ.test_quantize_v_layout_tail_block,
+        TQ.test_mx_block_idempotent_and_on_grid_round_trip,
+    ]
+    for name, x, sc, codes in TQ._golden_blocks():
+        checks.append(lambda x=x, sc=sc, codes=codes, name=name: TQ.test_mx_block_golden(name, x, sc, codes))
+    for case in TA.CASES:
+        checks.append(lambda case=case: TA.test_exact_mode_equals_textbook_softmax(case, 64))
+    checks += [
+        lambda: TA.test_single_tile_mxfp4_p_closed_form(75),
+        lambda: TA.test_smooth_qk_invariance_exact(True),
+        lambda: TA.test_p_reordering_convex_weights(True, 64),
+        TA.test_inconsistent_normaliser_is_coherent_row_scaling,
+        lambda: TA.test_split_k_mxfp4_equals_merge_of_chunk_runs(64),
+        lambda: TA.test_split_k_exact_equals_unsplit(128),
+    ]
+    return checks
+
+
+def test_unmutated_oracle_passes_every_check():
+    for chk in _pin_checks():
+        chk()
+
+
+@pytest.mark.parametrize("name,orig,planted,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, orig, planted, occ, tmp_path):
+    src = open(SRC).read()
+    pos = -1
+    for _ in range(occ + 1):
+        pos = src.index(orig, pos + 1)
+    mutated = src[:pos] + planted + src[pos + len(orig):]
+    assert mutated != src
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(mutated)
+    lib = oracle.build(str(msrc), str(tmp_path / "libmutant.so"))
+    caught = []
+    with oracle.use_library(lib), np.errstate(all="ignore"):
+        for chk in _pin_checks():
+            try:
+                chk()
+            except (AssertionError, ValueError, FloatingPointError) as e:  # noqa: PERF203
+                caught.append(type(e).__name__)
+                break
+    assert caught, "planted mistake %r passed every pin" % name
