@@ -1,0 +1,252 @@
+"""ctypes binding of libhifa4.so (C ABI: include/hifa4.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind these calls.  PyTorch supplies device memory (the caller's
+tensors, or ``torch.empty`` for outputs the caller did not pass) and the
+current HIP stream.  There is no CPU fallback: if the library is missing or
+the tensors are not on the GPU, the calls raise.
+
+The Python names match the C entry points: ``hifa4_quantize_qkv``,
+``hifa4_attn_fwd``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
+``hifa4_attn_workspace_size``, ``hifa4_status_string``, ``hifa4_last_error``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhifa4.so")
+
+HIFA4_OK = 0
+HIFA4_ERR_INVALID_ARGUMENT = -1
+HIFA4_ERR_UNSUPPORTED = -2
+HIFA4_ERR_WORKSPACE_TOO_SMALL = -3
+HIFA4_ERR_HIP = -4
+HIFA4_BF16 = 0
+HIFA4_FP16 = 1
+
+
+class HiFA4Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s (%d): %s" % (hifa4_status_string(status), status, detail))
+        self.status = status
+
+
+class MxTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class AttnParamsC(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("kv_stride", ctypes.c_int32), ("kv_lens", ctypes.c_void_p),
+        ("decode_chunk", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Open libhifa4.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libhifa4.so is not built (%s). Build it with `python -m "
+            "bit_flashattention_hifa4_amd.build`; there is no CPU fallback." % path)
+    lib = ctypes.CDLL(path)
+    st = ctypes.c_int
+    vp = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.hifa4_quantize_qkv.restype = st
+    lib.hifa4_quantize_qkv.argtypes = [vp, vp, vp, st, i32, i32, i32, i32, i32, i32, i32, vp,
+                                       MxTensorC, MxTensorC, MxTensorC, vp]
+    lib.hifa4_attn_workspace_size.restype = ctypes.c_size_t
+    lib.hifa4_attn_workspace_size.argtypes = [ctypes.POINTER(AttnParamsC)]
+    lib.hifa4_attn_fwd.restype = st
+    lib.hifa4_attn_fwd.argtypes = [ctypes.POINTER(AttnParamsC), MxTensorC, MxTensorC, MxTensorC,
+                                   vp, st, vp, vp, ctypes.c_size_t, vp]
+    lib.bf16_attn_fwd.restype = st
+    lib.bf16_attn_fwd.argtypes = [ctypes.POINTER(AttnParamsC), vp, vp, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
+    lib.hifa4_attn_schedule.restype = st
+    lib.hifa4_attn_schedule.argtypes = [ctypes.POINTER(AttnParamsC), ctypes.POINTER(i32),
+                                        ctypes.POINTER(i32)]
+    lib.hifa4_status_string.restype = ctypes.c_char_p
+    lib.hifa4_status_string.argtypes = [st]
+    lib.hifa4_last_error.restype = ctypes.c_char_p
+    lib.hifa4_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def hifa4_status_string(status: int) -> str:
+    return load_library().hifa4_status_string(int(status)).decode()
+
+
+def hifa4_last_error() -> str:
+    return load_library().hifa4_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != HIFA4_OK:
+        raise HiFA4Error(status, hifa4_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return HIFA4_BF16
+    if dt == torch.float16:
+        return HIFA4_FP16
+    raise ValueError("dtype must be bfloat16 or float16, got %s" % dt)
+
+
+@dataclasses.dataclass
+class MXQKV:
+    """Quantised operands in the library's layouts (see include/hifa4.h)."""
+    q_codes: Optional[torch.Tensor]
+    q_scales: Optional[torch.Tensor]
+    k_codes: Optional[torch.Tensor]
+    k_scales: Optional[torch.Tensor]
+    v_codes: Optional[torch.Tensor]
+    v_scales: Optional[torch.Tensor]
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    d: int
+    kv_stride: int
+
+
+def alloc_mx(B, Hq, Hkv, Sq, kv_stride, d, device="cuda") -> MXQKV:
+    """Output buffers of hifa4_quantize_qkv (uninitialised device memory)."""
+    nblk = (kv_stride + 31) // 32
+    u8 = dict(dtype=torch.uint8, device=device)
+    return MXQKV(torch.empty((B, Hq, Sq, d // 2), **u8), torch.empty((B, Hq, Sq, d // 32), **u8),
+                 torch.empty((B, Hkv, kv_stride, d // 2), **u8),
+                 torch.empty((B, Hkv, kv_stride, d // 32), **u8),
+                 torch.empty((B, Hkv, nblk, d, 16), **u8), torch.empty((B, Hkv, nblk, d), **u8),
+                 B, Hq, Hkv, Sq, 0, d, kv_stride)
+
+
+def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
+                       v: Optional[torch.Tensor], smooth: Optional[torch.Tensor] = None, *,
+                       kv_stride: int = 0, out: Optional[MXQKV] = None, stream=None) -> MXQKV:
+    """Smooth-QK + MXFP4 quantisation; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] bf16 or fp16 on the GPU."""
+    ref = next(t for t in (q, k, v) if t is not None)
+    B, d = ref.shape[0], ref.shape[3]
+    Hq, Sq = (q.shape[1], q.shape[2]) if q is not None else (1, 0)
+    kk = k if k is not None else v
+    Hkv, Sk = (kk.shape[1], kk.shape[2]) if kk is not None else (Hq, 0)
+    if q is None:
+        Hq = Hkv
+    for t in (q, k, v):
+        if t is not None and (t.dim() != 4 or t.dtype != ref.dtype):
+            raise ValueError("q/k/v must be 4-d tensors of one dtype")
+    cap = kv_stride or Sk
+    if out is None:
+        out = alloc_mx(B, Hq, Hkv, Sq, cap, d, device=ref.device)
+    out.Sk, out.Sq, out.kv_stride = Sk, Sq, cap
+    if smooth is not None and (smooth.dtype != torch.float32 or tuple(smooth.shape) != (Hkv, d)):
+        raise ValueError("smooth must be float32 [Hkv, d]")
+    lib = load_library()
+    mq = MxTensorC(_ptr(out.q_codes) if q is not None else None,
+                   _ptr(out.q_scales) if q is not None else None)
+    mk = MxTensorC(_ptr(out.k_codes) if k is not None else None,
+                   _ptr(out.k_scales) if k is not None else None)
+    mv = MxTensorC(_ptr(out.v_codes) if v is not None else None,
+                   _ptr(out.v_scales) if v is not None else None)
+    _check(lib.hifa4_quantize_qkv(_ptr(q), _ptr(k), _ptr(v), _dtype_code(ref.dtype), B, Hq, Hkv,
+                                  Sq, Sk, kv_stride, d, _ptr(smooth), mq, mk, mv,
+                                  _stream(stream)))
+    return out
+
+
+def make_params(B, Hq, Hkv, Sq, Sk, d, *, causal, sm_scale=None, kv_stride=0, kv_lens=None,
+                decode_chunk=0) -> AttnParamsC:
+    return AttnParamsC(B, Hq, Hkv, Sq, Sk, d, 1 if causal else 0,
+                       float(sm_scale) if sm_scale else 0.0, kv_stride,
+                       _ptr(kv_lens) if kv_lens is not None else None, decode_chunk)
+
+
+def hifa4_attn_workspace_size(params: AttnParamsC) -> int:
+    return int(load_library().hifa4_attn_workspace_size(ctypes.byref(params)))
+
+
+def hifa4_attn_schedule(params: AttnParamsC) -> tuple[int, int]:
+    bn, ch = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().hifa4_attn_schedule(ctypes.byref(params), ctypes.byref(bn),
+                                              ctypes.byref(ch)))
+    return bn.value, ch.value
+
+
+def hifa4_attn_fwd(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,
+                   kv_lens: Optional[torch.Tensor] = None, decode_chunk: int = 0,
+                   out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Fused MXFP4 attention on quantised operands; returns (out, lse or None)."""
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != mx.B):
+        raise ValueError("kv_lens must be int32 [B]")
+    p = make_params(mx.B, mx.Hq, mx.Hkv, mx.Sq, mx.Sk, mx.d, causal=causal, sm_scale=sm_scale,
+                    kv_stride=mx.kv_stride, kv_lens=kv_lens, decode_chunk=decode_chunk)
+    dev = mx.q_codes.device
+    if out is None:
+        out = torch.empty((mx.B, mx.Hq, mx.Sq, mx.d), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((mx.B, mx.Hq, mx.Sq), dtype=torch.float32, device=dev)
+    need = hifa4_attn_workspace_size(p)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    lib = load_library()
+    _check(lib.hifa4_attn_fwd(ctypes.byref(p), MxTensorC(_ptr(mx.q_codes), _ptr(mx.q_scales)),
+                              MxTensorC(_ptr(mx.k_codes), _ptr(mx.k_scales)),
+                              MxTensorC(_ptr(mx.v_codes), _ptr(mx.v_scales)), _ptr(out),
+                              _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
+                              workspace.numel() if workspace is not None else 0,
+                              _stream(stream)))
+    return out, lse
+
+
+def bf16_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool,
+                  sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """bf16 FlashAttention baseline; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] bf16; returns (out, lse)."""
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("bf16_attn_fwd takes bfloat16 tensors")
+    p = make_params(B, Hq, Hkv, Sq, Sk, d, causal=causal, sm_scale=sm_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check(load_library().bf16_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(lse), None, 0, _stream(stream)))
+    return out, lse

@@ -1,0 +1,345 @@
+// api.cpp -- the C ABI declared in include/hifa4.h: argument validation,
+// problem set-up and kernel dispatch.  Nothing is enqueued unless every
+// argument has been checked; no device memory is ever allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "hifa4.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hifa4_status fail(hifa4_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hifa4_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return HIFA4_OK;
+  return fail(HIFA4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const char* name;
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  auto alo = reinterpret_cast<uintptr_t>(a.p), blo = reinterpret_cast<uintptr_t>(b.p);
+  return alo < blo + (uintptr_t)b.bytes && blo < alo + (uintptr_t)a.bytes;
+}
+
+// Every output must be disjoint from every input and from every other output.
+hifa4_status check_disjoint(const Span* in, int n_in, const Span* out, int n_out) {
+  for (int i = 0; i < n_out; i++) {
+    for (int j = 0; j < n_in; j++)
+      if (overlaps(out[i], in[j]))
+        return fail(HIFA4_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", out[i].name,
+                    in[j].name);
+    for (int j = i + 1; j < n_out; j++)
+      if (overlaps(out[i], out[j]))
+        return fail(HIFA4_ERR_INVALID_ARGUMENT, "outputs %s and %s overlap", out[i].name,
+                    out[j].name);
+  }
+  return HIFA4_OK;
+}
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+int64_t row_codes_bytes(int64_t rows, int d) { return rows * (d / 2); }
+int64_t row_scales_bytes(int64_t rows, int d) { return rows * (d / 32); }
+int64_t col_blocks(int64_t heads, int cap) { return heads * ((cap + 31) / 32); }
+
+// Shared validation of the attention parameter block.
+hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
+  if (!p) return fail(HIFA4_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->B < 0 || p->Sq < 0 || p->Sk < 0 || p->kv_stride < 0)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Sk=%d kv_stride=%d)", p->B,
+                p->Sq, p->Sk, p->kv_stride);
+  if (p->Hq <= 0 || p->Hkv <= 0 || p->Hq % p->Hkv != 0)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                p->Hq, p->Hkv);
+  if (!supported_d(p->d)) return fail(HIFA4_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128, 256)", p->d);
+  if (!std::isfinite(p->sm_scale))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
+  *cap = p->kv_stride ? p->kv_stride : p->Sk;
+  if (*cap < p->Sk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_stride %d < Sk %d", *cap, p->Sk);
+  if (p->kv_lens && p->Sq != 1)
+    return fail(HIFA4_ERR_UNSUPPORTED, "kv_lens is only supported with Sq == 1 (decode)");
+  *chunk = 0;
+  if (p->Sq == 1) {
+    const int bn = hifa4::attn_block_n(p->d);
+    int c = p->decode_chunk ? p->decode_chunk : hifa4::attn_default_chunk(p->d);
+    if (c <= 0 || c % bn)
+      return fail(HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk %d is not a positive multiple of %d",
+                  p->decode_chunk, bn);
+    *chunk = c;
+  } else if (p->decode_chunk) {
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk is only meaningful with Sq == 1");
+  }
+  return HIFA4_OK;
+}
+
+size_t decode_workspace(const hifa4_attn_params* p, int cap, int chunk) {
+  if (p->Sq != 1 || chunk <= 0) return 0;
+  const int64_t n_chunks = (cap + chunk - 1) / chunk;
+  return (size_t)p->B * p->Hq * n_chunks * (p->d + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hifa4_status_string(hifa4_status s) {
+  switch (s) {
+    case HIFA4_OK: return "ok";
+    case HIFA4_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HIFA4_ERR_UNSUPPORTED: return "unsupported";
+    case HIFA4_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case HIFA4_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* hifa4_last_error(void) { return g_last_error.c_str(); }
+
+hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const void* v, hifa4_dtype in_dtype,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Sk,
+                                int32_t kv_stride, int32_t d, const float* smooth,
+                                hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
+                                hifa4_mx_tensor v_out, void* stream) {
+  g_last_error.clear();
+  if (in_dtype != HIFA4_BF16 && in_dtype != HIFA4_FP16)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "in_dtype %d", (int)in_dtype);
+  if (B < 0 || Sq < 0 || Sk < 0 || kv_stride < 0)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "negative size");
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
+  if (!supported_d(d)) return fail(HIFA4_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128, 256)", d);
+  const int cap = kv_stride ? kv_stride : Sk;
+  if (cap < Sk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_stride %d < Sk %d", cap, Sk);
+  if (!q && !k && !v) return fail(HIFA4_ERR_INVALID_ARGUMENT, "q, k and v are all NULL");
+  struct Req {
+    const char* name;
+    const void* p;
+  };
+  const Req req[] = {{"q", q},           {"q_out.codes", q ? q_out.codes : nullptr},
+                     {"q_out.scales", q ? q_out.scales : nullptr},
+                     {"k", k},           {"k_out.codes", k ? k_out.codes : nullptr},
+                     {"k_out.scales", k ? k_out.scales : nullptr},
+                     {"v", v},           {"v_out.codes", v ? v_out.codes : nullptr},
+                     {"v_out.scales", v ? v_out.scales : nullptr},
+                     {"smooth", smooth}};
+  for (const Req& r : req)
+    if (r.p && !aligned16(r.p))
+      return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", r.name);
+  if (q && (!q_out.codes || !q_out.scales))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "q given but q_out has a NULL buffer");
+  if (k && (!k_out.codes || !k_out.scales))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "k given but k_out has a NULL buffer");
+  if (v && (!v_out.codes || !v_out.scales))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "v given but v_out has a NULL buffer");
+
+  const int64_t rq = (int64_t)B * Hq * Sq, rk = (int64_t)B * Hkv * Sk;
+  const int64_t rcap = (int64_t)B * Hkv * cap;
+  const Span in[] = {{"q", q, rq * d * 2}, {"k", k, rk * d * 2}, {"v", v, rk * d * 2},
+                     {"smooth", smooth, smooth ? (int64_t)Hkv * d * 4 : 0}};
+  const Span out[] = {
+      {"q_out.codes", q ? q_out.codes : nullptr, row_codes_bytes(rq, d)},
+      {"q_out.scales", q ? q_out.scales : nullptr, row_scales_bytes(rq, d)},
+      {"k_out.codes", k ? k_out.codes : nullptr, row_codes_bytes(rcap, d)},
+      {"k_out.scales", k ? k_out.scales : nullptr, row_scales_bytes(rcap, d)},
+      {"v_out.codes", v ? v_out.codes : nullptr, col_blocks((int64_t)B * Hkv, cap) * d * 16},
+      {"v_out.scales", v ? v_out.scales : nullptr, col_blocks((int64_t)B * Hkv, cap) * d}};
+  hifa4_status st = check_disjoint(in, 4, out, 6);
+  if (st != HIFA4_OK) return st;
+
+  hifa4::QuantizeArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.smooth = smooth;
+  a.q_codes = q_out.codes;
+  a.q_scales = q_out.scales;
+  a.k_codes = k_out.codes;
+  a.k_scales = k_out.scales;
+  a.v_codes = v_out.codes;
+  a.v_scales = v_out.scales;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.d = d;
+  a.cap = cap;
+  a.blocks_q = q ? rq * (d / 32) : 0;
+  a.blocks_k = k ? rk * (d / 32) : 0;
+  if (!q || rq == 0) a.q = nullptr;
+  if (!k || rk == 0) a.k = nullptr;
+  if (!v || rk == 0) a.v = nullptr;
+  return hip_status(hifa4::launch_quantize_qkv(a, in_dtype == HIFA4_BF16, (hipStream_t)stream),
+                    "quantize launch");
+}
+
+size_t hifa4_attn_workspace_size(const hifa4_attn_params* p) {
+  int cap, chunk;
+  const std::string saved = g_last_error;
+  if (check_params(p, &cap, &chunk) != HIFA4_OK) {
+    g_last_error = saved;
+    return 0;
+  }
+  return decode_workspace(p, cap, chunk);
+}
+
+hifa4_status hifa4_attn_schedule(const hifa4_attn_params* p, int32_t* block_n,
+                                 int32_t* chunk_tokens) {
+  g_last_error.clear();
+  int cap, chunk;
+  hifa4_status st = check_params(p, &cap, &chunk);
+  if (st != HIFA4_OK) return st;
+  if (block_n) *block_n = hifa4::attn_block_n(p->d);
+  if (chunk_tokens) *chunk_tokens = chunk;
+  return HIFA4_OK;
+}
+
+hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4_mx_tensor k,
+                            hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int cap, chunk;
+  hifa4_status st = check_params(p, &cap, &chunk);
+  if (st != HIFA4_OK) return st;
+  if (out_dtype != HIFA4_BF16 && out_dtype != HIFA4_FP16)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "out_dtype %d", (int)out_dtype);
+  const int d = p->d;
+  const int64_t rq = (int64_t)p->B * p->Hq * p->Sq;
+  const int64_t rcap = (int64_t)p->B * p->Hkv * cap;
+  if (rq == 0) return HIFA4_OK;
+  const void* ptrs[] = {q.codes, q.scales, k.codes, k.scales, v.codes, v.scales, out};
+  const char* names[] = {"q.codes", "q.scales", "k.codes", "k.scales", "v.codes", "v.scales", "out"};
+  for (int i = 0; i < 7; i++) {
+    if (!ptrs[i]) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  if (lse && !aligned16(lse)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
+  if (p->kv_lens && !aligned16(p->kv_lens))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_lens is not 16-byte aligned");
+  const size_t need = decode_workspace(p, cap, chunk);
+  if (workspace_bytes < need)
+    return fail(HIFA4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
+                need);
+  if (need && !workspace) return fail(HIFA4_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (need && !aligned16(workspace))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+  const Span in[] = {{"q.codes", q.codes, row_codes_bytes(rq, d)},
+                     {"q.scales", q.scales, row_scales_bytes(rq, d)},
+                     {"k.codes", k.codes, row_codes_bytes(rcap, d)},
+                     {"k.scales", k.scales, row_scales_bytes(rcap, d)},
+                     {"v.codes", v.codes, col_blocks((int64_t)p->B * p->Hkv, cap) * d * 16},
+                     {"v.scales", v.scales, col_blocks((int64_t)p->B * p->Hkv, cap) * d},
+                     {"kv_lens", p->kv_lens, p->kv_lens ? (int64_t)p->B * 4 : 0}};
+  const Span outs[] = {{"out", out, rq * d * 2},
+                       {"lse", lse, lse ? rq * 4 : 0},
+                       {"workspace", workspace, (int64_t)need}};
+  st = check_disjoint(in, 7, outs, 3);
+  if (st != HIFA4_OK) return st;
+
+  hifa4::AttnArgs a = {};
+  a.q_codes = q.codes;
+  a.q_scales = q.scales;
+  a.k_codes = k.codes;
+  a.k_scales = k.scales;
+  a.v_codes = v.codes;
+  a.v_scales = v.scales;
+  a.out = out;
+  a.lse = lse;
+  a.kv_lens = p->kv_lens;
+  a.partials = static_cast<float*>(workspace);
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.Sq = p->Sq;
+  a.Sk = p->Sk;
+  a.d = d;
+  a.cap = cap;
+  a.causal = p->causal ? 1 : 0;
+  a.out_fp16 = out_dtype == HIFA4_FP16;
+  a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)d);
+  a.sm_log2 = a.sm_scale * 1.4426950408889634f;
+  a.chunk = chunk;
+  a.n_chunks = chunk ? (cap + chunk - 1) / chunk : 0;
+  hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
+                            : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported)
+    return fail(HIFA4_ERR_UNSUPPORTED, "no kernel for this configuration");
+  return hip_status(e, "attention launch");
+}
+
+hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void* k,
+                           const void* v, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_last_error.clear();
+  int cap, chunk;
+  if (p && p->kv_lens) return fail(HIFA4_ERR_UNSUPPORTED, "bf16_attn_fwd takes no kv_lens");
+  if (p && p->decode_chunk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "bf16_attn_fwd takes no decode_chunk");
+  hifa4_attn_params pp;
+  if (p) {
+    pp = *p;
+    pp.Sq = pp.Sq == 1 ? 2 : pp.Sq;  // the bf16 path has no split-K variant; validate as prefill
+  }
+  hifa4_status st = check_params(p ? &pp : nullptr, &cap, &chunk);
+  if (st != HIFA4_OK) return st;
+  const int d = p->d;
+  const int64_t rq = (int64_t)p->B * p->Hq * p->Sq;
+  const int64_t rcap = (int64_t)p->B * p->Hkv * cap;
+  if (rq == 0) return HIFA4_OK;
+  const void* ptrs[] = {q, k, v, out};
+  const char* names[] = {"q", "k", "v", "out"};
+  for (int i = 0; i < 4; i++) {
+    if (!ptrs[i]) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  if (lse && !aligned16(lse)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
+  const Span in[] = {{"q", q, rq * d * 2}, {"k", k, rcap * d * 2}, {"v", v, rcap * d * 2}};
+  const Span outs[] = {{"out", out, rq * d * 2}, {"lse", lse, lse ? rq * 4 : 0}};
+  st = check_disjoint(in, 3, outs, 2);
+  if (st != HIFA4_OK) return st;
+  hifa4::Bf16AttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.Sq = p->Sq;
+  a.Sk = p->Sk;
+  a.d = d;
+  a.cap = cap;
+  a.causal = p->causal ? 1 : 0;
+  const float sm = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)d);
+  a.sm_log2 = sm * 1.4426950408889634f;
+  hipError_t e = hifa4::launch_attn_prefill_bf16(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(HIFA4_ERR_UNSUPPORTED, "no kernel for this configuration");
+  return hip_status(e, "bf16 attention launch");
+}
+
+}  // extern "C"

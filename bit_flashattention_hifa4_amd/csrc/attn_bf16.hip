@@ -1,0 +1,222 @@
+// attn_bf16.hip -- bf16 FlashAttention forward for gfx950: the accuracy and
+// latency baseline ("HiFA4: Training-Free 4-bit FlashAttention on Ascend HIF4
+// NPUs for LLM Inference", Abstract, compares the 4-bit operator against bf16
+// FlashAttention).  bf16 MFMA products, fp32 online softmax, the normaliser
+// summed on the vector ALU from the unrounded P.
+//
+// Same skeleton as the MXFP4 kernel: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
+// with the K rows loaded in a permuted order so that each lane's accumulator
+// registers already hold the keys of its P V operand (K = 16 keys per MFMA:
+// lane (q, h) needs keys 16u + 8h .. + 7 of MFMA u).  V is staged in LDS
+// transposed (channel-major) so its A operand is one 16-byte LDS read.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace hifa4 {
+namespace {
+
+constexpr int kBN = 64;
+constexpr int kBR = 128;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Key (within the 64-key step) loaded as A row m of 32-key tile t.
+__device__ __forceinline__ int perm_row_bf16(int t, int m) {
+  const int j = m >> 3, hh = (m >> 2) & 1, i = m & 3;
+  return 32 * t + 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
+}
+
+template <int D, bool kCausal>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
+  constexpr int NJ = D / 16;     // QK MFMAs per 32-key tile
+  constexpr int NC = D / 32;     // channel tiles
+  constexpr int VT = kBN + 8;    // padded key stride of the transposed V tile (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[D * VT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, n = lane & 31;
+  const int G = a.Hq / a.Hkv;
+  const int n_kv = a.B * a.Hkv;
+  const int n_qt = (a.Sq + kBR - 1) / kBR;
+  int wi = blockIdx.x;
+  const int kv = wi % n_kv;
+  wi /= n_kv;
+  const int hg = wi % G;
+  const int qt = n_qt - 1 - wi / G;
+  const int b = kv / a.Hkv, g = kv % a.Hkv;
+  const int hq = g * G + hg;
+  const int L = a.Sk;
+  const int64_t bhq = (int64_t)b * a.Hq + hq;
+  const int64_t bkv = (int64_t)b * a.Hkv + g;
+  const int q_wave0 = qt * kBR + wave * 32;
+  const int q = q_wave0 + n;
+
+  v8s qa[NJ];
+  if (q < a.Sq) {
+    const uint16_t* qr = a.q + (bhq * a.Sq + q) * D;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      uint4 w = *reinterpret_cast<const uint4*>(qr + 16 * j + 8 * h);
+      __builtin_memcpy(&qa[j], &w, 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; j++) qa[j] = v8s{};
+  }
+
+  int kv_end = L, wave_end = L, wave_full = L;
+  if (kCausal) {
+    const int last_q = min(a.Sq, (qt + 1) * kBR) - 1;
+    kv_end = max(0, min(L, last_q + L - a.Sq + 1));
+    const int wl = min(a.Sq, q_wave0 + 32) - 1;
+    wave_end = max(0, min(L, wl + L - a.Sq + 1));
+    wave_full = max(0, min(L, q_wave0 + L - a.Sq + 1));
+  }
+  if (q_wave0 >= a.Sq) wave_end = 0;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int row_lim = kCausal ? min(L, q + L - a.Sq + 1) : L;
+  const float c = a.sm_log2;
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  v16f acc[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
+
+  for (int kt = 0; kt < n_tiles; kt++) {
+    const int n0 = kt * kBN;
+    __syncthreads();
+    // K tile, row-major [key][D]
+    for (int ci = tid; ci < kBN * D / 8; ci += 256) {
+      const int row = ci / (D / 8), off = (ci % (D / 8)) * 8;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (n0 + row < L)
+        w = *reinterpret_cast<const uint4*>(a.k + (bkv * a.cap + n0 + row) * D + off);
+      *reinterpret_cast<uint4*>(lds_k + row * D + off) = w;
+    }
+    // V tile transposed: thread -> (key = ci % 64, 8 channels)
+    for (int ci = tid; ci < kBN * D / 8; ci += 256) {
+      const int key = ci % kBN, cg = (ci / kBN) * 8;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (n0 + key < L)
+        w = *reinterpret_cast<const uint4*>(a.v + (bkv * a.cap + n0 + key) * D + cg);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        lds_vt[(cg + 2 * i) * VT + key] = (uint16_t)(ws[i] & 0xFFFFu);
+        lds_vt[(cg + 2 * i + 1) * VT + key] = (uint16_t)(ws[i] >> 16);
+      }
+    }
+    __syncthreads();
+    if (n0 >= wave_end) continue;
+
+    v16f s0 = v16f{}, s1 = v16f{};
+    const int r0 = perm_row_bf16(0, n), r1 = perm_row_bf16(1, n);
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      v8s k0, k1;
+      uint4 w0 = *reinterpret_cast<const uint4*>(lds_k + r0 * D + 16 * j + 8 * h);
+      uint4 w1 = *reinterpret_cast<const uint4*>(lds_k + r1 * D + 16 * j + 8 * h);
+      __builtin_memcpy(&k0, &w0, 16);
+      __builtin_memcpy(&k1, &w1, 16);
+      s0 = mfma_bf16_32x32x16(k0, qa[j], s0);
+      s1 = mfma_bf16_32x32x16(k1, qa[j], s1);
+    }
+    // lane (q, h): tile t register r holds key 32t + 16*(r/8) + 8h + r%8
+    float s[32];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      s[r] = s0[r];
+      s[16 + r] = s1[r];
+    }
+    if (n0 + kBN > wave_full) {
+#pragma unroll
+      for (int k = 0; k < 32; k++) {
+        const int key = n0 + 32 * (k >> 4) + 16 * ((k >> 3) & 1) + 8 * h + (k & 7);
+        if (key >= row_lim) s[k] = -INFINITY;
+      }
+    }
+    float bm = s[0];
+#pragma unroll
+    for (int k = 1; k < 32; k++) bm = fmaxf(bm, s[k]);
+    const float rm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m_run, rm * c);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float p[32];
+    float ps = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      p[k] = __builtin_amdgcn_exp2f(fmaf(s[k], c, -m_use));
+      ps += p[k];
+    }
+    ps += __shfl_xor(ps, 32);
+    l_run = alpha * l_run + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) acc[cc] *= alpha;
+    // P V: 4 MFMAs of 16 keys; MFMA u = 2t + j2 takes registers 8*j2 .. +7 of tile t
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int k = 16 * (u >> 1) + 8 * (u & 1) + 2 * i;
+        pw[i] = float_to_bf16_bits(p[k]) | (float_to_bf16_bits(p[k + 1]) << 16);
+      }
+      v8s pb;
+      __builtin_memcpy(&pb, pw, 16);
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) {
+        v8s va;
+        uint4 w = *reinterpret_cast<const uint4*>(lds_vt + (32 * cc + n) * VT + 16 * u + 8 * h);
+        __builtin_memcpy(&va, &w, 16);
+        acc[cc] = mfma_bf16_32x32x16(va, pb, acc[cc]);
+      }
+    }
+  }
+
+  if (q < a.Sq) {
+    const int64_t row = bhq * a.Sq + q;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        const int ch = 32 * cc + 8 * g4 + 4 * h;
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) u[i] = float_to_bf16_bits(acc[cc][4 * g4 + i] * inv);
+        *reinterpret_cast<uint2*>(a.out + row * D + ch) =
+            make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16));
+      }
+    if (a.lse && h == 0) a.lse[row] = l_run > 0.0f ? m_run * kLn2 + logf(l_run) : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const Bf16AttnArgs& a, hipStream_t stream) {
+  const int n_qt = (a.Sq + kBR - 1) / kBR;
+  const int64_t grid = (int64_t)n_qt * a.B * a.Hq;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (a.causal)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill_bf16(const Bf16AttnArgs& a, hipStream_t stream) {
+  switch (a.d) {
+    case 64: return launch_d<64>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    case 256: return launch_d<256>(a, stream);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace hifa4

@@ -1,0 +1,525 @@
+// attn_mxfp4.hip -- fused MXFP4 FlashAttention for gfx950: prefill and
+// split-K decode with a log-sum-exp merge.
+//
+// Method: "HiFA4: Training-Free 4-bit FlashAttention on Ascend HIF4 NPUs for
+// LLM Inference", Abstract:
+//   - Q K^T and P V are both 4-bit block-scaled products: here the gfx950
+//     scaled-FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), E2M1 operands with
+//     E8M0 scales per 32 elements fed straight into the instruction;
+//   - the online-softmax state (running max m, normaliser l) stays in higher
+//     precision than the operands (fp32 here);
+//   - P-Reordering: P = exp(S - m_new) is quantised to MXFP4 in registers and
+//     the normaliser is summed from that same P_hat; the sum is fused into the
+//     P V product by appending an all-ones column to V (an extra 32-row MFMA
+//     tile whose row 0 is E2M1 1.0 with scale 2^0), so l comes out of the
+//     matrix core next to P_hat V.
+//
+// Layouts (see include/hifa4.h): Q / K rows hold d/2 code bytes and d/32
+// scale bytes; V is key-blocked, every channel's 32 tokens contiguous in 16
+// bytes, which is exactly one lane's P V operand.
+//
+// Register layouts of the 32x32x64 MFMA (checked by the probe tests):
+// lane l supplies row / column l % 32 and the 32-element K block l / 32; the
+// accumulator register r of lane l holds D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+//
+// S is computed transposed (S^T = K Q^T), so a lane owns one query and 16
+// keys per 32-key tile.  The K rows of the A operand are loaded in the
+// permuted order perm_row(), chosen so that after the two 32-key MFMAs of a
+// 64-key step, lane (q, h) holds exactly keys 32h .. 32h+31 of that step, in
+// order, in registers (tile t, register r) -> key 32h + 16t + r.  That is the
+// B-operand layout of the P V MFMA (K = 64 keys, block h), so P goes from the
+// accumulator to the next MFMA with no cross-lane traffic: its block max is
+// an in-lane max, its 32 values are packed by 16 v_cvt_scalef32_pk_fp4_f32.
+// The row max over a step needs one exchange between lanes l and l ^ 32.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace hifa4 {
+
+namespace {
+
+constexpr int kBN = 64;            // keys per online-softmax step (the P frame tile)
+constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kBR = 32 * kWaves;   // queries per prefill workgroup
+constexpr int kDecodeChunk = 512;  // tokens per decode wave (fresh state), default
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Row of the 64-key step that A-operand row m of 32-key tile t loads.
+__device__ __forceinline__ int perm_row(int t, int m) {
+  return 32 * ((m >> 2) & 1) + 16 * t + 4 * (m >> 3) + (m & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pack the lane's 32 P values (natural key order) into E2M1 codes with the
+// block scale `scale` (= 2^(e8m0 - 127)).
+__device__ __forceinline__ uint4 pack_p(const float (&p)[32], float scale) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t x = 0;
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 0], p[8 * q + 1], scale, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 2], p[8 * q + 3], scale, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 4], p[8 * q + 5], scale, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 6], p[8 * q + 7], scale, 3);
+    w[q] = x;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// One online-softmax step on the 32 scores a lane holds for its query
+// (already masked with -inf).  Updates m_run, rescales the accumulators and
+// returns the packed P operand plus its E8M0 byte.
+struct SoftmaxStep {
+  uint4 p_codes;
+  int p_scale;
+  float alpha;
+};
+
+__device__ __forceinline__ SoftmaxStep softmax_step(float (&s)[32], float& m_run, float c) {
+  float bm = s[0];
+#pragma unroll
+  for (int k = 1; k < 32; k++) bm = fmaxf(bm, s[k]);
+  const float rm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(m_run, rm * c);
+  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+  SoftmaxStep st;
+  st.alpha = fast_exp2(m_run - m_use);
+  float p[32];
+#pragma unroll
+  for (int k = 0; k < 32; k++) p[k] = fast_exp2(fmaf(s[k], c, -m_use));
+  const float pmax = fast_exp2(fmaf(bm, c, -m_use));
+  const uint32_t sb = e8m0_from_amax(pmax);
+  st.p_scale = (int)sb;
+  st.p_codes = pack_p(p, e8m0_to_float(sb));
+  m_run = m_new;
+  return st;
+}
+
+template <int NC>
+__device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row, int h, const v16f (&acc)[NC],
+                                          float inv) {
+  constexpr int D = NC * 32;
+#pragma unroll
+  for (int c = 0; c < NC; c++) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; g4++) {
+      const int ch = 32 * c + 8 * g4 + 4 * h;
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float v = acc[c][4 * g4 + i] * inv;
+        u[i] = a.out_fp16 ? float_to_half_bits(v) : float_to_bf16_bits(v);
+      }
+      uint2 w = make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + ch) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one workgroup = 128 queries of one (batch, query head); 4 waves of
+// 32 queries share K / V tiles staged in LDS.
+// ---------------------------------------------------------------------------
+template <int D, bool kCausal>
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ones_scale) {
+  constexpr int DB = D / 2;   // code bytes per Q / K row
+  constexpr int DS = D / 32;  // scale bytes per Q / K row
+  constexpr int NJ = D / 64;  // QK MFMAs per 32-key tile
+  constexpr int NC = D / 32;  // P V channel tiles
+  __shared__ __attribute__((aligned(16))) uint8_t lds_kc[kBN * DB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ks[kBN * DS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_vc[2 * D * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_vs[2 * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, n = lane & 31;
+
+  // Work item.  Linear order: kv head fastest (so the query heads of one GQA
+  // group, which read the same K / V, land on the same XCD when B*Hkv is a
+  // multiple of 8), then the query head within the group, then query tiles
+  // from the last (most keys under a causal mask) to the first.
+  const int G = a.Hq / a.Hkv;
+  const int n_kv = a.B * a.Hkv;
+  const int n_qt = (a.Sq + kBR - 1) / kBR;
+  int wi = blockIdx.x;
+  const int kv = wi % n_kv;
+  wi /= n_kv;
+  const int hg = wi % G;
+  const int qt = n_qt - 1 - wi / G;
+  const int b = kv / a.Hkv, g = kv % a.Hkv;
+  const int hq = g * G + hg;
+  const int L = a.Sk;
+  const int64_t bhq = (int64_t)b * a.Hq + hq;
+  const int64_t bkv = (int64_t)b * a.Hkv + g;
+  const int q_wave0 = qt * kBR + wave * 32;
+  const int q = q_wave0 + n;
+  const int nblk_valid = (L + 31) / 32;
+  const int nblk_cap = (a.cap + 31) / 32;
+
+  // Q operand (B of S^T = K Q^T): query q, K blocks of 32 along d.
+  uint4 qa[NJ];
+  int qs[NJ];
+  if (q < a.Sq) {
+    const uint8_t* qc = a.q_codes + (bhq * a.Sq + q) * DB;
+    const uint8_t* qsc = a.q_scales + (bhq * a.Sq + q) * DS;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
+      qs[j] = qsc[2 * j + h];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      qa[j] = make_uint4(0, 0, 0, 0);
+      qs[j] = 0;
+    }
+  }
+
+  // Key ranges: the workgroup stages every tile any of its rows can see; a
+  // wave computes only tiles its own rows can see; tiles below wave_full are
+  // visible to every row of the wave (no mask needed).
+  int kv_end = L, wave_end = L, wave_full = L;
+  if (kCausal) {
+    const int last_q = min(a.Sq, (qt + 1) * kBR) - 1;
+    kv_end = max(0, min(L, last_q + L - a.Sq + 1));
+    const int wl = min(a.Sq, q_wave0 + 32) - 1;
+    wave_end = max(0, min(L, wl + L - a.Sq + 1));
+    wave_full = max(0, min(L, q_wave0 + L - a.Sq + 1));
+  }
+  if (q_wave0 >= a.Sq) wave_end = 0;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int row_lim = kCausal ? min(L, q + L - a.Sq + 1) : L;  // keys < row_lim visible
+
+  const uint32_t one_bits = n == 0 ? 0x22222222u : 0u;  // E2M1 1.0 in every nibble of row 0
+  const uint4 ones = make_uint4(one_bits, one_bits, one_bits, one_bits);
+  const float c = a.sm_log2;
+
+  float m_run = -INFINITY;
+  v16f acc[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
+  v16f accl = v16f{};
+
+  for (int kt = 0; kt < n_tiles; kt++) {
+    const int n0 = kt * kBN;
+    __syncthreads();
+    // ---- stage K codes / scales and V codes / scales of keys n0 .. n0+63
+    for (int ci = tid; ci < kBN * DB / 16; ci += 256) {
+      const int row = ci / (DB / 16), off = (ci % (DB / 16)) * 16;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (n0 + row < L)
+        w = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + n0 + row) * DB + off);
+      *reinterpret_cast<uint4*>(lds_kc + row * DB + off) = w;
+    }
+    if (tid < kBN) {
+      const int row = tid;
+      const bool ok = n0 + row < L;
+      const uint8_t* src = a.k_scales + (bkv * a.cap + n0 + row) * DS;
+      if constexpr (DS == 2) {
+        *reinterpret_cast<uint16_t*>(lds_ks + row * DS) = ok ? *reinterpret_cast<const uint16_t*>(src) : 0;
+      } else if constexpr (DS == 4) {
+        *reinterpret_cast<uint32_t*>(lds_ks + row * DS) = ok ? *reinterpret_cast<const uint32_t*>(src) : 0;
+      } else {
+        *reinterpret_cast<uint2*>(lds_ks + row * DS) = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+      }
+    }
+    for (int ci = tid; ci < 2 * D; ci += 256) {
+      const int blk = ci / D, ch = ci % D;
+      const int gb = n0 / 32 + blk;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (gb < nblk_valid)
+        w = *reinterpret_cast<const uint4*>(a.v_codes + ((bkv * nblk_cap + gb) * D + ch) * 16);
+      *reinterpret_cast<uint4*>(lds_vc + ci * 16) = w;
+    }
+    for (int ci = tid; ci < 2 * D / 16; ci += 256) {
+      const int blk = (ci * 16) / D, off = (ci * 16) % D;
+      const int gb = n0 / 32 + blk;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (gb < nblk_valid)
+        w = *reinterpret_cast<const uint4*>(a.v_scales + (bkv * nblk_cap + gb) * D + off);
+      *reinterpret_cast<uint4*>(lds_vs + ci * 16) = w;
+    }
+    __syncthreads();
+    if (n0 >= wave_end) continue;  // uniform per wave
+
+    // ---- S^T = K Q^T for the two 32-key tiles
+    v16f s0 = v16f{}, s1 = v16f{};
+    const int r0 = perm_row(0, n), r1 = perm_row(1, n);
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const uint4 k0 = *reinterpret_cast<const uint4*>(lds_kc + r0 * DB + 32 * j + 16 * h);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(lds_kc + r1 * DB + 32 * j + 16 * h);
+      const int ks0 = lds_ks[r0 * DS + 2 * j + h];
+      const int ks1 = lds_ks[r1 * DS + 2 * j + h];
+      s0 = mfma_fp4_32x32x64(k0, qa[j], s0, ks0, qs[j]);
+      s1 = mfma_fp4_32x32x64(k1, qa[j], s1, ks1, qs[j]);
+    }
+    float s[32];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      s[r] = s0[r];
+      s[16 + r] = s1[r];
+    }
+    if (n0 + kBN > wave_full) {
+      const int kb = n0 + 32 * h;
+#pragma unroll
+      for (int k = 0; k < 32; k++)
+        if (kb + k >= row_lim) s[k] = -INFINITY;
+    }
+
+    const SoftmaxStep st = softmax_step(s, m_run, c);
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
+    accl[0] *= st.alpha;
+
+    // ---- [acc | l] += P_hat [V | 1]
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) {
+      const int ch = 32 * cc + n;
+      const uint4 va = *reinterpret_cast<const uint4*>(lds_vc + (h * D + ch) * 16);
+      const int vs = lds_vs[h * D + ch];
+      acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
+    }
+    accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
+  }
+
+  // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
+  const float lsum = __shfl(accl[0], n);
+  if (q < a.Sq) {
+    const int64_t row = bhq * a.Sq + q;
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    write_out<NC>(a, row, h, acc, inv);
+    if (a.lse && h == 0) a.lse[row] = lsum > 0.0f ? m_run * kLn2 + logf(lsum) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode (Sq == 1), split-K: one wave = one chunk of `a.chunk` keys of one
+// (batch, kv head) against the G query heads of that group (the MFMA's 32
+// query columns, G used).  Each wave starts from a fresh state and writes its
+// partial (m, l, acc[d]) to the workspace; the merge kernel combines them.
+// K / V operands are loaded straight from global memory (no reuse to stage).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int ones_scale) {
+  constexpr int DB = D / 2, DS = D / 32, NJ = D / 64, NC = D / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, n = lane & 31;
+  const int G = a.Hq / a.Hkv;
+  const int bkv_i = blockIdx.y;
+  const int b = bkv_i / a.Hkv, g = bkv_i % a.Hkv;
+  const int64_t bkv = (int64_t)b * a.Hkv + g;
+  int L = a.Sk;
+  if (a.kv_lens) L = min(max(a.kv_lens[b], 0), a.Sk);
+  const int chunk_idx = blockIdx.x * kWaves + wave;
+  const int s0 = chunk_idx * a.chunk;
+  if (s0 >= L) return;  // uniform per wave; no barriers below
+  const int s1 = min(L, s0 + a.chunk);
+  const int nblk_valid = (L + 31) / 32;
+  const int nblk_cap = (a.cap + 31) / 32;
+
+  // Q operand: column n is query head g*G + n (zero for n >= G).
+  uint4 qa[NJ];
+  int qs[NJ];
+  if (n < G) {
+    const int64_t row = ((int64_t)b * a.Hq + g * G + n);  // Sq == 1
+    const uint8_t* qc = a.q_codes + row * DB;
+    const uint8_t* qsc = a.q_scales + row * DS;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
+      qs[j] = qsc[2 * j + h];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      qa[j] = make_uint4(0, 0, 0, 0);
+      qs[j] = 0;
+    }
+  }
+  const uint32_t one_bits = n == 0 ? 0x22222222u : 0u;
+  const uint4 ones = make_uint4(one_bits, one_bits, one_bits, one_bits);
+  const float c = a.sm_log2;
+  float m_run = -INFINITY;
+  v16f acc[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
+  v16f accl = v16f{};
+  const int r0 = perm_row(0, n), r1 = perm_row(1, n);
+
+  for (int n0 = s0; n0 < s1; n0 += kBN) {
+    v16f t0 = v16f{}, t1 = v16f{};
+    const int k0row = n0 + r0, k1row = n0 + r1;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      uint4 k0 = make_uint4(0, 0, 0, 0), k1 = make_uint4(0, 0, 0, 0);
+      int ks0 = 0, ks1 = 0;
+      if (k0row < L) {
+        k0 = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + k0row) * DB + 32 * j + 16 * h);
+        ks0 = a.k_scales[(bkv * a.cap + k0row) * DS + 2 * j + h];
+      }
+      if (k1row < L) {
+        k1 = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + k1row) * DB + 32 * j + 16 * h);
+        ks1 = a.k_scales[(bkv * a.cap + k1row) * DS + 2 * j + h];
+      }
+      t0 = mfma_fp4_32x32x64(k0, qa[j], t0, ks0, qs[j]);
+      t1 = mfma_fp4_32x32x64(k1, qa[j], t1, ks1, qs[j]);
+    }
+    float s[32];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      s[r] = t0[r];
+      s[16 + r] = t1[r];
+    }
+    if (n0 + kBN > s1) {
+      const int kb = n0 + 32 * h;
+#pragma unroll
+      for (int k = 0; k < 32; k++)
+        if (kb + k >= s1) s[k] = -INFINITY;
+    }
+    const SoftmaxStep st = softmax_step(s, m_run, c);
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
+    accl[0] *= st.alpha;
+    const int gb = n0 / 32 + h;
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) {
+      const int ch = 32 * cc + n;
+      uint4 va = make_uint4(0, 0, 0, 0);
+      int vs = 0;
+      if (gb < nblk_valid) {
+        va = *reinterpret_cast<const uint4*>(a.v_codes + ((bkv * nblk_cap + gb) * D + ch) * 16);
+        vs = a.v_scales[(bkv * nblk_cap + gb) * D + ch];
+      }
+      acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
+    }
+    accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
+  }
+
+  // partial row: [m, l, acc[0..D)] for (b, query head, chunk)
+  const float lsum = __shfl(accl[0], n);
+  if (n < G) {
+    float* part = a.partials + (((int64_t)b * a.Hq + g * G + n) * a.n_chunks + chunk_idx) * (D + 2);
+    if (h == 0) {
+      part[0] = m_run;
+      part[1] = lsum;
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        const int ch = 32 * cc + 8 * g4 + 4 * h;
+#pragma unroll
+        for (int i = 0; i < 4; i++) part[2 + ch + i] = acc[cc][4 * g4 + i];
+      }
+  }
+}
+
+// Log-sum-exp merge of the chunk partials: one wave per (batch, query head).
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);  // b * Hq + hq
+  if (row >= (int64_t)a.B * a.Hq) return;
+  const int b = (int)(row / a.Hq);
+  int L = a.Sk;
+  if (a.kv_lens) L = min(max(a.kv_lens[b], 0), a.Sk);
+  const int nc = (L + a.chunk - 1) / a.chunk;
+  const float* part = a.partials + row * a.n_chunks * (D + 2);
+  float M = -INFINITY;
+  for (int i = lane; i < nc; i += 64) M = fmaxf(M, part[(int64_t)i * (D + 2)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  constexpr int CPL = (D + 63) / 64;  // channels per lane
+  float o[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; j++) o[j] = 0.0f;
+  float lsum = 0.0f;
+  for (int i = 0; i < nc; i++) {
+    const float* pr = part + (int64_t)i * (D + 2);
+    const float w = M == -INFINITY ? 0.0f : fast_exp2(pr[0] - M);
+    lsum += w * pr[1];
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+      const int ch = lane + 64 * j;
+      if (ch < D) o[j] += w * pr[2 + ch];
+    }
+  }
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; j++) {
+    const int ch = lane + 64 * j;
+    if (ch < D) {
+      const float v = o[j] * inv;
+      static_cast<uint16_t*>(a.out)[row * D + ch] =
+          (uint16_t)(a.out_fp16 ? float_to_half_bits(v) : float_to_bf16_bits(v));
+    }
+  }
+  if (a.lse && lane == 0) a.lse[row] = lsum > 0.0f ? M * kLn2 + logf(lsum) : -INFINITY;
+}
+
+// The E8M0 byte for 2^0, passed as a kernel argument: the scaled MFMA must
+// see its scale operands as integer registers, not as a folded constant.
+constexpr int kScaleOne = 127;
+
+template <int D>
+hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
+  const int n_qt = (a.Sq + kBR - 1) / kBR;
+  const int64_t grid = (int64_t)n_qt * a.B * a.Hq;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (a.causal)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       a, kScaleOne);
+  else
+    hipLaunchKernelGGL((attn_prefill_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       a, kScaleOne);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
+  if (a.B == 0) return hipSuccess;
+  if (a.Hq / a.Hkv > 32) return hipErrorNotSupported;  // one MFMA column per query head
+  const int wg_x = (a.n_chunks + kWaves - 1) / kWaves;
+  if (wg_x > 0) {
+    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(wg_x, a.B * a.Hkv), dim3(256), 0, stream,
+                       a, kScaleOne);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rows = (int64_t)a.B * a.Hq;
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((unsigned)((rows + kWaves - 1) / kWaves)),
+                     dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_block_n(int) { return kBN; }
+int attn_default_chunk(int) { return kDecodeChunk; }
+
+hipError_t launch_attn_prefill_mxfp4(const AttnArgs& a, hipStream_t stream) {
+  switch (a.d) {
+    case 64: return launch_prefill_d<64>(a, stream);
+    case 128: return launch_prefill_d<128>(a, stream);
+    case 256: return launch_prefill_d<256>(a, stream);
+  }
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_attn_decode_mxfp4(const AttnArgs& a, hipStream_t stream) {
+  switch (a.d) {
+    case 64: return launch_decode_d<64>(a, stream);
+    case 128: return launch_decode_d<128>(a, stream);
+    case 256: return launch_decode_d<256>(a, stream);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace hifa4

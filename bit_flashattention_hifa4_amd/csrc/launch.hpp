@@ -1,0 +1,70 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hifa4 {
+
+struct QuantizeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* smooth;
+  uint8_t* q_codes;
+  uint8_t* q_scales;
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  int B, Hq, Hkv, Sq, Sk, d, cap;
+  int64_t blocks_q, blocks_k;  // 32-element row blocks
+  int64_t wg_q, wg_k;          // filled by the launcher
+};
+
+hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream);
+
+// Attention problem after validation; pointers are device pointers.
+struct AttnArgs {
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  void* out;
+  float* lse;
+  const int32_t* kv_lens;  // decode only, may be null
+  float* partials;         // decode workspace
+  int B, Hq, Hkv, Sq, Sk, d, cap;
+  int causal;
+  int out_fp16;
+  float sm_log2;           // sm_scale * log2(e)
+  float sm_scale;
+  int chunk;               // decode chunk (tokens)
+  int n_chunks;            // ceil(cap / chunk)
+};
+
+// Key tile width of the online-softmax frame for a head dim.
+int attn_block_n(int d);
+// Decode chunk the library picks when the caller passes 0.
+int attn_default_chunk(int d);
+
+hipError_t launch_attn_prefill_mxfp4(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_decode_mxfp4(const AttnArgs& a, hipStream_t stream);
+
+struct Bf16AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;
+  int B, Hq, Hkv, Sq, Sk, d, cap;
+  int causal;
+  float sm_log2;
+};
+
+hipError_t launch_attn_prefill_bf16(const Bf16AttnArgs& a, hipStream_t stream);
+
+}  // namespace hifa4

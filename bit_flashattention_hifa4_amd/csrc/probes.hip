@@ -1,0 +1,182 @@
+// probes.hip -- diagnostic kernels that pin down gfx950 instruction behaviour
+// the attention kernels rely on: the operand / scale / accumulator lane
+// layouts of the scaled-FP4 and bf16 MFMAs, the rounding of the packed FP4
+// convert, and the issue rates of v_exp_f32 and the FP4 MFMA.
+//
+// Built into its own library (libhifa4_probes.so); the tests call it to check
+// those facts against independent host-side expectations.  Every kernel reads
+// and writes exactly the buffers sized by its arguments.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "hifa4_probes.h"
+
+namespace hifa4 {
+namespace {
+
+template <int kOpsel>
+__global__ __launch_bounds__(64) void mfma_fp4_32_kernel(const uint4* a, const uint4* b,
+                                                         const uint32_t* sa, const uint32_t* sb,
+                                                         float* d) {
+  const int w = blockIdx.x, l = threadIdx.x;
+  v16f c = {};
+  v8i A = {(int)a[w * 64 + l].x, (int)a[w * 64 + l].y, (int)a[w * 64 + l].z, (int)a[w * 64 + l].w,
+           0, 0, 0, 0};
+  v8i B = {(int)b[w * 64 + l].x, (int)b[w * 64 + l].y, (int)b[w * 64 + l].z, (int)b[w * 64 + l].w,
+           0, 0, 0, 0};
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, kFmtFp4, kFmtFp4, kOpsel,
+                                                      (int)sa[w * 64 + l], kOpsel,
+                                                      (int)sb[w * 64 + l]);
+#pragma unroll
+  for (int r = 0; r < 16; r++) d[(w * 64 + l) * 16 + r] = c[r];
+}
+
+template <int kOpsel>
+__global__ __launch_bounds__(64) void mfma_fp4_16_kernel(const uint4* a, const uint4* b,
+                                                         const uint32_t* sa, const uint32_t* sb,
+                                                         float* d) {
+  const int w = blockIdx.x, l = threadIdx.x;
+  v4f c = {};
+  v8i A = {(int)a[w * 64 + l].x, (int)a[w * 64 + l].y, (int)a[w * 64 + l].z, (int)a[w * 64 + l].w,
+           0, 0, 0, 0};
+  v8i B = {(int)b[w * 64 + l].x, (int)b[w * 64 + l].y, (int)b[w * 64 + l].z, (int)b[w * 64 + l].w,
+           0, 0, 0, 0};
+  c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, kFmtFp4, kFmtFp4, kOpsel,
+                                                       (int)sa[w * 64 + l], kOpsel,
+                                                       (int)sb[w * 64 + l]);
+#pragma unroll
+  for (int r = 0; r < 4; r++) d[(w * 64 + l) * 4 + r] = c[r];
+}
+
+__global__ __launch_bounds__(64) void mfma_bf16_32_kernel(const uint4* a, const uint4* b,
+                                                          float* d) {
+  const int w = blockIdx.x, l = threadIdx.x;
+  uint4 x = a[w * 64 + l], y = b[w * 64 + l];
+  v8s A, B;
+  __builtin_memcpy(&A, &x, 16);
+  __builtin_memcpy(&B, &y, 16);
+  v16f c = {};
+  c = mfma_bf16_32x32x16(A, B, c);
+#pragma unroll
+  for (int r = 0; r < 16; r++) d[(w * 64 + l) * 16 + r] = c[r];
+}
+
+template <int kSel>
+__global__ void cvt_fp4_kernel(const float2* x, const float* scale, uint32_t* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[i].x, x[i].y, scale[i], kSel);
+  out[i] = r;
+}
+
+__global__ void exp2_rate_kernel(float* out, int iters) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) x[j] = 0.001f * (threadIdx.x + j);
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) s += x[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void mfma_rate_kernel(float* out, int iters) {
+  const int l = threadIdx.x;
+  uint4 a = make_uint4(0x22222222u ^ l, 0x12345678u, 0x0u, 0x76543210u);
+  uint4 b = make_uint4(0x11111111u, 0x22222222u ^ l, 0x33333333u, 0x0u);
+  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  int s = 127 + (l & 1);
+  for (int it = 0; it < iters; it++) {
+    c0 = mfma_fp4_32x32x64(a, b, c0, s, s);
+    c1 = mfma_fp4_32x32x64(b, a, c1, s, s);
+    c2 = mfma_fp4_32x32x64(a, a, c2, s, s);
+    c3 = mfma_fp4_32x32x64(b, b, c3, s, s);
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r++) t += c0[r] + c1[r] + c2[r] + c3[r];
+  out[blockIdx.x * blockDim.x + l] = t;
+}
+
+int status(hipError_t e) { return e == hipSuccess ? 0 : -(int)e; }
+
+}  // namespace
+}  // namespace hifa4
+
+using namespace hifa4;
+
+extern "C" {
+
+int probe_mfma_fp4_32x32x64(const uint32_t* a, const uint32_t* b, const uint32_t* sa,
+                            const uint32_t* sb, float* d, int n_waves, int opsel, void* stream) {
+  if (n_waves <= 0 || opsel < 0 || opsel > 3) return -1;
+  auto s = (hipStream_t)stream;
+  auto A = reinterpret_cast<const uint4*>(a);
+  auto B = reinterpret_cast<const uint4*>(b);
+  switch (opsel) {
+    case 0: hipLaunchKernelGGL(mfma_fp4_32_kernel<0>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+    case 1: hipLaunchKernelGGL(mfma_fp4_32_kernel<1>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+    case 2: hipLaunchKernelGGL(mfma_fp4_32_kernel<2>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+    default: hipLaunchKernelGGL(mfma_fp4_32_kernel<3>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+  }
+  return status(hipGetLastError());
+}
+
+int probe_mfma_fp4_16x16x128(const uint32_t* a, const uint32_t* b, const uint32_t* sa,
+                             const uint32_t* sb, float* d, int n_waves, int opsel, void* stream) {
+  if (n_waves <= 0 || opsel < 0 || opsel > 3) return -1;
+  auto s = (hipStream_t)stream;
+  auto A = reinterpret_cast<const uint4*>(a);
+  auto B = reinterpret_cast<const uint4*>(b);
+  switch (opsel) {
+    case 0: hipLaunchKernelGGL(mfma_fp4_16_kernel<0>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+    case 1: hipLaunchKernelGGL(mfma_fp4_16_kernel<1>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+    case 2: hipLaunchKernelGGL(mfma_fp4_16_kernel<2>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+    default: hipLaunchKernelGGL(mfma_fp4_16_kernel<3>, dim3(n_waves), dim3(64), 0, s, A, B, sa, sb, d); break;
+  }
+  return status(hipGetLastError());
+}
+
+int probe_mfma_bf16_32x32x16(const uint16_t* a, const uint16_t* b, float* d, int n_waves,
+                             void* stream) {
+  if (n_waves <= 0) return -1;
+  hipLaunchKernelGGL(mfma_bf16_32_kernel, dim3(n_waves), dim3(64), 0, (hipStream_t)stream,
+                     reinterpret_cast<const uint4*>(a), reinterpret_cast<const uint4*>(b), d);
+  return status(hipGetLastError());
+}
+
+int probe_cvt_pk_fp4(const float* x, const float* scale, uint32_t* out, int n, int sel,
+                     void* stream) {
+  if (n <= 0 || sel < 0 || sel > 3) return -1;
+  auto s = (hipStream_t)stream;
+  auto X = reinterpret_cast<const float2*>(x);
+  dim3 g((n + 255) / 256), t(256);
+  switch (sel) {
+    case 0: hipLaunchKernelGGL(cvt_fp4_kernel<0>, g, t, 0, s, X, scale, out, n); break;
+    case 1: hipLaunchKernelGGL(cvt_fp4_kernel<1>, g, t, 0, s, X, scale, out, n); break;
+    case 2: hipLaunchKernelGGL(cvt_fp4_kernel<2>, g, t, 0, s, X, scale, out, n); break;
+    default: hipLaunchKernelGGL(cvt_fp4_kernel<3>, g, t, 0, s, X, scale, out, n); break;
+  }
+  return status(hipGetLastError());
+}
+
+int probe_exp2_rate(float* out, int n_blocks, int iters, void* stream) {
+  if (n_blocks <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(exp2_rate_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, out,
+                     iters);
+  return status(hipGetLastError());
+}
+
+int probe_mfma_rate(float* out, int n_blocks, int iters, void* stream) {
+  if (n_blocks <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, out,
+                     iters);
+  return status(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+/*
+ * hifa4.h -- C ABI of the MXFP4 FlashAttention library for MI355X (gfx950).
+ *
+ * Method: "HiFA4: Training-Free 4-bit FlashAttention on Ascend HIF4 NPUs for
+ * LLM Inference", Abstract.  Both attention products (Q K^T and P V) run on
+ * 4-bit block-scaled operands while the online-softmax state (running max m,
+ * normaliser l) stays in higher precision (fp32 here); Smooth-QK rescales Q
+ * and K per channel after RoPE (Q * s, K / s) with a calibration-static s;
+ * P-Reordering sums the normaliser from the same quantised P_hat that feeds
+ * the P V product, and that sum is fused into the P V matrix product.
+ *
+ * 4-bit format.  The pages name HIF4 but never define its bit layout, so the
+ * library uses gfx950's native OCP MXFP4 as the stand-in: FP4 E2M1 elements
+ * (2 per byte, element 2i in the low nibble), one E8M0 scale byte per 32
+ * elements with exponent floor(log2(amax)) - 2 (byte = exponent + 127),
+ * elements rounded to nearest-even and clamped to +-6.
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, contiguous in the layouts documented below;
+ *   - `stream` is a hipStream_t (NULL = the default stream); every call only
+ *     enqueues work on it and never synchronises;
+ *   - the library never allocates device memory; scratch memory comes from the
+ *     caller's `workspace` (size from hifa4_attn_workspace_size);
+ *   - arguments are validated before anything is enqueued: on a negative
+ *     status nothing was enqueued and hifa4_last_error() describes why;
+ *   - a launch failure returns HIFA4_ERR_HIP; faults during execution surface
+ *     at the caller's next synchronisation;
+ *   - outputs must not overlap inputs; inputs are read only;
+ *   - NaN / Inf inputs are unsupported (results unspecified);
+ *   - calls are reentrant; the only global state is the per-thread error text.
+ */
+#ifndef HIFA4_H_
+#define HIFA4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define HIFA4_API __attribute__((visibility("default")))
+#else
+#define HIFA4_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hifa4_status {
+  HIFA4_OK = 0,
+  HIFA4_ERR_INVALID_ARGUMENT = -1, /* null / misaligned pointer, bad size, overlap */
+  HIFA4_ERR_UNSUPPORTED = -2,      /* valid request outside what the kernels implement */
+  HIFA4_ERR_WORKSPACE_TOO_SMALL = -3,
+  HIFA4_ERR_HIP = -4               /* the HIP runtime refused a launch */
+} hifa4_status;
+
+typedef enum hifa4_dtype { HIFA4_BF16 = 0, HIFA4_FP16 = 1 } hifa4_dtype;
+
+/* An MXFP4 tensor: E2M1 codes and E8M0 scales, both device buffers.
+ * Row layout (queries, keys), blocks of 32 along the head dim d:
+ *   codes  [B][H][T][d/2]   scales [B][H][T][d/32]
+ * Column layout (values), blocks of 32 consecutive tokens of one channel,
+ * aligned to token 0, nblk = ceil(T / 32):
+ *   codes  [B][H][nblk][d][16]  (token 32*j + 2i in the low nibble of byte i)
+ *   scales [B][H][nblk][d]
+ * T is Sq for queries and the token capacity kv_stride for keys / values. */
+typedef struct hifa4_mx_tensor {
+  uint8_t* codes;
+  uint8_t* scales;
+} hifa4_mx_tensor;
+
+typedef struct hifa4_attn_params {
+  int32_t B;          /* batch */
+  int32_t Hq;         /* query heads */
+  int32_t Hkv;        /* key/value heads; Hq % Hkv == 0, query head h reads kv head h / (Hq / Hkv) */
+  int32_t Sq;         /* query tokens per sequence (1 selects the split-K decode path) */
+  int32_t Sk;         /* key tokens per sequence (upper bound when kv_lens is given) */
+  int32_t d;          /* head dim: 64, 128 or 256 */
+  int32_t causal;     /* nonzero: key t visible to query i iff t <= i + L - Sq (bottom-right) */
+  float sm_scale;     /* score scale applied to Q K^T; <= 0 selects 1/sqrt(d) */
+  int32_t kv_stride;  /* token capacity of the K/V buffers (>= Sk); 0 means Sk */
+  const int32_t* kv_lens; /* device [B] per-sequence key count L (<= Sk), or NULL (L = Sk);
+                             only with Sq == 1 */
+  int32_t decode_chunk;   /* split-K chunk in tokens (multiple of the key tile); 0 = library's choice */
+} hifa4_attn_params;
+
+/*
+ * Smooth-QK + MXFP4 quantisation of Q, K and V (one launch).
+ * Abstract, Smooth-QK: Q' = Q * s and K' = K / s per channel, in fp32 with
+ * IEEE round-to-nearest multiply and divide, applied to the post-RoPE
+ * activations; s is static (from offline calibration).  V is not smoothed.
+ * Inputs (device, in_dtype, contiguous):
+ *   q [B][Hq][Sq][d], k [B][Hkv][Sk][d], v [B][Hkv][Sk][d]
+ *   smooth: device fp32 [Hkv][d] (query head h uses row h / (Hq / Hkv)), or NULL for s = 1
+ * Outputs: q_out in the row layout with T = Sq; k_out in the row layout and
+ *   v_out in the column layout, both with T = kv_stride (>= Sk, 0 means Sk).
+ *   Only tokens < Sk are written; the tail value block is zero-padded.
+ * Any of q / k / v may be NULL (with its output ignored) to skip that tensor.
+ * d must be 64, 128 or 256.
+ */
+HIFA4_API hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const void* v, hifa4_dtype in_dtype,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Sk,
+                                int32_t kv_stride, int32_t d, const float* smooth,
+                                hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
+                                hifa4_mx_tensor v_out, void* stream);
+
+/* Bytes of device workspace hifa4_attn_fwd / bf16_attn_fwd need for p
+ * (0 when none); returns 0 as well for invalid parameters. */
+HIFA4_API size_t hifa4_attn_workspace_size(const hifa4_attn_params* p);
+
+/*
+ * Fused MXFP4 FlashAttention forward (prefill for Sq > 1, split-K decode for
+ * Sq == 1).  Abstract: Q K^T and P V are 4-bit block-scaled products (gfx950
+ * scaled-FP4 MFMA); m and l are fp32; P = exp(S - m_new) is quantised to
+ * MXFP4 in registers (blocks of 32 keys aligned to key 0); the normaliser
+ * l = sum(P_hat) comes out of the P V MFMA through an all-ones value column
+ * (P-Reordering with the fused normaliser).  The running max is updated once
+ * per key tile (width from hifa4_attn_schedule).  Decode splits the keys into
+ * chunks, runs each from a fresh state and merges (m, l, acc) with the
+ * log-sum-exp rule.
+ * q, k, v: MX tensors from hifa4_quantize_qkv (T = Sq for q, kv_stride for k, v).
+ * out: device [B][Hq][Sq][d] in out_dtype, O = acc / l (rows without any
+ *      visible key are 0).
+ * lse: device fp32 [B][Hq][Sq] natural-log sum-exp of the scaled scores
+ *      (m + ln l; -inf for rows without a visible key), or NULL.
+ * workspace: device scratch of hifa4_attn_workspace_size(p) bytes (may be NULL if 0).
+ */
+HIFA4_API hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4_mx_tensor k,
+                            hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bf16 FlashAttention forward, the accuracy and latency baseline the pages
+ * compare against (Abstract): bf16 MFMA products, fp32 softmax state, no
+ * quantisation and no smoothing.  q [B][Hq][Sq][d], k / v [B][Hkv][kv_stride][d]
+ * bf16 device; out bf16 [B][Hq][Sq][d]; lse as for hifa4_attn_fwd.
+ * kv_lens must be NULL.
+ */
+HIFA4_API hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void* k,
+                           const void* v, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* The key-tile width of the online-softmax frame (*block_n) and the split-K
+ * chunk (*chunk_tokens, 0 for prefill) hifa4_attn_fwd uses for p.  P_hat
+ * depends on both, so a reference implementation needs them. */
+HIFA4_API hifa4_status hifa4_attn_schedule(const hifa4_attn_params* p, int32_t* block_n,
+                                 int32_t* chunk_tokens);
+
+/* Static text for a status code. */
+HIFA4_API const char* hifa4_status_string(hifa4_status s);
+
+/* Detail text of the last failing call on this thread ("" if none). */
+HIFA4_API const char* hifa4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIFA4_H_ */

@@ -1,0 +1,61 @@
+/*
+ * hifa4_probes.h -- diagnostic entry points of libhifa4_probes.so.
+ *
+ * They run single gfx950 instructions on caller-supplied operands so that
+ * tests can check, against host-side expectations, the facts the attention
+ * kernels rely on: which lane holds which operand element and block scale of
+ * the scaled-FP4 MFMA (the 4-bit products the HiFA4 abstract puts under both
+ * Q K^T and P V), the accumulator layout, the rounding of the packed FP4
+ * convert used to quantise P, and the issue rates of v_exp_f32 and the FP4
+ * MFMA (the softmax / matrix-core balance).  They are not part of the
+ * attention API.
+ *
+ * All pointers are device pointers; every call only enqueues on `stream`
+ * (a hipStream_t, NULL = default) and returns 0, or a negative value for a
+ * bad argument or launch failure.
+ */
+#ifndef HIFA4_PROBES_H_
+#define HIFA4_PROBES_H_
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define HIFA4_PROBE_API __attribute__((visibility("default")))
+#else
+#define HIFA4_PROBE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One v_mfma_scale_f32_32x32x64_f8f6f4 (both operands FP4 E2M1) per wave.
+ * a, b: [n_waves][64 lanes][4] dwords (the A / B operand registers of each
+ * lane); sa, sb: [n_waves][64] scale registers; d: [n_waves][64][16] fp32
+ * accumulator registers (C = 0).  opsel (0..3) is passed for both scales. */
+HIFA4_PROBE_API int probe_mfma_fp4_32x32x64(const uint32_t* a, const uint32_t* b, const uint32_t* sa,
+                            const uint32_t* sb, float* d, int n_waves, int opsel, void* stream);
+
+/* Same for v_mfma_scale_f32_16x16x128_f8f6f4; d: [n_waves][64][4]. */
+HIFA4_PROBE_API int probe_mfma_fp4_16x16x128(const uint32_t* a, const uint32_t* b, const uint32_t* sa,
+                             const uint32_t* sb, float* d, int n_waves, int opsel, void* stream);
+
+/* One v_mfma_f32_32x32x16_bf16 per wave: a, b [n_waves][64][8] bf16, d [n_waves][64][16]. */
+HIFA4_PROBE_API int probe_mfma_bf16_32x32x16(const uint16_t* a, const uint16_t* b, float* d, int n_waves,
+                             void* stream);
+
+/* out[i] = v_cvt_scalef32_pk_fp4_f32(0, x[2i], x[2i+1], scale[i]) writing byte `sel`. */
+HIFA4_PROBE_API int probe_cvt_pk_fp4(const float* x, const float* scale, uint32_t* out, int n, int sel,
+                     void* stream);
+
+/* Throughput loops (n_blocks x 256 threads): 8 independent v_exp_f32 chains per
+ * thread, or 4 independent FP4 32x32x64 MFMA chains per wave, iters times.
+ * out: [n_blocks * 256] floats (keeps the work alive). */
+HIFA4_PROBE_API int probe_exp2_rate(float* out, int n_blocks, int iters, void* stream);
+HIFA4_PROBE_API int probe_mfma_rate(float* out, int n_blocks, int iters, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIFA4_PROBES_H_ */

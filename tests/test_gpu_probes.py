@@ -1,0 +1,255 @@
+"""gfx950 instruction facts the attention kernels depend on (GPU).
+
+Each probe runs one instruction per wave on random operands and compares the
+result with a host computation of the hypothesised semantics:
+  * scaled FP4 MFMA 32x32x64 / 16x16x128: lane l of A holds row l % M and the
+    32-element K block l // M (byte i low nibble = element 2i), its E8M0 scale
+    in byte 0 of the scale register; the accumulator holds D[m][n] with
+    n = l % N and m as documented in device_common.hpp;
+  * bf16 MFMA 32x32x16: lane l holds row / column l % 32, K elements
+    8 * (l // 32) .. + 7;
+  * v_cvt_scalef32_pk_fp4_f32 rounds x / scale to nearest-even E2M1 with
+    saturation, like the oracle's encoder, and writes the selected byte.
+Also measures the v_exp_f32 and FP4 MFMA issue rates (printed, loosely bounded).
+Set HIFA4_PROBE_DUMP=<dir> to save raw operands / results for offline study.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROBES = os.path.join(ROOT, "bit_flashattention_hifa4_amd", "libhifa4_probes.so")
+MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+CODE_VAL = np.array([MAG[c & 7] * (-1 if c & 8 else 1) for c in range(16)])
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(PROBES):
+        pytest.fail("libhifa4_probes.so is not built")
+    l = ctypes.CDLL(PROBES)
+    for name in ("probe_mfma_fp4_32x32x64", "probe_mfma_fp4_16x16x128"):
+        getattr(l, name).argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_int,
+                                                             ctypes.c_void_p]
+    l.probe_mfma_bf16_32x32x16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
+    l.probe_cvt_pk_fp4.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int,
+                                                           ctypes.c_void_p]
+    l.probe_exp2_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    l.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return l
+
+
+def _dump(name, **arrays):
+    d = os.environ.get("HIFA4_PROBE_DUMP")
+    if d:
+        os.makedirs(d, exist_ok=True)
+        np.savez(os.path.join(d, name + ".npz"), **arrays)
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _nibbles(words: np.ndarray) -> np.ndarray:
+    """[..., 4] uint32 -> [..., 32] codes, element i = nibble i (little-endian)."""
+    b = words.astype("<u4").view(np.uint8)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def _expected_fp4(a, b, sa, sb, M, N, sel):
+    """Host D = A @ B for one wave under the hypothesised lane layout."""
+    kb = 64 // M          # K blocks per lane group: 2 for 32x32x64, 4 for 16x16x128
+    K = 32 * kb
+    A = np.zeros((M, K))
+    Bm = np.zeros((K, N))
+    ca, cb = _nibbles(a), _nibbles(b)
+    sca = ((sa >> (8 * sel)) & 0xFF).astype(np.int64)
+    scb = ((sb >> (8 * sel)) & 0xFF).astype(np.int64)
+    for l in range(64):
+        blk = l // M
+        A[l % M, 32 * blk:32 * blk + 32] = CODE_VAL[ca[l]] * 2.0 ** (sca[l] - 127)
+        Bm[32 * blk:32 * blk + 32, l % N] = CODE_VAL[cb[l]] * 2.0 ** (scb[l] - 127)
+    return A @ Bm
+
+
+def _acc_index(M, l, r):
+    if M == 32:
+        return 8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32
+    return 4 * (l // 16) + r, l % 16
+
+
+def _run_fp4(lib, M, opsel, n_waves=64, seed=0, scale_byte=None):
+    rng = np.random.default_rng(seed)
+    R = 16 if M == 32 else 4
+    a = rng.integers(0, 2**32, size=(n_waves, 64, 4), dtype=np.uint64).astype(np.uint32)
+    b = rng.integers(0, 2**32, size=(n_waves, 64, 4), dtype=np.uint64).astype(np.uint32)
+    sa = rng.integers(0, 2**32, size=(n_waves, 64), dtype=np.uint64).astype(np.uint32)
+    sb = rng.integers(0, 2**32, size=(n_waves, 64), dtype=np.uint64).astype(np.uint32)
+    sel = 0 if scale_byte is None else scale_byte
+    # the scale that matters lives in byte `sel`, in [117, 137]; other bytes are random
+    mask = np.uint32(0xFF << (8 * sel))
+    sa = (sa & ~mask) | (rng.integers(117, 138, size=sa.shape).astype(np.uint32) << (8 * sel))
+    sb = (sb & ~mask) | (rng.integers(117, 138, size=sb.shape).astype(np.uint32) << (8 * sel))
+    dev = lambda x: torch.from_numpy(x.view(np.int32)).cuda()
+    ta, tb, tsa, tsb = dev(a), dev(b), dev(sa), dev(sb)
+    d = torch.zeros((n_waves, 64, R), dtype=torch.float32, device="cuda")
+    fn = lib.probe_mfma_fp4_32x32x64 if M == 32 else lib.probe_mfma_fp4_16x16x128
+    assert fn(ta.data_ptr(), tb.data_ptr(), tsa.data_ptr(), tsb.data_ptr(), d.data_ptr(), n_waves,
+              opsel, _stream()) == 0
+    torch.cuda.synchronize()
+    return a, b, sa, sb, d.cpu().numpy()
+
+
+def _compare_fp4(a, b, sa, sb, d, M, sel):
+    R = d.shape[-1]
+    worst = 0.0
+    for w in range(a.shape[0]):
+        ref = _expected_fp4(a[w], b[w], sa[w], sb[w], M, M, sel)
+        got = np.zeros_like(ref)
+        for l in range(64):
+            for r in range(R):
+                m, n = _acc_index(M, l, r)
+                got[m, n] = d[w, l, r]
+        err = np.abs(got - ref) / (np.abs(ref).max() + 1e-300)
+        worst = max(worst, err.max())
+    return worst
+
+
+@pytest.mark.parametrize("M", [32, 16])
+def test_scaled_fp4_mfma_layout(lib, M):
+    a, b, sa, sb, d = _run_fp4(lib, M, opsel=0, seed=M)
+    _dump("mfma_fp4_%d" % M, a=a, b=b, sa=sa, sb=sb, d=d)
+    worst = _compare_fp4(a, b, sa, sb, d, M, 0)
+    print("fp4 %dx%d MFMA layout: worst relative error %.3g" % (M, M, worst))
+    assert worst < 1e-5
+
+
+@pytest.mark.parametrize("opsel", [1, 2, 3])
+def test_scaled_fp4_mfma_opsel_report(lib, opsel):
+    """Which scale byte does a non-zero opsel pick?  Reported; only byte 0 is relied on."""
+    a, b, sa, sb, d = _run_fp4(lib, 32, opsel=opsel, seed=100 + opsel, n_waves=8,
+                               scale_byte=opsel)
+    e_sel = _compare_fp4(a, b, sa, sb, d, 32, opsel)
+    e_b0 = _compare_fp4(a, b, sa, sb, d, 32, 0)
+    print("opsel=%d: error if byte %d used %.3g, if byte 0 used %.3g" % (opsel, opsel, e_sel, e_b0))
+    assert min(e_sel, e_b0) < 1e-5
+
+
+def test_bf16_mfma_layout(lib):
+    rng = np.random.default_rng(5)
+    n_waves = 16
+    a = torch.randn(n_waves, 64, 8).to(torch.bfloat16)
+    b = torch.randn(n_waves, 64, 8).to(torch.bfloat16)
+    d = torch.zeros((n_waves, 64, 16), dtype=torch.float32, device="cuda")
+    ta, tb = a.cuda(), b.cuda()
+    assert lib.probe_mfma_bf16_32x32x16(ta.data_ptr(), tb.data_ptr(), d.data_ptr(), n_waves,
+                                        _stream()) == 0
+    torch.cuda.synchronize()
+    af, bf, dd = a.double().numpy(), b.double().numpy(), d.cpu().numpy()
+    for w in range(n_waves):
+        A = np.zeros((32, 16))
+        Bm = np.zeros((16, 32))
+        for l in range(64):
+            A[l % 32, 8 * (l // 32):8 * (l // 32) + 8] = af[w, l]
+            Bm[8 * (l // 32):8 * (l // 32) + 8, l % 32] = bf[w, l]
+        ref = A @ Bm
+        got = np.zeros_like(ref)
+        for l in range(64):
+            for r in range(16):
+                m, n = _acc_index(32, l, r)
+                got[m, n] = dd[w, l, r]
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
+    del rng
+
+
+def _cvt_inputs():
+    rng = np.random.default_rng(17)
+    pts = [0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0]
+    bits = []
+    for p in pts:
+        c = int(np.array([p], dtype=np.float32).view(np.uint32)[0])
+        bits.append(np.arange(c - 2048, c + 2048, dtype=np.int64).astype(np.uint32))
+    bits.append(rng.integers(0, 0x41000000, size=1 << 16, dtype=np.uint32))
+    bits.append(np.array([0, 0x41000000, 0x42000000], dtype=np.uint32))   # 0, 8, 32
+    y = np.concatenate(bits).view(np.float32)
+    y = np.concatenate([y, -y])
+    if y.size % 2:
+        y = y[:-1]
+    return y
+
+
+@pytest.mark.parametrize("sel", [0, 1, 2, 3])
+def test_cvt_pk_fp4_rounding_matches_oracle(lib, sel):
+    y = _cvt_inputs()                      # values already divided by the scale
+    n = y.size // 2
+    rng = np.random.default_rng(sel)
+    k = rng.integers(-100, 101, size=n)    # normal power-of-two scales
+    scale = np.exp2(k).astype(np.float32)
+    x = (y.reshape(n, 2).astype(np.float64) * scale[:, None]).astype(np.float32)
+    tx, ts = torch.from_numpy(x).cuda(), torch.from_numpy(scale).cuda()
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    assert lib.probe_cvt_pk_fp4(tx.data_ptr(), ts.data_ptr(), out.data_ptr(), n, sel,
+                                _stream()) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint32)
+    byte = (o >> (8 * sel)) & 0xFF
+    got = np.stack([byte & 0xF, byte >> 4], axis=1).astype(np.uint8)
+    # exact quotient x / scale (power-of-two scale) rounded by the oracle's encoder
+    want = oracle.e2m1_encode_array(x.astype(np.float64) / scale[:, None].astype(np.float64))
+    other = o & ~np.uint32(0xFF << (8 * sel))
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    _dump("cvt_fp4_sel%d" % sel, x=x, scale=scale, out=o)
+    assert bad.size == 0, [(x[i], scale[i], got[i], want[i]) for i in bad[:8]]
+    assert not other.any(), "bytes other than the selected one were written"
+
+
+def test_cvt_pk_fp4_small_scales_report(lib):
+    """Scales 2^-127 (denormal) .. 2^-120: reported, the kernel's P path avoids relying on them."""
+    e = np.arange(-127, -119)
+    scale = np.exp2(e.astype(np.float64)).astype(np.float32)
+    x = np.stack([scale * 4.0, scale * 1.0], axis=1).astype(np.float32)
+    tx, ts = torch.from_numpy(x).cuda(), torch.from_numpy(scale).cuda()
+    out = torch.zeros(e.size, dtype=torch.int32, device="cuda")
+    assert lib.probe_cvt_pk_fp4(tx.data_ptr(), ts.data_ptr(), out.data_ptr(), e.size, 0,
+                                _stream()) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint32) & 0xFF
+    print("small-scale converts (want 0x26):", [hex(v) for v in o])
+
+
+def _time(fn, reps=3):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps * 1e-3
+
+
+def test_issue_rates_report(lib):
+    n_blocks, iters = 256 * 8, 2000
+    out = torch.zeros(n_blocks * 256, device="cuda")
+    t = _time(lambda: lib.probe_exp2_rate(out.data_ptr(), n_blocks, iters, _stream()))
+    exps = n_blocks * 256 * iters * 8
+    per_cu_clk = exps / t / 256 / 2.4e9
+    print("v_exp_f32: %.3g /s = %.1f lanes per CU per clock at 2.4 GHz" % (exps / t, per_cu_clk))
+    n_blocks, iters = 256 * 2, 200
+    t = _time(lambda: lib.probe_mfma_rate(out.data_ptr(), n_blocks, iters, _stream()))
+    mfmas = n_blocks * 4 * iters * 4
+    flops = mfmas * 2 * 32 * 32 * 64
+    print("fp4 32x32x64 MFMA: %.3g TFLOP/s (%.1f%% of 10.066 PFLOP/s), %.1f cycles per MFMA per SIMD"
+          % (flops / t / 1e12, flops / t / 10.066e15 * 100, t * 2.4e9 * 1024 / mfmas))
+    assert per_cu_clk > 4 and flops / t > 1e15
