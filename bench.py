@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 FlashAttention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: the Qwen3-8B-shaped causal prefill layer (B=1, 32 query
+heads, 8 KV heads, d=128, S=4096, bf16 inputs after synthetic RoPE, 4 outlier
+key channels per head, calibration-static smoothing).  One step is one pass of
+the whole hot path over that batch: Smooth-QK + MXFP4 quantisation of Q, K, V
+(one launch) and the fused MXFP4 attention (one launch), inputs resident in
+HBM.  `value` = algorithmic attention flops (4 d per unmasked query-key pair)
+per second of step time.
+
+Also reported (in "extra"): the attention kernel alone, the quantise kernel's
+GB/s, the split-K decode on 64 sequences with 1k-32k MXFP4 cache entries (HBM
+GB/s, split + merge), and the bf16 FlashAttention baseline on the same prefill
+(time ratio = the measured counterpart of the pages' projected latency cut).
+
+`roofline` is for the dominant kernel (the fused prefill attention), timed
+with HIP events on the stream it is launched on; `traffic` comes from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/ when that summary was
+taken on the current kernel source, else null.  `cpu_baseline` times the CPU
+oracle (test infrastructure) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MXFP4_PEAK_TFLOPS = 10066.0   # MI355X dense FP4 (spec)
+BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0
+METRIC = "attention TFLOPS (prefill) and HBM GB/s (decode) vs MI355X MXFP4 roofline"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_prefill_mxfp4_qwen3_8b_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "bit_flashattention_hifa4_amd", "csrc", "attn_mxfp4.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per prefill launch from the committed rocprofv3 counter summary, if current."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def time_events(fn, n, torch):
+    """Run fn n times, each bracketed by HIP events on the current stream; returns ms list."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(W, cfg, inp):
+    """The oracle on a bounded sample of the prefill workload: 2 query heads (one KV head).
+
+    Includes the oracle's quantisation of the sample's Q rows and of that KV head's K / V.
+    """
+    import numpy as np
+    import oracle
+
+    heads = [0, 1]
+    qs = W.to_f32(inp["q"][:, heads])
+    ks = W.to_f32(inp["k"][:, :1])
+    vs = W.to_f32(inp["v"][:, :1])
+    sm = inp["smooth"][:1] if inp["smooth"] is not None else None
+    nthreads = oracle.default_threads()
+    t0 = time.perf_counter()
+    qq = oracle.quantize_qkv(qs, ks, vs, sm)
+    oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=cfg.causal, bc=64,
+                     quant_p=True, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    pairs = cfg.S * (cfg.S + 1) // 2 if cfg.causal else cfg.S * cfg.S
+    flops = 4.0 * cfg.d * pairs * len(heads)
+    del np
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": "%s, query heads %s of batch 0 (one KV head): MXFP4 quantisation of the "
+                      "sample + online-softmax attention with P-Reordering, fp64, %.1f s"
+                      % (cfg.name, heads, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the attention path has no "
+              "multi-GPU leg); got --gpus %d, WORLD_SIZE %d" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_flashattention_hifa4_amd import binding as hb
+    from bit_flashattention_hifa4_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hb.load_library()
+    dev = torch.device("cuda:0")
+    cfg = W.QWEN3_8B
+    log("generating", cfg.name)
+    inp = W.prefill_inputs(cfg)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    smooth = torch.from_numpy(inp["smooth"]).to(dev)
+    mx = hb.alloc_mx(cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.S, cfg.d, device=dev)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.S, cfg.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.S), dtype=torch.float32, device=dev)
+    flops = cfg.flops()
+
+    def quantise():
+        hb.hifa4_quantize_qkv(q, k, v, smooth, out=mx)
+
+    def attend():
+        hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse)
+
+    # ---- headline: K timed steps of (quantise + attention)
+    for _ in range(args.warmup):
+        quantise()
+        attend()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        quantise()
+        e1.record()
+        attend()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    a_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_avg = float(a_ms.mean())
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+    q_bytes = (cfg.B * (cfg.Hq + 2 * cfg.Hkv) * cfg.S * cfg.d) * (2 + 17 / 32) + cfg.Hkv * cfg.d * 4
+    log("step %.3f ms (quantise %.3f ms, attention %.3f ms): %.1f TFLOP/s step, %.1f attention"
+        % (ms_per_step, q_ms.mean(), attn_avg, value, achieved))
+
+    extra = {
+        "attention_ms_avg": attn_avg,
+        "attention_ms_p10_p50_p90": [float(np.percentile(a_ms, p)) for p in (10, 50, 90)],
+        "attention_tflops": achieved,
+        "quantize_ms_avg": float(q_ms.mean()),
+        "quantize_gbs": q_bytes / (q_ms.mean() * 1e-3) / 1e9,
+        "flops_per_step": flops,
+        "kernel_source_sha256_16": kernel_source_sha(),
+    }
+
+    # ---- bf16 FlashAttention baseline on the same inputs
+    if not args.no_bf16:
+        bout = torch.empty_like(out)
+        blse = torch.empty_like(lse)
+        f = lambda: hb.bf16_attn_fwd(q, k, v, causal=cfg.causal, out=bout, lse=blse)
+        for _ in range(3):
+            f()
+        b_ms = np.array(time_events(f, max(5, args.steps // 2), torch))
+        extra["bf16_attention_ms_avg"] = float(b_ms.mean())
+        extra["bf16_attention_tflops"] = flops / (b_ms.mean() * 1e-3) / 1e12
+        extra["bf16_fraction_of_bf16_peak"] = extra["bf16_attention_tflops"] / BF16_PEAK_TFLOPS
+        extra["mxfp4_over_bf16_latency_ratio"] = attn_avg / float(b_ms.mean())
+        log("bf16 baseline %.3f ms (%.1f TFLOP/s); MXFP4 / bf16 latency %.3f"
+            % (b_ms.mean(), extra["bf16_attention_tflops"], extra["mxfp4_over_bf16_latency_ratio"]))
+        del bout, blse
+
+    # ---- split-K decode against the long MXFP4 cache
+    if not args.no_decode:
+        extra.update(decode_leg(W, hb, torch, np, dev, args))
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(W, cfg, inp)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "S": cfg.S, "d": cfg.d, "causal": cfg.causal,
+                   "step": "hifa4_quantize_qkv + hifa4_attn_fwd", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MXFP4_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MXFP4_PEAK_TFLOPS,
+                     "traffic": read_traffic()},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def decode_leg(W, hb, torch, np, dev, args):
+    cfg = W.DECODE
+    lens = W.decode_lengths(cfg)
+    cap = int(-(-int(lens.max()) // 64) * 64)
+    log("building the decode cache: %d sequences, %d tokens" % (cfg.B, int(lens.sum())))
+    mx = hb.alloc_mx(cfg.B, cfg.Hq, cfg.Hkv, 1, cap, cfg.d, device=dev)
+    hb.hifa4_quantize_qkv(W.decode_q(cfg).to(dev), None, None, None, out=mx)
+    for b, L in enumerate(lens):
+        kk, vv = W.decode_kv(cfg, b, int(L))
+        sl = hb.MXQKV(None, None, mx.k_codes[b:b + 1], mx.k_scales[b:b + 1], mx.v_codes[b:b + 1],
+                      mx.v_scales[b:b + 1], 1, cfg.Hq, cfg.Hkv, 0, int(L), cfg.d, cap)
+        hb.hifa4_quantize_qkv(None, kk.to(dev), vv.to(dev), None, kv_stride=cap, out=sl)
+    mx.Sq, mx.Sk, mx.kv_stride = 1, cap, cap
+    lens_t = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = torch.empty((cfg.B, cfg.Hq, 1, cfg.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg.B, cfg.Hq, 1), dtype=torch.float32, device=dev)
+    p = hb.make_params(cfg.B, cfg.Hq, cfg.Hkv, 1, cap, cfg.d, causal=True, kv_stride=cap,
+                       kv_lens=lens_t)
+    ws = torch.empty(hb.hifa4_attn_workspace_size(p), dtype=torch.uint8, device=dev)
+    f = lambda: hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, out=out, lse=lse, workspace=ws)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    d_ms = np.array(time_events(f, max(10, args.steps), torch))
+    # algorithmic bytes: valid-token K (codes + scales), V blocks covering the valid
+    # tokens, bf16 Q and O
+    L = lens.astype(np.int64)
+    kv_bytes = cfg.Hkv * (L * (cfg.d // 2 + cfg.d // 32)).sum() \
+        + cfg.Hkv * (((L + 31) // 32) * 32 * (cfg.d // 2 + cfg.d // 32)).sum()
+    qo = 2 * cfg.B * cfg.Hq * cfg.d * 2
+    total = float(kv_bytes + qo)
+    gbs = total / (d_ms.mean() * 1e-3) / 1e9
+    log("decode %.3f ms: %.1f GB/s (%.1f%% of HBM peak)" % (d_ms.mean(), gbs, gbs / HBM_PEAK_GBS * 100))
+    return {"decode_workload": cfg.name, "decode_tokens": int(lens.sum()),
+            "decode_ms_avg": float(d_ms.mean()), "decode_bytes": total, "decode_gbs": gbs,
+            "decode_fraction_of_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
+if __name__ == "__main__":
+    main()

@@ -36,6 +36,11 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+// Products and sums are rounded separately unless fmaf is spelled out: the
+// softmax relies on fl(S * c) being the same value in the max and in the
+// block-scale exponent.
+#pragma clang fp contract(off)
+
 namespace hifa4 {
 
 namespace {
@@ -78,19 +83,29 @@ struct SoftmaxStep {
   float alpha;
 };
 
+//
+// The running max and the block scale of P are taken from the *rounded*
+// products fl(S * c): the row max is max_k fl(S_k * c) (rounding is monotone,
+// so this is fl(max_k S_k * c)), and the block maximum of P is
+// exp2(fl(bm * c) - m_new), which is exactly 1 for the block holding the row
+// max, as in exact arithmetic.  (Taking the block max from the fused
+// fma(S, c, -m) instead would see the product's rounding error: the row max
+// could come out as 1 - 2^-24, dropping that block's E8M0 exponent by one and
+// saturating its largest P to 0.75.)  The P elements themselves use the fused
+// form; the row max then lands within an ulp of 1 and rounds to E2M1 4.0.
 __device__ __forceinline__ SoftmaxStep softmax_step(float (&s)[32], float& m_run, float c) {
   float bm = s[0];
 #pragma unroll
   for (int k = 1; k < 32; k++) bm = fmaxf(bm, s[k]);
-  const float rm = fmaxf(bm, __shfl_xor(bm, 32));
-  const float m_new = fmaxf(m_run, rm * c);
+  const float bmc = bm * c;  // contraction is off in this file: a rounded product
+  const float m_new = fmaxf(m_run, fmaxf(bmc, __shfl_xor(bmc, 32)));
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   SoftmaxStep st;
   st.alpha = fast_exp2(m_run - m_use);
   float p[32];
 #pragma unroll
-  for (int k = 0; k < 32; k++) p[k] = fast_exp2(fmaf(s[k], c, -m_use));
-  const float pmax = fast_exp2(fmaf(bm, c, -m_use));
+  for (int k = 0; k < 32; k++) p[k] = fast_exp2(__builtin_fmaf(s[k], c, -m_use));
+  const float pmax = fast_exp2(bmc - m_use);
   const uint32_t sb = e8m0_from_amax(pmax);
   st.p_scale = (int)sb;
   st.p_codes = pack_p(p, e8m0_to_float(sb));

@@ -1,0 +1,222 @@
+"""Fused MXFP4 attention (prefill + split-K decode) and the bf16 baseline vs the oracle (GPU).
+
+Gate (per output element): |O_gpu - O_oracle| <= 2e-2 * max|V|, where the
+oracle runs the same quantised operands, the same key-tile frame and decode
+chunk (read from hifa4_attn_schedule) in fp64.  The bf16 baseline is gated
+against exact fp64 softmax attention at 1e-2 * max|V|.  Errors against exact
+attention are printed for the 4-bit path as well.
+
+Small cases compare every output; the full-size workloads (Qwen3-8B-,
+Llama-3.1-8B-, Gemma2-9B-shaped prefill and the 64-sequence decode) run in the
+benchmark's launch configuration and compare sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_flashattention_hifa4_amd import binding as hb
+from bit_flashattention_hifa4_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-2      # times max|V|, MXFP4 path vs the oracle
+BF16_TOL = 1e-2   # times max|V|, bf16 path vs exact attention
+LSE_TOL = 2e-2    # absolute, natural log units
+
+
+def _run_hifa4(inp, causal, kv_stride=0, out_dtype=torch.bfloat16):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    s = torch.from_numpy(inp["smooth"]).cuda() if inp["smooth"] is not None else None
+    mx = hb.hifa4_quantize_qkv(q, k, v, s, kv_stride=kv_stride)
+    out, lse = hb.hifa4_attn_fwd(mx, causal=causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    p = hb.make_params(mx.B, mx.Hq, mx.Hkv, mx.Sq, mx.Sk, mx.d, causal=causal,
+                       kv_stride=mx.kv_stride)
+    bc, chunk = hb.hifa4_attn_schedule(p)
+    return out.float().cpu().numpy(), lse.cpu().numpy(), bc, chunk
+
+
+def _oracle_quant(inp):
+    f = W.to_f32
+    return oracle.quantize_qkv(f(inp["q"]), f(inp["k"]), f(inp["v"]), inp["smooth"])
+
+
+def _check_rows(o_gpu, lse_gpu, ref, vmax, what):
+    err = np.abs(o_gpu - ref["o"])
+    worst = err.max() if err.size else 0.0
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isfinite(lse_gpu), fin), what + ": rows without keys differ"
+    lerr = np.abs(lse_gpu[fin] - ref["lse"][fin]).max() if fin.any() else 0.0
+    print("%s: max|O - oracle| = %.4g (bound %.4g), max|lse diff| = %.3g"
+          % (what, worst, O_TOL * vmax, lerr), flush=True)
+    assert worst <= O_TOL * vmax
+    assert lerr <= LSE_TOL
+
+
+SMALL = [
+    # B, Hq, Hkv, Sq, Sk, d, causal, dtype, smooth, kv_stride
+    (1, 4, 2, 200, 200, 128, True, "bf16", True, 0),
+    (2, 2, 1, 130, 300, 64, False, "bf16", False, 0),
+    (1, 8, 2, 257, 513, 256, True, "bf16", True, 600),
+    (1, 2, 2, 96, 40, 128, True, "bf16", False, 0),     # Sq > Sk: first rows see no key
+    (1, 3, 1, 33, 161, 64, True, "fp16", True, 0),
+    (2, 4, 4, 64, 64, 128, False, "bf16", True, 0),
+    (1, 1, 1, 5, 1, 128, False, "bf16", False, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(str(v) for v in c))
+def test_prefill_small_cases_match_oracle(case):
+    B, Hq, Hkv, Sq, Sk, d, causal, dt, sm, stride = case
+    print("prefill parity:", case, flush=True)
+    inp = W.random_case(B, Hq, Hkv, Sq, Sk, d, dtype=dt, seed=sum(case[:6]), rope_theta=1e4,
+                        n_outliers=2, smooth_alpha=0.5 if sm else None)
+    out_dt = torch.float16 if dt == "fp16" else torch.bfloat16
+    o, lse, bc, chunk = _run_hifa4(inp, causal, kv_stride=stride, out_dtype=out_dt)
+    assert chunk == 0
+    qq = _oracle_quant(inp)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=bc,
+                           quant_p=True)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    _check_rows(o, lse, ref, vmax, "case %s" % (case,))
+    # P-Reordering: every output row is a convex combination of the visible
+    # dequantised V rows (bf16 output rounding as slack)
+    vd = qq["v_deq"]
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Sq):
+                nv = min(Sk, i + Sk - Sq + 1) if causal else Sk
+                if nv <= 0:
+                    assert not o[b, h, i].any()
+                    continue
+                lo = vd[b, h // g, :nv].min(axis=0)
+                hi = vd[b, h // g, :nv].max(axis=0)
+                slack = 1e-2 * np.maximum(np.abs(lo), np.abs(hi)) + 1e-6
+                assert (o[b, h, i] >= lo - slack).all() and (o[b, h, i] <= hi + slack).all()
+
+
+def test_tiny_workload_all_outputs():
+    cfg = W.TINY
+    inp = W.prefill_inputs(cfg)
+    o, lse, bc, _ = _run_hifa4(inp, cfg.causal, out_dtype=torch.float16)
+    qq = _oracle_quant(inp)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=cfg.causal, bc=bc)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    _check_rows(o, lse, ref, vmax, cfg.name)
+    exact = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
+                             causal=cfg.causal, bc=bc, quant_p=False)
+    print("%s: max|O - exact attention| = %.4g" % (cfg.name, np.abs(o - exact["o"]).max()))
+
+
+def _sample_rows(B, Hq, Sq, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(B):
+        for h in (0, Hq - 1):
+            for i in (0, 1, Sq // 2, Sq - 1):
+                rows.add((b * Hq + h) * Sq + i)
+    rows.update(int(r) for r in rng.integers(0, B * Hq * Sq, size=n))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+FULL = [W.QWEN3_8B, W.LLAMA31_8B, W.GEMMA2_9B]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
+def test_prefill_full_size_sampled_rows(cfg):
+    print("full-size prefill parity:", cfg.name, flush=True)
+    inp = W.prefill_inputs(cfg)
+    o, lse, bc, _ = _run_hifa4(inp, cfg.causal)
+    qq = _oracle_quant(inp)
+    rows = _sample_rows(cfg.B, cfg.Hq, cfg.S, 192, seed=cfg.seed)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=cfg.causal, bc=bc,
+                           rows=rows)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    _check_rows(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], ref, vmax, cfg.name)
+    exact = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
+                             causal=cfg.causal, bc=bc, quant_p=False, rows=rows)
+    print("%s: sampled max|O - exact attention| = %.4g, rms %.4g" % (
+        cfg.name, np.abs(o.reshape(-1, cfg.d)[rows] - exact["o"]).max(),
+        np.sqrt(np.mean((o.reshape(-1, cfg.d)[rows] - exact["o"]) ** 2))))
+
+
+def _decode_case(cfg, lens, cap, chunk=0):
+    B, Hq, Hkv, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.d
+    mx = hb.alloc_mx(B, Hq, Hkv, 1, cap, d)
+    q = W.decode_q(cfg)
+    hb.hifa4_quantize_qkv(q.cuda(), None, None, None, out=mx)
+    for b, L in enumerate(lens):
+        if int(L) == 0:
+            continue
+        k, v = W.decode_kv(cfg, b, int(L))
+        sl = hb.MXQKV(None, None, mx.k_codes[b:b + 1], mx.k_scales[b:b + 1], mx.v_codes[b:b + 1],
+                      mx.v_scales[b:b + 1], 1, Hq, Hkv, 0, int(L), d, cap)
+        hb.hifa4_quantize_qkv(None, k.cuda(), v.cuda(), None, kv_stride=cap, out=sl)
+    mx.Sq, mx.Sk, mx.kv_stride = 1, cap, cap
+    lens_t = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    out, lse = hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, decode_chunk=chunk)
+    torch.cuda.synchronize()
+    p = hb.make_params(B, Hq, Hkv, 1, cap, d, causal=True, kv_stride=cap, decode_chunk=chunk)
+    bc, ch = hb.hifa4_attn_schedule(p)
+    return q, out.float().cpu().numpy(), lse.cpu().numpy(), bc, ch
+
+
+def _decode_oracle(cfg, q, b, L, bc, chunk):
+    k, v = W.decode_kv(cfg, b, int(L))
+    qq = oracle.quantize_qkv(W.to_f32(q[b:b + 1]), W.to_f32(k), W.to_f32(v), None)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=bc, chunk=chunk)
+    vmax = np.abs(W.to_f32(v)).max()
+    return ref, vmax
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 192])
+def test_decode_small_matches_oracle(chunk):
+    cfg = W.DecodeConfig("small_decode", 5, 8, 2, 128, 1, 700)
+    lens = [700, 1, 64, 65, 333]
+    print("decode parity: lens", lens, "chunk", chunk, flush=True)
+    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=704, chunk=chunk)
+    assert ch == (chunk or ch) and ch % bc == 0
+    for b, L in enumerate(lens):
+        ref, vmax = _decode_oracle(cfg, q, b, L, bc, ch)
+        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L))
+
+
+def test_decode_zero_length_sequence_gives_zero_rows():
+    cfg = W.DecodeConfig("zero_len", 2, 4, 1, 64, 0, 100)
+    q, o, lse, bc, ch = _decode_case(cfg, [0, 100], cap=128)
+    assert not o[0].any() and np.isneginf(lse[0]).all()
+    ref, vmax = _decode_oracle(cfg, q, 1, 100, bc, ch)
+    _check_rows(o[1:2], lse[1:2], ref, vmax, "decode L=100 next to L=0")
+
+
+def test_decode_full_size_sampled_sequences():
+    cfg = W.DECODE
+    lens = W.decode_lengths(cfg)
+    cap = int(-(-lens.max() // 64) * 64)
+    print("full-size decode parity: sum(L) =", int(lens.sum()), flush=True)
+    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=cap)
+    for b in (0, int(np.argmax(lens)), int(np.argmin(lens)), 37):
+        ref, vmax = _decode_oracle(cfg, q, b, lens[b], bc, ch)
+        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, lens[b]))
+
+
+@pytest.mark.parametrize("case", [
+    (1, 4, 2, 200, 200, 128, True),
+    (2, 2, 1, 130, 300, 64, False),
+    (1, 4, 2, 257, 300, 256, True),
+])
+def test_bf16_baseline_matches_exact_attention(case):
+    B, Hq, Hkv, Sq, Sk, d, causal = case
+    inp = W.random_case(B, Hq, Hkv, Sq, Sk, d, dtype="bf16", seed=7 + sum(case[:6]))
+    out, lse = hb.bf16_attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
+                           causal=causal, bc=64, quant_p=False)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    err = np.abs(out.float().cpu().numpy() - ref["o"]).max()
+    fin = np.isfinite(ref["lse"])
+    lerr = np.abs(lse.cpu().numpy()[fin] - ref["lse"][fin]).max()
+    print("bf16 %s: max|O - exact| = %.4g (bound %.4g), lse %.3g" % (case, err, BF16_TOL * vmax, lerr))
+    assert err <= BF16_TOL * vmax and lerr < 1e-2
