@@ -113,6 +113,10 @@ def _f32(x) -> np.ndarray:
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: OMP_NUM_THREADS when set (the CPU share), else all cores."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
     return max(1, os.cpu_count() or 1)
 
 
