@@ -142,8 +142,10 @@ def main():
     def quantise():
         hb.hifa4_quantize_qkv(q, k, v, smooth, out=mx)
 
+    tau = hb.RESCALE_THRESHOLD_FAST
+
     def attend():
-        hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse)
+        hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse, rescale_threshold=tau)
 
     # ---- headline: K timed steps of (quantise + attention)
     for _ in range(args.warmup):
@@ -186,7 +188,8 @@ def main():
     if not args.no_bf16:
         bout = torch.empty_like(out)
         blse = torch.empty_like(lse)
-        f = lambda: hb.bf16_attn_fwd(q, k, v, causal=cfg.causal, out=bout, lse=blse)
+        f = lambda: hb.bf16_attn_fwd(q, k, v, causal=cfg.causal, out=bout, lse=blse,
+                                     rescale_threshold=tau)
         for _ in range(3):
             f()
         b_ms = np.array(time_events(f, max(5, args.steps // 2), torch))
@@ -221,7 +224,7 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
-                   "S": cfg.S, "d": cfg.d, "causal": cfg.causal,
+                   "S": cfg.S, "d": cfg.d, "causal": cfg.causal, "rescale_threshold": tau,
                    "step": "hifa4_quantize_qkv + hifa4_attn_fwd", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MXFP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MXFP4_PEAK_TFLOPS,
@@ -251,7 +254,8 @@ def decode_leg(W, hb, torch, np, dev, args):
     p = hb.make_params(cfg.B, cfg.Hq, cfg.Hkv, 1, cap, cfg.d, causal=True, kv_stride=cap,
                        kv_lens=lens_t)
     ws = torch.empty(hb.hifa4_attn_workspace_size(p), dtype=torch.uint8, device=dev)
-    f = lambda: hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, out=out, lse=lse, workspace=ws)
+    f = lambda: hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, out=out, lse=lse, workspace=ws,
+                                  rescale_threshold=hb.RESCALE_THRESHOLD_FAST)
     for _ in range(5):
         f()
     torch.cuda.synchronize()

@@ -77,6 +77,8 @@ hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
   if (!supported_d(p->d)) return fail(HIFA4_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128, 256)", p->d);
   if (!std::isfinite(p->sm_scale))
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
+  if (!std::isfinite(p->rescale_threshold) || p->rescale_threshold < 0.0f)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "rescale_threshold must be finite and >= 0");
   *cap = p->kv_stride ? p->kv_stride : p->Sk;
   if (*cap < p->Sk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_stride %d < Sk %d", *cap, p->Sk);
   if (p->kv_lens && p->Sq != 1)
@@ -283,6 +285,7 @@ hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4
   a.sm_log2 = a.sm_scale * 1.4426950408889634f;
   a.chunk = chunk;
   a.n_chunks = chunk ? (cap + chunk - 1) / chunk : 0;
+  a.tau = p->rescale_threshold;
   hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
                             : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported)
@@ -337,6 +340,7 @@ hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void
   a.causal = p->causal ? 1 : 0;
   const float sm = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)d);
   a.sm_log2 = sm * 1.4426950408889634f;
+  a.tau = p->rescale_threshold;
   hipError_t e = hifa4::launch_attn_prefill_bf16(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return fail(HIFA4_ERR_UNSUPPORTED, "no kernel for this configuration");
   return hip_status(e, "bf16 attention launch");

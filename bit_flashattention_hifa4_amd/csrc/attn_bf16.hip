@@ -140,8 +140,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
     float bm = s[0];
 #pragma unroll
     for (int k = 1; k < 32; k++) bm = fmaxf(bm, s[k]);
-    const float rm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, rm * c);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
+                                                     false, false);
+    const float rmc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    // lazy rescale (same rule as the MXFP4 kernel; exact attention is frame-free)
+    const float m_new = rmc > m_run + a.tau ? rmc : m_run;
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float p[32];
@@ -151,11 +154,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
       p[k] = __builtin_amdgcn_exp2f(fmaf(s[k], c, -m_use));
       ps += p[k];
     }
-    ps += __shfl_xor(ps, 32);
+    {
+      const auto pw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps),
+                                                       false, false);
+      ps = __uint_as_float(pw[0]) + __uint_as_float(pw[1]);
+    }
     l_run = alpha * l_run + ps;
     m_run = m_new;
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int cc = 0; cc < NC; cc++) acc[cc] *= alpha;
+      for (int cc = 0; cc < NC; cc++) acc[cc] *= alpha;
+    }
     // P V: 4 MFMAs of 16 keys; MFMA u = 2t + j2 takes registers 8*j2 .. +7 of tile t
 #pragma unroll
     for (int u = 0; u < 4; u++) {

@@ -84,21 +84,39 @@ struct SoftmaxStep {
 };
 
 //
+// Lazy rescale: the running max m moves to the tile's row max only when that
+// exceeds m by more than tau (log2 units); otherwise the frame is kept and P
+// may reach 2^tau.  tau = 0 is the FlashAttention-2 frame (P <= 1).  Exact
+// attention does not depend on the frame; P_hat does, so tau is part of the
+// operator's definition (the oracle takes the same value).
+//
 // The running max and the block scale of P are taken from the *rounded*
 // products fl(S * c): the row max is max_k fl(S_k * c) (rounding is monotone,
 // so this is fl(max_k S_k * c)), and the block maximum of P is
 // exp2(fl(bm * c) - m_new), which is exactly 1 for the block holding the row
-// max, as in exact arithmetic.  (Taking the block max from the fused
-// fma(S, c, -m) instead would see the product's rounding error: the row max
-// could come out as 1 - 2^-24, dropping that block's E8M0 exponent by one and
-// saturating its largest P to 0.75.)  The P elements themselves use the fused
-// form; the row max then lands within an ulp of 1 and rounds to E2M1 4.0.
-__device__ __forceinline__ SoftmaxStep softmax_step(float (&s)[32], float& m_run, float c) {
+// max when the frame moves to it, as in exact arithmetic.  (Taking it from the
+// fused fma(S, c, -m) instead would see the product's rounding error: the row
+// max could come out as 1 - 2^-24, dropping that block's E8M0 exponent by one
+// and saturating its largest P to 0.75.)  The P elements themselves use the
+// fused form; the row max then lands within an ulp of 1 and rounds to 4.0.
+//
+// The row max needs the partner lane l ^ 32 (the other 32 keys of the step):
+// v_permlane32_swap exchanges the two halves of the wave in one VALU op, and
+// the max of its two results is max(own, partner) in every lane.
+__device__ __forceinline__ float max_with_half_swap(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ SoftmaxStep softmax_step(float (&s)[32], float& m_run, float c,
+                                                    float tau) {
   float bm = s[0];
 #pragma unroll
   for (int k = 1; k < 32; k++) bm = fmaxf(bm, s[k]);
   const float bmc = bm * c;  // contraction is off in this file: a rounded product
-  const float m_new = fmaxf(m_run, fmaxf(bmc, __shfl_xor(bmc, 32)));
+  const float rmc = max_with_half_swap(bmc);
+  const float m_new = rmc > m_run + tau ? rmc : m_run;
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   SoftmaxStep st;
   st.alpha = fast_exp2(m_run - m_use);
@@ -136,18 +154,195 @@ __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row, int h,
 
 // ---------------------------------------------------------------------------
 // Prefill: one workgroup = 128 queries of one (batch, query head); 4 waves of
-// 32 queries share K / V tiles staged in LDS.
+// 32 queries share 64-key K / V tiles staged in LDS.
+//
+// Software pipeline.  Step kt of a wave issues the Q K^T MFMAs of tile kt+1
+// first, then runs the softmax of tile kt (whose scores came out of the
+// previous step) and its P V MFMAs: the matrix core computes the next scores
+// while the vector ALU does the exponentials and FP4 conversions.  K is
+// therefore staged one tile ahead of V: during step kt the LDS holds K of
+// tile kt+1 and V of tile kt, and the bytes of K tile kt+2 / V tile kt+1 are
+// in flight into registers; they are written to the free buffers at the end
+// of the step and one barrier per step publishes them.
+//
+// K rows are stored in LDS in the order the MFMA A operand reads them (row
+// 32t + n of a buffer holds key perm_row(t, n)) with a padded stride of
+// d/2 + 16 bytes, so the 16-byte reads of 8 neighbouring lanes fall in
+// distinct bank groups.
 // ---------------------------------------------------------------------------
+template <int D>
+struct PrefillTile {
+  static constexpr int DB = D / 2;               // code bytes per K row
+  static constexpr int DS = D / 32;              // scale bytes per K row
+  static constexpr int RS = DB + 16;             // padded LDS stride of a K row
+  static constexpr int KC = kBN * DB / 16;       // 16-byte K code chunks per tile
+  static constexpr int VC = 2 * D;               // 16-byte V code chunks per tile
+  static constexpr int KC_T = (KC + 255) / 256;  // per thread
+  static constexpr int VC_T = (VC + 255) / 256;
+  static constexpr int VS_W = 2 * D / 4;         // 4-byte V scale words per tile
+  static constexpr int LDS_K = kBN * RS + kBN * DS;   // codes + scales of one K tile
+  static constexpr int LDS_V = VC * 16 + 2 * D;       // codes + scales of one V tile
+};
+
+// LDS row of key r in the read order of the QK A operand.
+__device__ __forceinline__ int k_lds_row(int r) {
+  return 32 * ((r >> 4) & 1) + 8 * ((r >> 2) & 3) + 4 * (r >> 5) + (r & 3);
+}
+
+template <int D>
+struct KRegs {
+  uint4 kc[PrefillTile<D>::KC_T];
+  uint2 ks;  // DS scale bytes of one K row (threads < 64)
+};
+
+template <int D>
+struct VRegs {
+  uint4 vc[PrefillTile<D>::VC_T];
+  uint32_t vs;  // one 4-byte word of V scales
+};
+
+// Global loads of a 64-key tile starting at n0.  Rows / blocks past the valid
+// keys are clamped to the last valid one (finite data); their scores are
+// masked and their P is zero, so they never contribute.
+template <int D>
+__device__ __forceinline__ void load_k(const AttnArgs& a, int64_t bkv, int n0, int L, int tid,
+                                       KRegs<D>& r) {
+  using T = PrefillTile<D>;
+#pragma unroll
+  for (int i = 0; i < T::KC_T; i++) {
+    const int ci = tid + 256 * i;
+    if (ci < T::KC) {
+      const int row = ci / (T::DB / 16), off = (ci % (T::DB / 16)) * 16;
+      const int key = min(n0 + row, L - 1);
+      r.kc[i] = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + key) * T::DB + off);
+    }
+  }
+  if (tid < kBN) {
+    const int key = min(n0 + tid, L - 1);
+    const uint8_t* src = a.k_scales + (bkv * a.cap + key) * T::DS;
+    if constexpr (T::DS == 2) {
+      r.ks = make_uint2(*reinterpret_cast<const uint16_t*>(src), 0);
+    } else if constexpr (T::DS == 4) {
+      r.ks = make_uint2(*reinterpret_cast<const uint32_t*>(src), 0);
+    } else {
+      r.ks = *reinterpret_cast<const uint2*>(src);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(const AttnArgs& a, int64_t bkv, int n0, int nblk_valid,
+                                       int nblk_cap, int tid, VRegs<D>& r) {
+  using T = PrefillTile<D>;
+#pragma unroll
+  for (int i = 0; i < T::VC_T; i++) {
+    const int ci = tid + 256 * i;
+    if (ci < T::VC) {
+      const int blk = ci / D, ch = ci % D;
+      const int gb = min(n0 / 32 + blk, nblk_valid - 1);
+      r.vc[i] = *reinterpret_cast<const uint4*>(a.v_codes + ((bkv * nblk_cap + gb) * D + ch) * 16);
+    }
+  }
+  if (tid < T::VS_W) {
+    const int blk = (tid * 4) / D, off = (tid * 4) % D;
+    const int gb = min(n0 / 32 + blk, nblk_valid - 1);
+    r.vs = *reinterpret_cast<const uint32_t*>(a.v_scales + (bkv * nblk_cap + gb) * D + off);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(uint8_t* buf, int tid, const KRegs<D>& r) {
+  using T = PrefillTile<D>;
+  uint8_t* ks = buf + kBN * T::RS;
+#pragma unroll
+  for (int i = 0; i < T::KC_T; i++) {
+    const int ci = tid + 256 * i;
+    if (ci < T::KC) {
+      const int row = ci / (T::DB / 16), off = (ci % (T::DB / 16)) * 16;
+      *reinterpret_cast<uint4*>(buf + k_lds_row(row) * T::RS + off) = r.kc[i];
+    }
+  }
+  if (tid < kBN) {
+    uint8_t* dst = ks + k_lds_row(tid) * T::DS;
+    if constexpr (T::DS == 2) {
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)r.ks.x;
+    } else if constexpr (T::DS == 4) {
+      *reinterpret_cast<uint32_t*>(dst) = r.ks.x;
+    } else {
+      *reinterpret_cast<uint2*>(dst) = r.ks;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_v(uint8_t* buf, int tid, const VRegs<D>& r) {
+  using T = PrefillTile<D>;
+#pragma unroll
+  for (int i = 0; i < T::VC_T; i++) {
+    const int ci = tid + 256 * i;
+    if (ci < T::VC) *reinterpret_cast<uint4*>(buf + ci * 16) = r.vc[i];
+  }
+  if (tid < T::VS_W) *reinterpret_cast<uint32_t*>(buf + T::VC * 16 + tid * 4) = r.vs;
+}
+
+// Scale operand of K block (2j + h) of a row whose DS scale bytes start at p:
+// the 32-bit word holding it, shifted by 8h so that byte 2*(j%2) is the one.
+template <int DS>
+__device__ __forceinline__ int k_scale_word(const uint8_t* p, int j, int h) {
+  if constexpr (DS == 2) {
+    return (int)(*reinterpret_cast<const uint16_t*>(p) >> (8 * h));
+  } else {
+    return (int)(reinterpret_cast<const uint32_t*>(p)[j >> 1] >> (8 * h));
+  }
+}
+
+template <int OPSEL>
+__device__ __forceinline__ v16f mfma_fp4_sel(const uint4& a, const uint4& b, const v16f& c, int sa,
+                                             int sb) {
+  v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v8i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, kFmtFp4, kFmtFp4, OPSEL, sa,
+                                                         OPSEL, sb);
+}
+
+// S^T = K Q^T for the two 32-key tiles of a 64-key step held in one K buffer.
+template <int D>
+__device__ __forceinline__ void qk_step(const uint8_t* kbuf, const uint4 (&qa)[D / 64],
+                                        const int (&qsw)[(D / 64 + 1) / 2], int n, int h,
+                                        v16f& s0, v16f& s1) {
+  using T = PrefillTile<D>;
+  constexpr int NJ = D / 64;
+  const uint8_t* ks = kbuf + kBN * T::RS;
+  s0 = v16f{};
+  s1 = v16f{};
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
+    const uint4 k0 = *reinterpret_cast<const uint4*>(kbuf + n * T::RS + 32 * j + 16 * h);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(kbuf + (32 + n) * T::RS + 32 * j + 16 * h);
+    const int ks0 = k_scale_word<T::DS>(ks + n * T::DS, j, h);
+    const int ks1 = k_scale_word<T::DS>(ks + (32 + n) * T::DS, j, h);
+    if (j % 2 == 0) {
+      s0 = mfma_fp4_sel<0>(k0, qa[j], s0, ks0, qsw[j / 2]);
+      s1 = mfma_fp4_sel<0>(k1, qa[j], s1, ks1, qsw[j / 2]);
+    } else {
+      s0 = mfma_fp4_sel<2>(k0, qa[j], s0, ks0, qsw[j / 2]);
+      s1 = mfma_fp4_sel<2>(k1, qa[j], s1, ks1, qsw[j / 2]);
+    }
+  }
+}
+
+template <int D>
+constexpr int prefill_min_blocks() { return D >= 256 ? 1 : 2; }
+
 template <int D, bool kCausal>
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ones_scale) {
-  constexpr int DB = D / 2;   // code bytes per Q / K row
-  constexpr int DS = D / 32;  // scale bytes per Q / K row
+__global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_kernel(
+    AttnArgs a, int ones_scale) {
+  using T = PrefillTile<D>;
+  constexpr int DB = T::DB, DS = T::DS;
   constexpr int NJ = D / 64;  // QK MFMAs per 32-key tile
   constexpr int NC = D / 32;  // P V channel tiles
-  __shared__ __attribute__((aligned(16))) uint8_t lds_kc[kBN * DB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_ks[kBN * DS];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_vc[2 * D * 16];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_vs[2 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2 * T::LDS_K];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * T::LDS_V];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -175,23 +370,22 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int on
   const int nblk_valid = (L + 31) / 32;
   const int nblk_cap = (a.cap + 31) / 32;
 
-  // Q operand (B of S^T = K Q^T): query q, K blocks of 32 along d.
+  // Q operand (B of S^T = K Q^T): query q, K blocks of 32 along d; its scale
+  // bytes packed so that MFMA j reads byte 2*(j%2) of word j/2.
   uint4 qa[NJ];
-  int qs[NJ];
+  int qsw[(NJ + 1) / 2];
   if (q < a.Sq) {
     const uint8_t* qc = a.q_codes + (bhq * a.Sq + q) * DB;
     const uint8_t* qsc = a.q_scales + (bhq * a.Sq + q) * DS;
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
-      qs[j] = qsc[2 * j + h];
-    }
+    for (int j = 0; j < NJ; j++) qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
+#pragma unroll
+    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = k_scale_word<DS>(qsc, j, h);
   } else {
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      qa[j] = make_uint4(0, 0, 0, 0);
-      qs[j] = 0;
-    }
+    for (int j = 0; j < NJ; j++) qa[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = 0;
   }
 
   // Key ranges: the workgroup stages every tile any of its rows can see; a
@@ -219,87 +413,79 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int on
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
   v16f accl = v16f{};
 
-  for (int kt = 0; kt < n_tiles; kt++) {
+  // prologue: K tiles 0 and 1, V tile 0; scores of tile 0
+  KRegs<D> kpre;
+  VRegs<D> vpre;
+  if (n_tiles > 0) {
+    load_k<D>(a, bkv, 0, L, tid, kpre);
+    load_v<D>(a, bkv, 0, nblk_valid, nblk_cap, tid, vpre);
+    store_k<D>(lds_k, tid, kpre);
+    store_v<D>(lds_v, tid, vpre);
+    if (n_tiles > 1) {
+      load_k<D>(a, bkv, kBN, L, tid, kpre);
+      store_k<D>(lds_k + T::LDS_K, tid, kpre);
+    }
+  }
+  __syncthreads();
+
+  // One pipeline step: scores of tile kt are in (c0, c1); the next tile's go
+  // to (n0r, n1r).  The loop below alternates the two register sets, so no
+  // copies are needed; registers of a tile a wave does not compute are never
+  // read (the softmax of that tile is skipped as well).
+  auto step = [&](int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
     const int n0 = kt * kBN;
-    __syncthreads();
-    // ---- stage K codes / scales and V codes / scales of keys n0 .. n0+63
-    for (int ci = tid; ci < kBN * DB / 16; ci += 256) {
-      const int row = ci / (DB / 16), off = (ci % (DB / 16)) * 16;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (n0 + row < L)
-        w = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + n0 + row) * DB + off);
-      *reinterpret_cast<uint4*>(lds_kc + row * DB + off) = w;
-    }
-    if (tid < kBN) {
-      const int row = tid;
-      const bool ok = n0 + row < L;
-      const uint8_t* src = a.k_scales + (bkv * a.cap + n0 + row) * DS;
-      if constexpr (DS == 2) {
-        *reinterpret_cast<uint16_t*>(lds_ks + row * DS) = ok ? *reinterpret_cast<const uint16_t*>(src) : 0;
-      } else if constexpr (DS == 4) {
-        *reinterpret_cast<uint32_t*>(lds_ks + row * DS) = ok ? *reinterpret_cast<const uint32_t*>(src) : 0;
-      } else {
-        *reinterpret_cast<uint2*>(lds_ks + row * DS) = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+    const bool more_k = kt + 2 < n_tiles, more_v = kt + 1 < n_tiles;
+    if (more_k) load_k<D>(a, bkv, n0 + 2 * kBN, L, tid, kpre);
+    if (more_v) load_v<D>(a, bkv, n0 + kBN, nblk_valid, nblk_cap, tid, vpre);
+
+    // scores of the next tile go to the matrix core first
+    if (more_v && n0 + kBN < wave_end)
+      qk_step<D>(lds_k + ((kt + 1) & 1) * T::LDS_K, qa, qsw, n, h, n0r, n1r);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (n0 < wave_end) {  // uniform per wave
+      float s[32];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        s[r] = c0[r];
+        s[16 + r] = c1[r];
       }
+      if (n0 + kBN > wave_full) {
+        const int kb = n0 + 32 * h;
+#pragma unroll
+        for (int k = 0; k < 32; k++)
+          if (kb + k >= row_lim) s[k] = -INFINITY;
+      }
+
+      const SoftmaxStep st = softmax_step(s, m_run, c, a.tau);
+      // rescale only when some row's max moved (multiplying by 1 is exact)
+      if (__any(st.alpha != 1.0f)) {
+#pragma unroll
+        for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
+        accl[0] *= st.alpha;
+      }
+
+      // ---- [acc | l] += P_hat [V | 1]
+      const uint8_t* vbuf = lds_v + (kt & 1) * T::LDS_V;
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) {
+        const int ch = 32 * cc + n;
+        const uint4 va = *reinterpret_cast<const uint4*>(vbuf + (h * D + ch) * 16);
+        const int vs = vbuf[T::VC * 16 + h * D + ch];
+        acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
+      }
+      accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
     }
-    for (int ci = tid; ci < 2 * D; ci += 256) {
-      const int blk = ci / D, ch = ci % D;
-      const int gb = n0 / 32 + blk;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (gb < nblk_valid)
-        w = *reinterpret_cast<const uint4*>(a.v_codes + ((bkv * nblk_cap + gb) * D + ch) * 16);
-      *reinterpret_cast<uint4*>(lds_vc + ci * 16) = w;
-    }
-    for (int ci = tid; ci < 2 * D / 16; ci += 256) {
-      const int blk = (ci * 16) / D, off = (ci * 16) % D;
-      const int gb = n0 / 32 + blk;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (gb < nblk_valid)
-        w = *reinterpret_cast<const uint4*>(a.v_scales + (bkv * nblk_cap + gb) * D + off);
-      *reinterpret_cast<uint4*>(lds_vs + ci * 16) = w;
-    }
+    if (more_k) store_k<D>(lds_k + (kt & 1) * T::LDS_K, tid, kpre);
+    if (more_v) store_v<D>(lds_v + ((kt + 1) & 1) * T::LDS_V, tid, vpre);
     __syncthreads();
-    if (n0 >= wave_end) continue;  // uniform per wave
+  };
 
-    // ---- S^T = K Q^T for the two 32-key tiles
-    v16f s0 = v16f{}, s1 = v16f{};
-    const int r0 = perm_row(0, n), r1 = perm_row(1, n);
-#pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      const uint4 k0 = *reinterpret_cast<const uint4*>(lds_kc + r0 * DB + 32 * j + 16 * h);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(lds_kc + r1 * DB + 32 * j + 16 * h);
-      const int ks0 = lds_ks[r0 * DS + 2 * j + h];
-      const int ks1 = lds_ks[r1 * DS + 2 * j + h];
-      s0 = mfma_fp4_32x32x64(k0, qa[j], s0, ks0, qs[j]);
-      s1 = mfma_fp4_32x32x64(k1, qa[j], s1, ks1, qs[j]);
-    }
-    float s[32];
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      s[r] = s0[r];
-      s[16 + r] = s1[r];
-    }
-    if (n0 + kBN > wave_full) {
-      const int kb = n0 + 32 * h;
-#pragma unroll
-      for (int k = 0; k < 32; k++)
-        if (kb + k >= row_lim) s[k] = -INFINITY;
-    }
-
-    const SoftmaxStep st = softmax_step(s, m_run, c);
-#pragma unroll
-    for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
-    accl[0] *= st.alpha;
-
-    // ---- [acc | l] += P_hat [V | 1]
-#pragma unroll
-    for (int cc = 0; cc < NC; cc++) {
-      const int ch = 32 * cc + n;
-      const uint4 va = *reinterpret_cast<const uint4*>(lds_vc + (h * D + ch) * 16);
-      const int vs = lds_vs[h * D + ch];
-      acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
-    }
-    accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
+  v16f sa0, sa1, sb0, sb1;
+  if (0 < wave_end) qk_step<D>(lds_k, qa, qsw, n, h, sa0, sa1);
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    step(kt, sa0, sa1, sb0, sb1);
+    if (kt + 1 < n_tiles) step(kt + 1, sb0, sb1, sa0, sa1);
   }
 
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
@@ -397,10 +583,12 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
       for (int k = 0; k < 32; k++)
         if (kb + k >= s1) s[k] = -INFINITY;
     }
-    const SoftmaxStep st = softmax_step(s, m_run, c);
+    const SoftmaxStep st = softmax_step(s, m_run, c, a.tau);
+    if (__any(st.alpha != 1.0f)) {
 #pragma unroll
-    for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
-    accl[0] *= st.alpha;
+      for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
+      accl[0] *= st.alpha;
+    }
     const int gb = n0 / 32 + h;
 #pragma unroll
     for (int cc = 0; cc < NC; cc++) {

@@ -44,6 +44,7 @@ struct AttnArgs {
   float sm_scale;
   int chunk;               // decode chunk (tokens)
   int n_chunks;            // ceil(cap / chunk)
+  float tau;               // lazy-rescale threshold, log2 units (0 = every increase)
 };
 
 // Key tile width of the online-softmax frame for a head dim.
@@ -63,6 +64,7 @@ struct Bf16AttnArgs {
   int B, Hq, Hkv, Sq, Sk, d, cap;
   int causal;
   float sm_log2;
+  float tau;
 };
 
 hipError_t launch_attn_prefill_bf16(const Bf16AttnArgs& a, hipStream_t stream);

@@ -62,6 +62,15 @@ __global__ __launch_bounds__(64) void mfma_bf16_32_kernel(const uint4* a, const 
   for (int r = 0; r < 16; r++) d[(w * 64 + l) * 16 + r] = c[r];
 }
 
+__global__ __launch_bounds__(64) void half_swap_kernel(const float* x, float* out) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  const float v = x[i];
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  out[2 * i] = __uint_as_float(r[0]);
+  out[2 * i + 1] = __uint_as_float(r[1]);
+}
+
 template <int kSel>
 __global__ void cvt_fp4_kernel(const float2* x, const float* scale, uint32_t* out, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -162,6 +171,12 @@ int probe_cvt_pk_fp4(const float* x, const float* scale, uint32_t* out, int n, i
     case 2: hipLaunchKernelGGL(cvt_fp4_kernel<2>, g, t, 0, s, X, scale, out, n); break;
     default: hipLaunchKernelGGL(cvt_fp4_kernel<3>, g, t, 0, s, X, scale, out, n); break;
   }
+  return status(hipGetLastError());
+}
+
+int probe_half_swap(const float* x, float* out, int n_waves, void* stream) {
+  if (n_waves <= 0) return -1;
+  hipLaunchKernelGGL(half_swap_kernel, dim3(n_waves), dim3(64), 0, (hipStream_t)stream, x, out);
   return status(hipGetLastError());
 }
 

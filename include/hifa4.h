@@ -82,6 +82,11 @@ typedef struct hifa4_attn_params {
   const int32_t* kv_lens; /* device [B] per-sequence key count L (<= Sk), or NULL (L = Sk);
                              only with Sq == 1 */
   int32_t decode_chunk;   /* split-K chunk in tokens (multiple of the key tile); 0 = library's choice */
+  float rescale_threshold;  /* log2 units, >= 0.  A row's running max moves only when a key
+                               tile's max exceeds it by more than this, so P may reach
+                               2^threshold; 0 = move on every increase (P <= 1, the
+                               FlashAttention-2 frame).  Exact attention is the same for any
+                               value; P_hat (and so the MXFP4 result) depends on it. */
 } hifa4_attn_params;
 
 /*
@@ -142,7 +147,8 @@ HIFA4_API hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, 
 
 /* The key-tile width of the online-softmax frame (*block_n) and the split-K
  * chunk (*chunk_tokens, 0 for prefill) hifa4_attn_fwd uses for p.  P_hat
- * depends on both, so a reference implementation needs them. */
+ * depends on both (and on p->rescale_threshold), so a reference
+ * implementation needs them. */
 HIFA4_API hifa4_status hifa4_attn_schedule(const hifa4_attn_params* p, int32_t* block_n,
                                  int32_t* chunk_tokens);
 

@@ -48,6 +48,10 @@ HIFA4_PROBE_API int probe_mfma_bf16_32x32x16(const uint16_t* a, const uint16_t* 
 HIFA4_PROBE_API int probe_cvt_pk_fp4(const float* x, const float* scale, uint32_t* out, int n, int sel,
                      void* stream);
 
+/* v_permlane32_swap_b32 with both operands = x: out[2i], out[2i+1] are the two
+ * results for element i = wave*64 + lane (x: [n_waves*64], out: [n_waves*64*2]). */
+HIFA4_PROBE_API int probe_half_swap(const float* x, float* out, int n_waves, void* stream);
+
 /* Throughput loops (n_blocks x 256 threads): 8 independent v_exp_f32 chains per
  * thread, or 4 independent FP4 32x32x64 MFMA chains per wave, iters times.
  * out: [n_blocks * 256] floats (keeps the work alive). */

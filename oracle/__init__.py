@@ -43,7 +43,7 @@ class _AttnCfg(ctypes.Structure):
         ("Sq", ctypes.c_int), ("Sk", ctypes.c_int), ("d", ctypes.c_int),
         ("causal", ctypes.c_int), ("sm_scale", ctypes.c_double),
         ("bc", ctypes.c_int), ("chunk", ctypes.c_int), ("quant_p", ctypes.c_int),
-        ("br", ctypes.c_int), ("nthreads", ctypes.c_int),
+        ("br", ctypes.c_int), ("nthreads", ctypes.c_int), ("tau", ctypes.c_double),
     ]
 
 
@@ -203,10 +203,12 @@ def quantize_v(x, *, cap: int | None = None, quantise: bool = True):
 
 def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int = 64,
               chunk: int = 0, quant_p: bool = True, br: int = 128, kv_lens=None, rows=None,
-              want_weights: bool = False, want_eps: bool = False, nthreads: int | None = None):
+              want_weights: bool = False, want_eps: bool = False, nthreads: int | None = None,
+              tau: float = 0.0):
     """Online-softmax attention over dequantised (or exact) operands, fp64.
 
-    q [B,Hq,Sq,d]; k, v [B,Hkv,Sk,d] (float64).  Returns a dict with
+    q [B,Hq,Sq,d]; k, v [B,Hkv,Sk,d] (float64).  tau: lazy-rescale threshold
+    (log2 units, 0 = FlashAttention-2 frame).  Returns a dict with
     o, o_naive, l, l_naive, lse (and w, eps_* when asked).  With ``rows`` (flat
     ids (b*Hq + h)*Sq + i) only those rows are computed, in that order.
     """
@@ -218,7 +220,7 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
     cfg = _AttnCfg(B, Hq, Hkv, Sq, Sk, d, int(causal),
                    float(sm_scale if sm_scale is not None else 1.0 / np.sqrt(d)),
                    int(bc), int(chunk), int(quant_p), int(br),
-                   int(nthreads or default_threads()))
+                   int(nthreads or default_threads()), float(tau))
     lens = None
     if kv_lens is not None:
         lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))

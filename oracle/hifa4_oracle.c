@@ -34,7 +34,9 @@
  * Readings of the pages' gaps (each is also listed in the design notes):
  *   - FlashAttention-2 frame: P = exp(S - m_new), m_new includes the current
  *     key tile, so P <= 1; the key tile width bc is a parameter because P_hat
- *     depends on it;
+ *     depends on it; optionally a lazy frame (parameter tau): the running max
+ *     moves only when a tile's row max exceeds it by more than tau (log2
+ *     units), so P <= 2^tau (exact attention is the same either way);
  *   - P blocks are 32 consecutive keys aligned to absolute key index 0 (or to
  *     the split chunk start, itself a multiple of 32); masked keys give P = 0;
  *   - causal masking is bottom-right aligned: key t is visible to query i iff
@@ -43,6 +45,7 @@
  *   - split-K decode runs the online softmax from a fresh state on each chunk
  *     and merges the partial (m, l, acc) with the log-sum-exp rule.
  */
+#define _USE_MATH_DEFINES
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -222,6 +225,9 @@ typedef struct {
   int quant_p;     /* 1: P_hat = MXFP4(P) per 32-key block; 0: P_hat = P */
   int br;          /* query rows per epsilon tile */
   int nthreads;
+  double tau;      /* lazy-rescale threshold in log2 units: the running max moves to a
+                      tile's row max only if that exceeds it by more than tau; 0 gives the
+                      FlashAttention-2 frame (P <= 1) */
 } oracle_attn_cfg;
 
 typedef struct {
@@ -276,7 +282,8 @@ static void attn_row(attn_job* J, int b, int h, int i, size_t out, double* S, do
         S[t - t0] = s;
         if (s > smax) smax = s;
       }
-      double m_new = m > smax ? m : smax;
+      /* the frame moves only for an increase of more than tau (log2 units) */
+      double m_new = smax > m + c->tau * M_LN2 ? smax : m;
       double sumP = 0.0, sumPh = 0.0;
       for (long u = 0; u < n; u++) {
         P[u] = exp(S[u] - m_new);

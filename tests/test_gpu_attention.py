@@ -25,11 +25,14 @@ BF16_TOL = 1e-2   # times max|V|, bf16 path vs exact attention
 LSE_TOL = 2e-2    # absolute, natural log units
 
 
-def _run_hifa4(inp, causal, kv_stride=0, out_dtype=torch.bfloat16):
+FAST = hb.RESCALE_THRESHOLD_FAST   # the benchmark's launch configuration
+
+
+def _run_hifa4(inp, causal, kv_stride=0, out_dtype=torch.bfloat16, tau=0.0):
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     s = torch.from_numpy(inp["smooth"]).cuda() if inp["smooth"] is not None else None
     mx = hb.hifa4_quantize_qkv(q, k, v, s, kv_stride=kv_stride)
-    out, lse = hb.hifa4_attn_fwd(mx, causal=causal, out_dtype=out_dtype)
+    out, lse = hb.hifa4_attn_fwd(mx, causal=causal, out_dtype=out_dtype, rescale_threshold=tau)
     torch.cuda.synchronize()
     p = hb.make_params(mx.B, mx.Hq, mx.Hkv, mx.Sq, mx.Sk, mx.d, causal=causal,
                        kv_stride=mx.kv_stride)
@@ -66,18 +69,19 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("tau", [0.0, FAST])
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(str(v) for v in c))
-def test_prefill_small_cases_match_oracle(case):
+def test_prefill_small_cases_match_oracle(case, tau):
     B, Hq, Hkv, Sq, Sk, d, causal, dt, sm, stride = case
-    print("prefill parity:", case, flush=True)
+    print("prefill parity:", case, "tau", tau, flush=True)
     inp = W.random_case(B, Hq, Hkv, Sq, Sk, d, dtype=dt, seed=sum(case[:6]), rope_theta=1e4,
                         n_outliers=2, smooth_alpha=0.5 if sm else None)
     out_dt = torch.float16 if dt == "fp16" else torch.bfloat16
-    o, lse, bc, chunk = _run_hifa4(inp, causal, kv_stride=stride, out_dtype=out_dt)
+    o, lse, bc, chunk = _run_hifa4(inp, causal, kv_stride=stride, out_dtype=out_dt, tau=tau)
     assert chunk == 0
     qq = _oracle_quant(inp)
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=bc,
-                           quant_p=True)
+                           quant_p=True, tau=tau)
     vmax = np.abs(W.to_f32(inp["v"])).max()
     _check_rows(o, lse, ref, vmax, "case %s" % (case,))
     # P-Reordering: every output row is a convex combination of the visible
@@ -128,11 +132,11 @@ FULL = [W.QWEN3_8B, W.LLAMA31_8B, W.GEMMA2_9B]
 def test_prefill_full_size_sampled_rows(cfg):
     print("full-size prefill parity:", cfg.name, flush=True)
     inp = W.prefill_inputs(cfg)
-    o, lse, bc, _ = _run_hifa4(inp, cfg.causal)
+    o, lse, bc, _ = _run_hifa4(inp, cfg.causal, tau=FAST)
     qq = _oracle_quant(inp)
     rows = _sample_rows(cfg.B, cfg.Hq, cfg.S, 192, seed=cfg.seed)
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=cfg.causal, bc=bc,
-                           rows=rows)
+                           rows=rows, tau=FAST)
     vmax = np.abs(W.to_f32(inp["v"])).max()
     _check_rows(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], ref, vmax, cfg.name)
     exact = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
@@ -142,7 +146,7 @@ def test_prefill_full_size_sampled_rows(cfg):
         np.sqrt(np.mean((o.reshape(-1, cfg.d)[rows] - exact["o"]) ** 2))))
 
 
-def _decode_case(cfg, lens, cap, chunk=0):
+def _decode_case(cfg, lens, cap, chunk=0, tau=0.0):
     B, Hq, Hkv, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.d
     mx = hb.alloc_mx(B, Hq, Hkv, 1, cap, d)
     q = W.decode_q(cfg)
@@ -156,30 +160,32 @@ def _decode_case(cfg, lens, cap, chunk=0):
         hb.hifa4_quantize_qkv(None, k.cuda(), v.cuda(), None, kv_stride=cap, out=sl)
     mx.Sq, mx.Sk, mx.kv_stride = 1, cap, cap
     lens_t = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
-    out, lse = hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, decode_chunk=chunk)
+    out, lse = hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, decode_chunk=chunk,
+                                 rescale_threshold=tau)
     torch.cuda.synchronize()
     p = hb.make_params(B, Hq, Hkv, 1, cap, d, causal=True, kv_stride=cap, decode_chunk=chunk)
     bc, ch = hb.hifa4_attn_schedule(p)
     return q, out.float().cpu().numpy(), lse.cpu().numpy(), bc, ch
 
 
-def _decode_oracle(cfg, q, b, L, bc, chunk):
+def _decode_oracle(cfg, q, b, L, bc, chunk, tau=0.0):
     k, v = W.decode_kv(cfg, b, int(L))
     qq = oracle.quantize_qkv(W.to_f32(q[b:b + 1]), W.to_f32(k), W.to_f32(v), None)
-    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=bc, chunk=chunk)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=bc, chunk=chunk,
+                           tau=tau)
     vmax = np.abs(W.to_f32(v)).max()
     return ref, vmax
 
 
-@pytest.mark.parametrize("chunk", [0, 64, 192])
-def test_decode_small_matches_oracle(chunk):
+@pytest.mark.parametrize("chunk,tau", [(0, 0.0), (64, 0.0), (192, 0.0), (0, FAST), (192, FAST)])
+def test_decode_small_matches_oracle(chunk, tau):
     cfg = W.DecodeConfig("small_decode", 5, 8, 2, 128, 1, 700)
     lens = [700, 1, 64, 65, 333]
-    print("decode parity: lens", lens, "chunk", chunk, flush=True)
-    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=704, chunk=chunk)
+    print("decode parity: lens", lens, "chunk", chunk, "tau", tau, flush=True)
+    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=704, chunk=chunk, tau=tau)
     assert ch == (chunk or ch) and ch % bc == 0
     for b, L in enumerate(lens):
-        ref, vmax = _decode_oracle(cfg, q, b, L, bc, ch)
+        ref, vmax = _decode_oracle(cfg, q, b, L, bc, ch, tau=tau)
         _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L))
 
 
@@ -196,21 +202,23 @@ def test_decode_full_size_sampled_sequences():
     lens = W.decode_lengths(cfg)
     cap = int(-(-lens.max() // 64) * 64)
     print("full-size decode parity: sum(L) =", int(lens.sum()), flush=True)
-    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=cap)
+    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=cap, tau=FAST)
     for b in (0, int(np.argmax(lens)), int(np.argmin(lens)), 37):
-        ref, vmax = _decode_oracle(cfg, q, b, lens[b], bc, ch)
+        ref, vmax = _decode_oracle(cfg, q, b, lens[b], bc, ch, tau=FAST)
         _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, lens[b]))
 
 
+@pytest.mark.parametrize("tau", [0.0, FAST])
 @pytest.mark.parametrize("case", [
     (1, 4, 2, 200, 200, 128, True),
     (2, 2, 1, 130, 300, 64, False),
     (1, 4, 2, 257, 300, 256, True),
 ])
-def test_bf16_baseline_matches_exact_attention(case):
+def test_bf16_baseline_matches_exact_attention(case, tau):
     B, Hq, Hkv, Sq, Sk, d, causal = case
     inp = W.random_case(B, Hq, Hkv, Sq, Sk, d, dtype="bf16", seed=7 + sum(case[:6]))
-    out, lse = hb.bf16_attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), causal=causal)
+    out, lse = hb.bf16_attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), causal=causal,
+                                rescale_threshold=tau)
     torch.cuda.synchronize()
     ref = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
                            causal=causal, bc=64, quant_p=False)

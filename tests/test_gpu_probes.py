@@ -41,6 +41,7 @@ def lib():
     l.probe_mfma_bf16_32x32x16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
     l.probe_cvt_pk_fp4.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int,
                                                            ctypes.c_void_p]
+    l.probe_half_swap.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_exp2_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return l
@@ -170,6 +171,23 @@ def test_bf16_mfma_layout(lib):
                 got[m, n] = dd[w, l, r]
         np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5)
     del rng
+
+
+def test_permlane32_swap_exchanges_wave_halves(lib):
+    """The kernels take max(r0, r1) of v_permlane32_swap(x, x) as max(x[l], x[l ^ 32])."""
+    n_waves = 8
+    x = torch.randn(n_waves * 64)
+    out = torch.zeros(n_waves * 64 * 2, device="cuda")
+    xd = x.cuda()
+    assert lib.probe_half_swap(xd.data_ptr(), out.data_ptr(), n_waves, _stream()) == 0
+    torch.cuda.synchronize()
+    r = out.cpu().numpy().reshape(n_waves, 64, 2)
+    xv = x.numpy().reshape(n_waves, 64)
+    partner = xv[:, np.arange(64) ^ 32]
+    # each lane sees its own value and its partner's, one in each result
+    got = np.sort(r, axis=-1)
+    want = np.sort(np.stack([xv, partner], axis=-1), axis=-1)
+    np.testing.assert_array_equal(got, want)
 
 
 def _cvt_inputs():

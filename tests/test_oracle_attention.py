@@ -83,20 +83,44 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES)
-@pytest.mark.parametrize("bc", [32, 64, 128, 4096])
-def test_exact_mode_equals_textbook_softmax(case, bc):
+@pytest.mark.parametrize("bc,tau", [(32, 0.0), (64, 0.0), (128, 0.0), (4096, 0.0), (32, 8.0),
+                                    (64, 3.0)])
+def test_exact_mode_equals_textbook_softmax(case, bc, tau):
     B, Hq, Hkv, Sq, Sk, d, causal = case
     rng = np.random.default_rng(hash((case, bc)) % 2**32)
     q = rng.standard_normal((B, Hq, Sq, d)) * 1.5
     k = rng.standard_normal((B, Hkv, Sk, d))
     v = rng.standard_normal((B, Hkv, Sk, d))
     sm = 1.0 / np.sqrt(d)
-    r = oracle.attention(q, k, v, causal=causal, sm_scale=sm, bc=bc, quant_p=False)
+    r = oracle.attention(q, k, v, causal=causal, sm_scale=sm, bc=bc, quant_p=False, tau=tau)
     o, lse = brute_attention(q, k, v, causal, sm)
     np.testing.assert_allclose(r["o"], o, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(r["lse"], lse, rtol=1e-12, atol=1e-12)
     # the inconsistent normaliser coincides with the exact one without quantisation
     np.testing.assert_allclose(r["o_naive"], o, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("tau,bc,rise", [(0.0, 64, 1.0), (8.0, 64, 1.0), (2.0, 32, 1.0),
+                                         (2.0, 32, 1.7)])
+def test_lazy_rescale_frame_hand_worked(tau, bc, rise):
+    """Two key tiles, scores 0 then `rise` (natural units), exact P: the frame decides l.
+
+    The frame moves to the second tile's max iff rise / ln 2 > tau (log2 units):
+    then l = n e^-rise + n, else l = n + n e^rise.  LSE = log(n + n e^rise)
+    either way.
+    """
+    n = bc
+    d = 32
+    q = np.zeros((1, 1, 1, d))
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, 2 * n, d))
+    k[0, 0, n:, 0] = rise
+    v = np.random.default_rng(0).standard_normal((1, 1, 2 * n, d))
+    r = oracle.attention(q, k, v, causal=False, sm_scale=1.0, bc=bc, quant_p=False, tau=tau)
+    moved = rise / np.log(2.0) > tau
+    want_l = n * np.exp(-rise) + n if moved else n + n * np.exp(rise)
+    np.testing.assert_allclose(r["l"][0, 0, 0], want_l, rtol=1e-14)
+    np.testing.assert_allclose(r["lse"][0, 0, 0], np.log(n + n * np.exp(rise)), rtol=1e-14)
 
 
 @pytest.mark.parametrize("Sk", [32, 75, 160])
@@ -152,11 +176,11 @@ def _quantised_case(seed, B=1, Hq=2, Hkv=1, Sq=150, Sk=150, d=64, outliers=True)
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("bc", [32, 64])
-def test_p_reordering_convex_weights(causal, bc):
+@pytest.mark.parametrize("bc,tau", [(32, 0.0), (64, 0.0), (64, 8.0)])
+def test_p_reordering_convex_weights(causal, bc, tau):
     qq = _quantised_case(1)
     r = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=bc,
-                         quant_p=True, want_weights=True)
+                         quant_p=True, want_weights=True, tau=tau)
     w = r["w"]                                   # [B,Hq,Sq,Sk]
     vd = qq["v_deq"]
     Sq, Sk = w.shape[2], w.shape[3]

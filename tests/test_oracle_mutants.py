@@ -7,7 +7,6 @@ against that library; at least one of them must fail.  Nothing here touches
 the HIP path.
 """
 import os
-import tempfile
 
 import numpy as np
 import pytest
@@ -47,6 +46,10 @@ MUTANTS = [
      "for (long a0 = t0 - (t0 % 32) - 16; a0 < t1; a0 += 32)", 0),
     ("v_tail_amax_over_padding", "col[k] = k < n ? (double)xh[(size_t)(t0 + k) * d + c] : 0.0;",
      "col[k] = (double)xh[(size_t)((t0 + k) % S) * d + c];", 0),
+    ("lazy_threshold_ignored", "double m_new = smax > m + c->tau * M_LN2 ? smax : m;",
+     "double m_new = smax > m ? smax : m;", 0),
+    ("lazy_threshold_in_natural_units", "double m_new = smax > m + c->tau * M_LN2 ? smax : m;",
+     "double m_new = smax > m + c->tau ? smax : m;", 0),
     ("dot_product_drops_last_channel", "for (int j = 0; j < d; j++) s += qr[j] * kr[j];",
      "for (int j = 0; j < d - 1; j++) s += qr[j] * kr[j];", 0),
 ]
@@ -64,11 +67,13 @@ def _pin_checks():
     for name, x, sc, codes in TQ._golden_blocks():
         checks.append(lambda x=x, sc=sc, codes=codes, name=name: TQ.test_mx_block_golden(name, x, sc, codes))
     for case in TA.CASES:
-        checks.append(lambda case=case: TA.test_exact_mode_equals_textbook_softmax(case, 64))
+        checks.append(lambda case=case: TA.test_exact_mode_equals_textbook_softmax(case, 64, 0.0))
     checks += [
         lambda: TA.test_single_tile_mxfp4_p_closed_form(75),
+        lambda: TA.test_lazy_rescale_frame_hand_worked(8.0, 64, 1.0),
+        lambda: TA.test_lazy_rescale_frame_hand_worked(2.0, 32, 1.7),
         lambda: TA.test_smooth_qk_invariance_exact(True),
-        lambda: TA.test_p_reordering_convex_weights(True, 64),
+        lambda: TA.test_p_reordering_convex_weights(True, 64, 8.0),
         TA.test_inconsistent_normaliser_is_coherent_row_scaling,
         lambda: TA.test_split_k_mxfp4_equals_merge_of_chunk_runs(64),
         lambda: TA.test_split_k_exact_equals_unsplit(128),
