@@ -163,13 +163,20 @@ def alloc_mx(B, Hq, Hkv, Sq, kv_stride, d, device="cuda") -> MXQKV:
 
 def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
                        v: Optional[torch.Tensor], smooth: Optional[torch.Tensor] = None, *,
-                       kv_stride: int = 0, out: Optional[MXQKV] = None, stream=None) -> MXQKV:
-    """Smooth-QK + MXFP4 quantisation; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] bf16 or fp16 on the GPU."""
+                       kv_stride: int = 0, out: Optional[MXQKV] = None, Hkv: Optional[int] = None,
+                       stream=None) -> MXQKV:
+    """Smooth-QK + MXFP4 quantisation; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] bf16 or fp16 on the GPU.
+
+    With k and v both None, pass Hkv (the smoothing rows are per KV head).
+    """
     ref = next(t for t in (q, k, v) if t is not None)
     B, d = ref.shape[0], ref.shape[3]
     Hq, Sq = (q.shape[1], q.shape[2]) if q is not None else (1, 0)
     kk = k if k is not None else v
-    Hkv, Sk = (kk.shape[1], kk.shape[2]) if kk is not None else (Hq, 0)
+    if kk is not None:
+        Hkv, Sk = kk.shape[1], kk.shape[2]
+    else:
+        Hkv, Sk = (Hkv if Hkv is not None else (smooth.shape[0] if smooth is not None else Hq)), 0
     if q is None:
         Hq = Hkv
     for t in (q, k, v):

@@ -21,6 +21,7 @@ struct QuantizeArgs {
   int B, Hq, Hkv, Sq, Sk, d, cap;
   int64_t blocks_q, blocks_k;  // 32-element row blocks
   int64_t wg_q, wg_k;          // filled by the launcher
+  int64_t items_v;             // (channel pair, 32-token block) items; filled by the launcher
 };
 
 hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream);

@@ -7,10 +7,21 @@
 // Format: OCP MXFP4 (E2M1 elements, E8M0 scale per 32), the stand-in for the
 // undefined HIF4 layout.
 //
-// One launch covers all three tensors; its grid is split in three uniform
-// ranges of workgroups (Q rows, K rows, V token blocks).  The work is HBM
-// bound: 2 bytes in and 17/32 byte out per element, so every store is a
-// contiguous 16-byte code chunk or a run of scale bytes across the wave.
+// One launch covers all three tensors; its grid is split in uniform ranges of
+// workgroups (V token blocks, K rows, Q rows).  The work is HBM bound (2 bytes
+// in, 17/32 byte out per element), so every access is coalesced across the
+// wave:
+//   - Q / K: four lanes share a 32-element block, each loading 16 contiguous
+//     bytes (a wave reads 1 KB contiguous per instruction, four such loads in
+//     flight per lane); the block max is two lane shuffles; each lane writes
+//     its 4 code bytes, so a block's 16 code bytes and a wave's 256 bytes are
+//     contiguous;
+//   - V: one lane per (channel pair, 32-token block) reads the pair down the
+//     32 tokens (a wave reads 256 contiguous bytes per token) and writes the
+//     two channels' 16-byte code runs next to each other.
+// The element encode is the gfx950 packed FP4 convert, which divides by the
+// power-of-two block scale and rounds to nearest-even with saturation (the
+// probes check it bit-for-bit against the CPU reference's encoder).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -35,159 +46,193 @@ __device__ __forceinline__ float elem(uint32_t bits16) {
   }
 }
 
-// E2M1 code of x / 2^e given neg_e = -e: the magnitude is compared with the
-// seven decision points between neighbouring E2M1 values; at an exact
-// midpoint the comparison direction picks the even code (0.25 -> 0,
-// 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0);
-// above 5 everything clamps to 6.0.  The sign bit of x is kept (-0 -> 0x8).
-__device__ __forceinline__ uint32_t e2m1_code(float x, int neg_e) {
-  float y = ldexpf(fabsf(x), neg_e);
-  uint32_t c = (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
-               (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
-               (uint32_t)(y > 5.0f);
-  return c | ((__float_as_uint(x) >> 28) & 8u);
+// Value of the lane selected by a DPP quad_perm control within each quad.
+#define quad_xor(x, ctrl)                                                               \
+  __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), (ctrl), 0xF, 0xF, false))
+
+// 8 elements -> 4 code bytes (element 2i in the low nibble of byte i).
+__device__ __forceinline__ uint32_t encode8(const float (&v)[8], float scale) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+  return w;
 }
 
-// Quantise 32 fp32 values: 16 code bytes + the E8M0 byte.
-__device__ __forceinline__ uint4 quantise32(const float (&v)[32], uint32_t& scale_byte) {
-  float amax = 0.0f;
+// Row blocks (blocks of 32 along the head dim): four lanes share a block,
+// lane `lane4` handling elements 8*lane4 .. 8*lane4+7.  A lane processes
+// kRowParts blocks, kThreads*4 parts apart, with every load issued before any
+// use so that a wave keeps kRowParts KB of HBM reads in flight.
+constexpr int kRowParts = 4;
+
+struct RowPart {
+  uint32_t orow;  // output row (b, h, t) with the token capacity applied
+  uint32_t j0;    // first element of this lane's 8
+  bool ok;
+};
+
+// Index arithmetic is 32-bit (the launcher checks the sizes fit), with the
+// head dim a compile-time constant, so the per-part decode is a handful of
+// integer ops rather than 64-bit divisions.
+template <bool kBf16, int D>
+__device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
+                                              const float* __restrict__ s, bool divide,
+                                              uint32_t part0, uint32_t n_parts, uint32_t H,
+                                              uint32_t S, uint32_t group, uint32_t cap,
+                                              uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ scales) {
+  constexpr uint32_t NB = D / 32;
+  uint4 w[kRowParts];
+  float4 f0[kRowParts], f1[kRowParts];
+  RowPart rp[kRowParts];
 #pragma unroll
-  for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
-  scale_byte = e8m0_from_amax(amax);
-  const int neg_e = 127 - (int)scale_byte;
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) acc |= e2m1_code(v[8 * q + i], neg_e) << (4 * i);
-    w[q] = acc;
+  for (int r = 0; r < kRowParts; r++) {
+    const uint32_t part = part0 + (uint32_t)r * kThreads;
+    rp[r].ok = part < n_parts;
+    const uint32_t blk = rp[r].ok ? part >> 2 : 0u;
+    const uint32_t row = blk / NB;  // flattened (b, h, t)
+    rp[r].j0 = (blk % NB) * 32u + 8u * (part & 3u);
+    const uint32_t bh = row / S;
+    const uint32_t t = row - bh * S;
+    rp[r].orow = bh * cap + t;
+    w[r] = rp[r].ok ? *reinterpret_cast<const uint4*>(x + (size_t)row * D + rp[r].j0)
+                    : make_uint4(0, 0, 0, 0);
+    if (s != nullptr) {
+      const uint32_t hs = (bh % H) / group;
+      const float4* sp = reinterpret_cast<const float4*>(s + hs * D + rp[r].j0);
+      f0[r] = sp[0];
+      f1[r] = sp[1];
+    }
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// One thread = one 32-element block of one row (blocks along the head dim).
-template <bool kBf16>
-__device__ void quantise_row_block(const uint16_t* __restrict__ x, const float* __restrict__ s,
-                                   bool divide, int64_t blk, int H, int S, int d, int group,
-                                   int cap, uint8_t* __restrict__ codes,
-                                   uint8_t* __restrict__ scales) {
-  const int nb = d / 32;
-  const int64_t row = blk / nb;  // flattened (b, h, t)
-  const int j0 = (int)(blk % nb) * 32;
-  const int t = (int)(row % S);
-  const int64_t bh = row / S;
-  const int h = (int)(bh % H);
-  const uint4* src = reinterpret_cast<const uint4*>(x + row * d + j0);
-  float v[32];
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    uint4 w = src[q];
-    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int r = 0; r < kRowParts; r++) {
+    const uint32_t ws[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+    float v[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      v[8 * q + 2 * i] = elem<kBf16>(ws[i] & 0xFFFFu);
-      v[8 * q + 2 * i + 1] = elem<kBf16>(ws[i] >> 16);
+      v[2 * i] = elem<kBf16>(ws[i] & 0xFFFFu);
+      v[2 * i + 1] = elem<kBf16>(ws[i] >> 16);
     }
-  }
-  if (s != nullptr) {
-    const float4* sp = reinterpret_cast<const float4*>(s + (int64_t)(h / group) * d + j0);
+    if (s != nullptr) {
+      const float ff[8] = {f0[r].x, f0[r].y, f0[r].z, f0[r].w, f1[r].x, f1[r].y, f1[r].z, f1[r].w};
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-      float4 f = sp[q];
-      float ff[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-      for (int i = 0; i < 4; i++) v[4 * q + i] = divide ? v[4 * q + i] / ff[i] : v[4 * q + i] * ff[i];
+      for (int i = 0; i < 8; i++) v[i] = divide ? v[i] / ff[i] : v[i] * ff[i];
     }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[i]));
+    // the four lanes of a block are one DPP quad (consecutive, all valid or
+    // all invalid): two quad permutes give the block max in every lane
+    amax = fmaxf(amax, quad_xor(amax, 0xB1));  // lanes 1,0,3,2
+    amax = fmaxf(amax, quad_xor(amax, 0x4E));  // lanes 2,3,0,1
+    if (!rp[r].ok) continue;
+    const uint32_t sb = e8m0_from_amax(amax);
+    *reinterpret_cast<uint32_t*>(codes + (size_t)rp[r].orow * (D / 2) + rp[r].j0 / 2) =
+        encode8(v, e8m0_to_float(sb));
+    if ((rp[r].j0 & 31u) == 0) scales[(size_t)rp[r].orow * NB + rp[r].j0 / 32] = (uint8_t)sb;
   }
-  uint32_t sb;
-  uint4 c = quantise32(v, sb);
-  const int64_t orow = bh * cap + t;
-  *reinterpret_cast<uint4*>(codes + orow * (d / 2) + j0 / 2) = c;
-  scales[orow * nb + j0 / 32] = (uint8_t)sb;
 }
 
-// One workgroup = kThreads / d consecutive 32-token blocks of one (b, h);
-// thread = one channel of one block.  The token tile is staged through LDS
-// with coalesced 16-byte loads; each thread then reads its channel's column
-// (a contiguous row of the wave per step, so no bank conflicts).
-template <bool kBf16>
-__device__ void quantise_v_tile(const uint16_t* __restrict__ x, int64_t wg, int S, int d, int cap,
-                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                uint16_t* lds) {
-  const int blocks_per_wg = kThreads / d;
-  const int nblk_valid = (S + 31) / 32;
-  const int wg_per_head = (nblk_valid + blocks_per_wg - 1) / blocks_per_wg;
-  const int64_t bh = wg / wg_per_head;
-  const int blk0 = (int)(wg % wg_per_head) * blocks_per_wg;
-  const int t0 = blk0 * 32;
-  const int ntok = blocks_per_wg * 32;  // tokens staged
-  const uint16_t* xh = x + bh * (int64_t)S * d;
-  // stage ntok x d elements (8192 for every d) as 16-byte chunks
-  const int chunks = ntok * d / 8;
-  for (int i = threadIdx.x; i < chunks; i += kThreads) {
-    const int tok = (i * 8) / d;
-    const int c8 = (i * 8) % d;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (t0 + tok < S) w = *reinterpret_cast<const uint4*>(xh + (int64_t)(t0 + tok) * d + c8);
-    *reinterpret_cast<uint4*>(lds + tok * d + c8) = w;
-  }
-  __syncthreads();
-  const int lb = threadIdx.x / d;  // local block
-  const int ch = threadIdx.x % d;
-  const int blk = blk0 + lb;
-  if (blk >= nblk_valid) return;
-  float v[32];
+// One lane = channels (2c, 2c+1) of one 32-token block of one (b, h); tokens
+// past S are zero.  Work item index: ((bh * nblk_valid) + blk) * (D/2) + c.
+template <bool kBf16, int D>
+__device__ __forceinline__ void quantise_v_pair(const uint16_t* __restrict__ x, uint32_t item,
+                                                uint32_t S, uint32_t cap,
+                                                uint8_t* __restrict__ codes,
+                                                uint8_t* __restrict__ scales) {
+  constexpr uint32_t HALF = D / 2;
+  const uint32_t nblk_valid = (S + 31) / 32;
+  const uint32_t c = item % HALF;
+  const uint32_t rest = item / HALF;
+  const uint32_t bh = rest / nblk_valid;
+  const uint32_t blk = rest - bh * nblk_valid;
+  const uint32_t t0 = blk * 32;
+  const uint16_t* src = x + ((size_t)bh * S + t0) * D + 2 * c;
+  float a[32], b[32];
 #pragma unroll
-  for (int k = 0; k < 32; k++) v[k] = elem<kBf16>(lds[(lb * 32 + k) * d + ch]);
-  uint32_t sb;
-  uint4 c = quantise32(v, sb);
-  const int nblk_cap = (cap + 31) / 32;
-  const int64_t ob = bh * nblk_cap + blk;
-  *reinterpret_cast<uint4*>(codes + (ob * d + ch) * 16) = c;
-  scales[ob * d + ch] = (uint8_t)sb;
+  for (int k = 0; k < 32; k++) {
+    uint32_t w = 0;
+    if (t0 + k < S) w = *reinterpret_cast<const uint32_t*>(src + (size_t)k * D);
+    a[k] = elem<kBf16>(w & 0xFFFFu);
+    b[k] = elem<kBf16>(w >> 16);
+  }
+  float ma = 0.0f, mb = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; k++) {
+    ma = fmaxf(ma, fabsf(a[k]));
+    mb = fmaxf(mb, fabsf(b[k]));
+  }
+  const uint32_t sa = e8m0_from_amax(ma), sbb = e8m0_from_amax(mb);
+  const float fa = e8m0_to_float(sa), fb = e8m0_to_float(sbb);
+  uint32_t ca[4], cb[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const float va[8] = {a[8 * q], a[8 * q + 1], a[8 * q + 2], a[8 * q + 3],
+                         a[8 * q + 4], a[8 * q + 5], a[8 * q + 6], a[8 * q + 7]};
+    const float vb[8] = {b[8 * q], b[8 * q + 1], b[8 * q + 2], b[8 * q + 3],
+                         b[8 * q + 4], b[8 * q + 5], b[8 * q + 6], b[8 * q + 7]};
+    ca[q] = encode8(va, fa);
+    cb[q] = encode8(vb, fb);
+  }
+  const uint32_t nblk_cap = (cap + 31) / 32;
+  const size_t ob = (size_t)bh * nblk_cap + blk;
+  uint4* dst = reinterpret_cast<uint4*>(codes + (ob * D + 2 * c) * 16);
+  dst[0] = make_uint4(ca[0], ca[1], ca[2], ca[3]);
+  dst[1] = make_uint4(cb[0], cb[1], cb[2], cb[3]);
+  *reinterpret_cast<uint16_t*>(scales + ob * D + 2 * c) = (uint16_t)(sa | (sbb << 8));
 }
 
-template <bool kBf16>
+template <bool kBf16, int D>
 __global__ __launch_bounds__(kThreads) void quantize_qkv_kernel(QuantizeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[8192];
-  const int64_t wg = blockIdx.x;
-  if (wg < a.wg_q) {
-    const int64_t blk = wg * kThreads + threadIdx.x;
-    if (blk < a.blocks_q)
-      quantise_row_block<kBf16>(a.q, a.smooth, false, blk, a.Hq, a.Sq, a.d, a.Hq / a.Hkv, a.Sq,
-                                a.q_codes, a.q_scales);
-  } else if (wg < a.wg_q + a.wg_k) {
-    const int64_t blk = (wg - a.wg_q) * kThreads + threadIdx.x;
-    if (blk < a.blocks_k)
-      quantise_row_block<kBf16>(a.k, a.smooth, true, blk, a.Hkv, a.Sk, a.d, 1, a.cap, a.k_codes,
-                                a.k_scales);
+  // Grid order: V token blocks (the longest work items) first, then K, then
+  // Q, so that the long items do not form the tail of the launch.
+  const uint32_t wg = blockIdx.x;
+  const uint32_t wg_v = (uint32_t)((a.items_v + kThreads - 1) / kThreads);
+  const uint32_t wg_k = (uint32_t)a.wg_k;
+  if (wg < wg_v) {
+    const uint32_t item = wg * kThreads + threadIdx.x;
+    if (item < (uint32_t)a.items_v)
+      quantise_v_pair<kBf16, D>(a.v, item, a.Sk, a.cap, a.v_codes, a.v_scales);
+  } else if (wg < wg_v + wg_k) {
+    const uint32_t part0 = (wg - wg_v) * kThreads * kRowParts + threadIdx.x;
+    quantise_rows<kBf16, D>(a.k, a.smooth, true, part0, (uint32_t)(4 * a.blocks_k), a.Hkv, a.Sk,
+                            1, a.cap, a.k_codes, a.k_scales);
   } else {
-    quantise_v_tile<kBf16>(a.v, wg - a.wg_q - a.wg_k, a.Sk, a.d, a.cap, a.v_codes, a.v_scales,
-                           lds);
+    const uint32_t part0 = (wg - wg_v - wg_k) * kThreads * kRowParts + threadIdx.x;  // 4 parts per block
+    quantise_rows<kBf16, D>(a.q, a.smooth, false, part0, (uint32_t)(4 * a.blocks_q), a.Hq, a.Sq,
+                            a.Hq / a.Hkv, a.Sq, a.q_codes, a.q_scales);
+  }
+}
+
+template <bool kBf16>
+void launch_d(const QuantizeArgs& a, unsigned grid, hipStream_t stream) {
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 64>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 128>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 256>), dim3(grid), dim3(kThreads), 0, stream, a); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream) {
-  a.wg_q = a.q ? (a.blocks_q + kThreads - 1) / kThreads : 0;
-  a.wg_k = a.k ? (a.blocks_k + kThreads - 1) / kThreads : 0;
-  int64_t wg_v = 0;
-  if (a.v) {
-    const int blocks_per_wg = kThreads / a.d;
-    const int nblk_valid = (a.Sk + 31) / 32;
-    wg_v = (int64_t)a.B * a.Hkv * ((nblk_valid + blocks_per_wg - 1) / blocks_per_wg);
-  }
+  const int64_t per_wg = (int64_t)kThreads * kRowParts;
+  a.wg_q = a.q ? (4 * a.blocks_q + per_wg - 1) / per_wg : 0;
+  a.wg_k = a.k ? (4 * a.blocks_k + per_wg - 1) / per_wg : 0;
+  a.items_v = a.v ? (int64_t)a.B * a.Hkv * ((a.Sk + 31) / 32) * (a.d / 2) : 0;
+  const int64_t wg_v = (a.items_v + kThreads - 1) / kThreads;
   const int64_t total = a.wg_q + a.wg_k + wg_v;
   if (total == 0) return hipSuccess;
-  if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  // 32-bit index arithmetic inside the kernel
+  const int64_t lim = 0x7FFFFFFF;
+  if (total > lim / (kThreads * kRowParts) || 4 * a.blocks_q > lim || 4 * a.blocks_k > lim ||
+      a.items_v > lim || (int64_t)a.B * a.Hkv * a.cap > lim || (int64_t)a.B * a.Hq * a.Sq > lim)
+    return hipErrorInvalidConfiguration;
   if (bf16)
-    hipLaunchKernelGGL(quantize_qkv_kernel<true>, dim3((unsigned)total), dim3(kThreads), 0, stream,
-                       a);
+    launch_d<true>(a, (unsigned)total, stream);
   else
-    hipLaunchKernelGGL(quantize_qkv_kernel<false>, dim3((unsigned)total), dim3(kThreads), 0,
-                       stream, a);
+    launch_d<false>(a, (unsigned)total, stream);
   return hipGetLastError();
 }
 
