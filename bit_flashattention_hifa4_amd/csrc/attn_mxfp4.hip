@@ -58,22 +58,6 @@ __device__ __forceinline__ int perm_row(int t, int m) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Pack the lane's 32 P values (natural key order) into E2M1 codes with the
-// block scale `scale` (= 2^(e8m0 - 127)).
-__device__ __forceinline__ uint4 pack_p(const float (&p)[32], float scale) {
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    uint32_t x = 0;
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 0], p[8 * q + 1], scale, 0);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 2], p[8 * q + 3], scale, 1);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 4], p[8 * q + 5], scale, 2);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, p[8 * q + 6], p[8 * q + 7], scale, 3);
-    w[q] = x;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // One online-softmax step on the 32 scores a lane holds for its query
 // (already masked with -inf).  Updates m_run, rescales the accumulators and
 // returns the packed P operand plus its E8M0 byte.
@@ -109,26 +93,59 @@ __device__ __forceinline__ float max_with_half_swap(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ SoftmaxStep softmax_step(float (&s)[32], float& m_run, float c,
+// Softmax step on the lane's 32 scores held in the two QK accumulators (tile
+// t, register r <-> key 32h + 16t + r), in place: the scores are replaced by
+// P before packing, so no copies of the accumulators are made.  Masked
+// scores are -inf on entry.
+__device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m_run, float c,
                                                     float tau) {
-  float bm = s[0];
+  float ma = s0[0], mb = s1[0];
 #pragma unroll
-  for (int k = 1; k < 32; k++) bm = fmaxf(bm, s[k]);
+  for (int r = 1; r < 16; r++) {
+    ma = fmaxf(ma, s0[r]);
+    mb = fmaxf(mb, s1[r]);
+  }
+  const float bm = fmaxf(ma, mb);
   const float bmc = bm * c;  // contraction is off in this file: a rounded product
   const float rmc = max_with_half_swap(bmc);
   const float m_new = rmc > m_run + tau ? rmc : m_run;
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
   SoftmaxStep st;
   st.alpha = fast_exp2(m_run - m_use);
-  float p[32];
 #pragma unroll
-  for (int k = 0; k < 32; k++) p[k] = fast_exp2(__builtin_fmaf(s[k], c, -m_use));
+  for (int r = 0; r < 16; r++) {
+    s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -m_use));
+    s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -m_use));
+  }
   const float pmax = fast_exp2(bmc - m_use);
   const uint32_t sb = e8m0_from_amax(pmax);
   st.p_scale = (int)sb;
-  st.p_codes = pack_p(p, e8m0_to_float(sb));
+  const float scale = e8m0_to_float(sb);
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const v16f& src = q < 2 ? s0 : s1;
+    const int o = 8 * (q & 1);
+    uint32_t x = 0;
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 0], src[o + 1], scale, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 2], src[o + 3], scale, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 4], src[o + 5], scale, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 6], src[o + 7], scale, 3);
+    w[q] = x;
+  }
+  st.p_codes = make_uint4(w[0], w[1], w[2], w[3]);
   m_run = m_new;
   return st;
+}
+
+// Mask keys >= lim (key of element (t, r) is kb + 16t + r) with -inf.
+__device__ __forceinline__ void mask_scores(v16f& s0, v16f& s1, int kb, int lim) {
+  const int rem = lim - kb;  // elements r < rem stay
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    if (r >= rem) s0[r] = -INFINITY;
+    if (16 + r >= rem) s1[r] = -INFINITY;
+  }
 }
 
 template <int NC>
@@ -332,7 +349,7 @@ __device__ __forceinline__ void qk_step(const uint8_t* kbuf, const uint4 (&qa)[D
 }
 
 template <int D>
-constexpr int prefill_min_blocks() { return D >= 256 ? 1 : 2; }
+constexpr int prefill_min_blocks() { return D >= 256 ? 1 : 2; }  // also used by decode
 
 template <int D, bool kCausal>
 __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_kernel(
@@ -426,6 +443,12 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
       store_k<D>(lds_k + T::LDS_K, tid, kpre);
     }
   }
+  // Drain every outstanding load on all paths into the loop.  Without it the
+  // compiler must assume the Q operand loads may still be in flight at the
+  // loop header (the prologue's loads are conditional) and makes the Q K^T
+  // MFMAs of each step wait on the vector-memory counter, i.e. on the
+  // prefetch loads issued just before them.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // One pipeline step: scores of tile kt are in (c0, c1); the next tile's go
@@ -444,20 +467,8 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     __builtin_amdgcn_sched_barrier(0);
 
     if (n0 < wave_end) {  // uniform per wave
-      float s[32];
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        s[r] = c0[r];
-        s[16 + r] = c1[r];
-      }
-      if (n0 + kBN > wave_full) {
-        const int kb = n0 + 32 * h;
-#pragma unroll
-        for (int k = 0; k < 32; k++)
-          if (kb + k >= row_lim) s[k] = -INFINITY;
-      }
-
-      const SoftmaxStep st = softmax_step(s, m_run, c, a.tau);
+      if (n0 + kBN > wave_full) mask_scores(c0, c1, n0 + 32 * h, row_lim);
+      const SoftmaxStep st = softmax_step(c0, c1, m_run, c, a.tau);
       // rescale only when some row's max moved (multiplying by 1 is exact)
       if (__any(st.alpha != 1.0f)) {
 #pragma unroll
@@ -478,6 +489,11 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     }
     if (more_k) store_k<D>(lds_k + (kt & 1) * T::LDS_K, tid, kpre);
     if (more_v) store_v<D>(lds_v + ((kt + 1) & 1) * T::LDS_V, tid, vpre);
+    // Every load of this step has been consumed by now; saying so on all
+    // paths keeps the compiler from assuming a load skipped by a branch is
+    // still in flight, which would make the next step's prefetch loads wait
+    // for one another.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
@@ -503,10 +519,64 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
 // (batch, kv head) against the G query heads of that group (the MFMA's 32
 // query columns, G used).  Each wave starts from a fresh state and writes its
 // partial (m, l, acc[d]) to the workspace; the merge kernel combines them.
-// K / V operands are loaded straight from global memory (no reuse to stage).
+// K / V operands are loaded straight from global memory (each byte is read
+// once), one 64-key tile ahead of the one being computed, so a wave always
+// has a tile of HBM reads in flight behind its MFMA / softmax work.  Rows
+// and blocks past the valid keys are clamped to the last valid one (finite
+// data, masked scores, zero P).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int ones_scale) {
+struct DecTile {
+  uint4 k0[D / 64], k1[D / 64];
+  uint32_t ks0[(D / 64 + 1) / 2], ks1[(D / 64 + 1) / 2];  // raw scale words (shifted at use)
+  uint4 va[D / 32];
+  int vs[D / 32];
+};
+
+// Raw 32-bit word holding the scale byte of K block 2j + h of a row.
+template <int DS>
+__device__ __forceinline__ uint32_t k_scale_raw(const uint8_t* p, int j) {
+  if constexpr (DS == 2) {
+    return *reinterpret_cast<const uint16_t*>(p);
+  } else {
+    return reinterpret_cast<const uint32_t*>(p)[j >> 1];
+  }
+}
+
+// Loads of the 64-key tile at n0.  Keys past last_key (and V blocks past
+// last_blk) are clamped to it, so the load count is the same for every tile,
+// including the prefetch past the end of the chunk (a re-read of rows just
+// loaded).  A fixed count lets each step wait for exactly the tile it uses.
+template <int D>
+__device__ __forceinline__ void dec_load(const AttnArgs& a, int64_t bkv, int n0, int last_key,
+                                         int last_blk, int nblk_cap, int r0, int r1, int n,
+                                         int h, DecTile<D>& t) {
+  constexpr int DB = D / 2, DS = D / 32, NJ = D / 64, NC = D / 32;
+  const int64_t k0row = bkv * a.cap + min(n0 + r0, last_key);
+  const int64_t k1row = bkv * a.cap + min(n0 + r1, last_key);
+  const uint8_t* kc0 = a.k_codes + k0row * DB + 16 * h;
+  const uint8_t* kc1 = a.k_codes + k1row * DB + 16 * h;
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
+    t.k0[j] = *reinterpret_cast<const uint4*>(kc0 + 32 * j);
+    t.k1[j] = *reinterpret_cast<const uint4*>(kc1 + 32 * j);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; j += 2) {
+    t.ks0[j / 2] = k_scale_raw<DS>(a.k_scales + k0row * DS, j);
+    t.ks1[j / 2] = k_scale_raw<DS>(a.k_scales + k1row * DS, j);
+  }
+  const int64_t vb = bkv * nblk_cap + min(n0 / 32 + h, last_blk);
+#pragma unroll
+  for (int cc = 0; cc < NC; cc++) {
+    t.va[cc] = *reinterpret_cast<const uint4*>(a.v_codes + (vb * D + 32 * cc + n) * 16);
+    t.vs[cc] = a.v_scales[vb * D + 32 * cc + n];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_split_kernel(AttnArgs a,
+                                                                                  int ones_scale) {
   constexpr int DB = D / 2, DS = D / 32, NJ = D / 64, NC = D / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -521,27 +591,24 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
   const int s0 = chunk_idx * a.chunk;
   if (s0 >= L) return;  // uniform per wave; no barriers below
   const int s1 = min(L, s0 + a.chunk);
-  const int nblk_valid = (L + 31) / 32;
   const int nblk_cap = (a.cap + 31) / 32;
 
   // Q operand: column n is query head g*G + n (zero for n >= G).
   uint4 qa[NJ];
-  int qs[NJ];
+  int qsw[(NJ + 1) / 2];
   if (n < G) {
     const int64_t row = ((int64_t)b * a.Hq + g * G + n);  // Sq == 1
     const uint8_t* qc = a.q_codes + row * DB;
     const uint8_t* qsc = a.q_scales + row * DS;
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
-      qs[j] = qsc[2 * j + h];
-    }
+    for (int j = 0; j < NJ; j++) qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
+#pragma unroll
+    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = k_scale_word<DS>(qsc, j, h);
   } else {
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      qa[j] = make_uint4(0, 0, 0, 0);
-      qs[j] = 0;
-    }
+    for (int j = 0; j < NJ; j++) qa[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = 0;
   }
   const uint32_t one_bits = n == 0 ? 0x22222222u : 0u;
   const uint4 ones = make_uint4(one_bits, one_bits, one_bits, one_bits);
@@ -552,56 +619,42 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
   v16f accl = v16f{};
   const int r0 = perm_row(0, n), r1 = perm_row(1, n);
+  const int last_key = s1 - 1, last_blk = (s1 - 1) / 32;
 
-  for (int n0 = s0; n0 < s1; n0 += kBN) {
+  // one 64-key step on the tile in `cur`, with the next tile's loads issued
+  // into `nxt` first
+  auto step = [&](int n0, const DecTile<D>& cur, DecTile<D>& nxt) {
+    dec_load<D>(a, bkv, n0 + kBN, last_key, last_blk, nblk_cap, r0, r1, n, h, nxt);
     v16f t0 = v16f{}, t1 = v16f{};
-    const int k0row = n0 + r0, k1row = n0 + r1;
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
-      uint4 k0 = make_uint4(0, 0, 0, 0), k1 = make_uint4(0, 0, 0, 0);
-      int ks0 = 0, ks1 = 0;
-      if (k0row < L) {
-        k0 = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + k0row) * DB + 32 * j + 16 * h);
-        ks0 = a.k_scales[(bkv * a.cap + k0row) * DS + 2 * j + h];
+      const int ks0 = (int)(cur.ks0[j / 2] >> (8 * h)), ks1 = (int)(cur.ks1[j / 2] >> (8 * h));
+      if (j % 2 == 0) {
+        t0 = mfma_fp4_sel<0>(cur.k0[j], qa[j], t0, ks0, qsw[j / 2]);
+        t1 = mfma_fp4_sel<0>(cur.k1[j], qa[j], t1, ks1, qsw[j / 2]);
+      } else {
+        t0 = mfma_fp4_sel<2>(cur.k0[j], qa[j], t0, ks0, qsw[j / 2]);
+        t1 = mfma_fp4_sel<2>(cur.k1[j], qa[j], t1, ks1, qsw[j / 2]);
       }
-      if (k1row < L) {
-        k1 = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + k1row) * DB + 32 * j + 16 * h);
-        ks1 = a.k_scales[(bkv * a.cap + k1row) * DS + 2 * j + h];
-      }
-      t0 = mfma_fp4_32x32x64(k0, qa[j], t0, ks0, qs[j]);
-      t1 = mfma_fp4_32x32x64(k1, qa[j], t1, ks1, qs[j]);
     }
-    float s[32];
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      s[r] = t0[r];
-      s[16 + r] = t1[r];
-    }
-    if (n0 + kBN > s1) {
-      const int kb = n0 + 32 * h;
-#pragma unroll
-      for (int k = 0; k < 32; k++)
-        if (kb + k >= s1) s[k] = -INFINITY;
-    }
-    const SoftmaxStep st = softmax_step(s, m_run, c, a.tau);
+    if (n0 + kBN > s1) mask_scores(t0, t1, n0 + 32 * h, s1);
+    const SoftmaxStep st = softmax_step(t0, t1, m_run, c, a.tau);
     if (__any(st.alpha != 1.0f)) {
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
       accl[0] *= st.alpha;
     }
-    const int gb = n0 / 32 + h;
 #pragma unroll
-    for (int cc = 0; cc < NC; cc++) {
-      const int ch = 32 * cc + n;
-      uint4 va = make_uint4(0, 0, 0, 0);
-      int vs = 0;
-      if (gb < nblk_valid) {
-        va = *reinterpret_cast<const uint4*>(a.v_codes + ((bkv * nblk_cap + gb) * D + ch) * 16);
-        vs = a.v_scales[(bkv * nblk_cap + gb) * D + ch];
-      }
-      acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
-    }
+    for (int cc = 0; cc < NC; cc++)
+      acc[cc] = mfma_fp4_32x32x64(cur.va[cc], st.p_codes, acc[cc], cur.vs[cc], st.p_scale);
     accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
+  };
+
+  DecTile<D> ta, tb;
+  dec_load<D>(a, bkv, s0, last_key, last_blk, nblk_cap, r0, r1, n, h, ta);
+  for (int n0 = s0; n0 < s1; n0 += 2 * kBN) {
+    step(n0, ta, tb);
+    if (n0 + kBN < s1) step(n0 + kBN, tb, ta);
   }
 
   // partial row: [m, l, acc[0..D)] for (b, query head, chunk)
@@ -624,8 +677,25 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
 }
 
 // Log-sum-exp merge of the chunk partials: one wave per (batch, query head).
+// Lane i owns chunk i (and i + 64, ...) for the max and the normaliser (wave
+// reductions); the accumulators are combined channel-parallel, eight chunks
+// per round so that eight partial rows are in flight at once.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
+  constexpr int CPL = (D + 63) / 64;  // channels per lane
+  constexpr int U = 8;                // chunks per round
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);  // b * Hq + hq
   if (row >= (int64_t)a.B * a.Hq) return;
@@ -636,22 +706,33 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
   const float* part = a.partials + row * a.n_chunks * (D + 2);
   float M = -INFINITY;
   for (int i = lane; i < nc; i += 64) M = fmaxf(M, part[(int64_t)i * (D + 2)]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  constexpr int CPL = (D + 63) / 64;  // channels per lane
+  M = wave_max(M);
+  float lpart = 0.0f;
+  for (int i = lane; i < nc; i += 64) {
+    const float* pr = part + (int64_t)i * (D + 2);
+    lpart += fast_exp2(pr[0] - M) * pr[1];
+  }
+  const float lsum = M == -INFINITY ? 0.0f : wave_sum(lpart);
   float o[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; j++) o[j] = 0.0f;
-  float lsum = 0.0f;
-  for (int i = 0; i < nc; i++) {
-    const float* pr = part + (int64_t)i * (D + 2);
-    const float w = M == -INFINITY ? 0.0f : fast_exp2(pr[0] - M);
-    lsum += w * pr[1];
+  for (int i0 = 0; i0 < nc; i0 += U) {
+    float w[U], x[U][CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; j++) {
-      const int ch = lane + 64 * j;
-      if (ch < D) o[j] += w * pr[2 + ch];
+    for (int u = 0; u < U; u++) {
+      const int i = min(i0 + u, nc - 1);
+      const float* pr = part + (int64_t)i * (D + 2);
+      w[u] = (i0 + u < nc && M != -INFINITY) ? fast_exp2(pr[0] - M) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < CPL; j++) {
+        const int ch = lane + 64 * j;
+        x[u][j] = ch < D ? pr[2 + ch] : 0.0f;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int j = 0; j < CPL; j++) o[j] += w[u] * x[u][j];
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
