@@ -33,6 +33,8 @@
 // The row max over a step needs one exchange between lanes l and l ^ 32.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -87,25 +89,33 @@ struct SoftmaxStep {
 // The row max needs the partner lane l ^ 32 (the other 32 keys of the step):
 // v_permlane32_swap exchanges the two halves of the wave in one VALU op, and
 // the max of its two results is max(own, partner) in every lane.
+__device__ __forceinline__ float fmax_(float a, float b) {
+  // IEEE maximum (v_maximum3_f32): no NaN-quieting of the operands needed
+  return __builtin_elementwise_maximum(a, b);
+}
+
 __device__ __forceinline__ float max_with_half_swap(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Softmax step on the lane's 32 scores held in the two QK accumulators (tile
 // t, register r <-> key 32h + 16t + r), in place: the scores are replaced by
 // P before packing, so no copies of the accumulators are made.  Masked
 // scores are -inf on entry.
+//
+// `pk` is the previous step's packed P: every byte of it is overwritten, it
+// only gives the partial-write converts a register to start from.
 __device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m_run, float c,
-                                                    float tau) {
+                                                    float tau, uint4& pk) {
   float ma = s0[0], mb = s1[0];
 #pragma unroll
   for (int r = 1; r < 16; r++) {
-    ma = fmaxf(ma, s0[r]);
-    mb = fmaxf(mb, s1[r]);
+    ma = fmax_(ma, s0[r]);
+    mb = fmax_(mb, s1[r]);
   }
-  const float bm = fmaxf(ma, mb);
+  const float bm = fmax_(ma, mb);
   const float bmc = bm * c;  // contraction is off in this file: a rounded product
   const float rmc = max_with_half_swap(bmc);
   const float m_new = rmc > m_run + tau ? rmc : m_run;
@@ -121,12 +131,12 @@ __device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m
   const uint32_t sb = e8m0_from_amax(pmax);
   st.p_scale = (int)sb;
   const float scale = e8m0_to_float(sb);
-  uint32_t w[4];
+  uint32_t w[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const v16f& src = q < 2 ? s0 : s1;
     const int o = 8 * (q & 1);
-    uint32_t x = 0;
+    uint32_t x = w[q];
     x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 0], src[o + 1], scale, 0);
     x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 2], src[o + 3], scale, 1);
     x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 4], src[o + 5], scale, 2);
@@ -134,6 +144,7 @@ __device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m
     w[q] = x;
   }
   st.p_codes = make_uint4(w[0], w[1], w[2], w[3]);
+  pk = st.p_codes;
   m_run = m_new;
   return st;
 }
@@ -218,31 +229,48 @@ struct VRegs {
   uint32_t vs;  // one 4-byte word of V scales
 };
 
-// Global loads of a 64-key tile starting at n0.  Rows / blocks past the valid
-// keys are clamped to the last valid one (finite data); their scores are
-// masked and their P is zero, so they never contribute.
+// Raw buffer resource (stride 0) over `bytes` bytes from `base`: the
+// hardware range check turns every load at or past `bytes` into zeros.  The
+// third descriptor word is the gfx9-family default (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Global loads of a 64-key tile starting at n0.  A tile's K codes, K scales,
+// V codes and V scales are each one contiguous run of bytes, so thread tid
+// loads chunk tid (+ 256 i) of each at a fixed lane offset from a uniform
+// tile base.  The buffer resources end at the last valid key (K) / block
+// (V): rows and blocks past them read as zeros (E2M1 zeros with the E8M0
+// byte 0, i.e. finite), their scores are masked and their P is zero, so
+// they never contribute.  No per-lane clamping or 64-bit address math.
 template <int D>
 __device__ __forceinline__ void load_k(const AttnArgs& a, int64_t bkv, int n0, int L, int tid,
                                        KRegs<D>& r) {
   using T = PrefillTile<D>;
+  const int64_t row0 = bkv * a.cap + n0;
+  const uint32_t rows = (uint32_t)(L - n0);
+  const auto kc = buffer_rsrc(a.k_codes + row0 * T::DB, rows * T::DB);
+  const auto ks = buffer_rsrc(a.k_scales + row0 * T::DS, rows * T::DS);
 #pragma unroll
   for (int i = 0; i < T::KC_T; i++) {
     const int ci = tid + 256 * i;
-    if (ci < T::KC) {
-      const int row = ci / (T::DB / 16), off = (ci % (T::DB / 16)) * 16;
-      const int key = min(n0 + row, L - 1);
-      r.kc[i] = *reinterpret_cast<const uint4*>(a.k_codes + (bkv * a.cap + key) * T::DB + off);
-    }
+    if (ci < T::KC) r.kc[i] = buffer_load16(kc, (uint32_t)ci * 16u);
   }
   if (tid < kBN) {
-    const int key = min(n0 + tid, L - 1);
-    const uint8_t* src = a.k_scales + (bkv * a.cap + key) * T::DS;
+    const uint32_t off = (uint32_t)tid * T::DS;
     if constexpr (T::DS == 2) {
-      r.ks = make_uint2(*reinterpret_cast<const uint16_t*>(src), 0);
+      r.ks = make_uint2(__builtin_amdgcn_raw_buffer_load_b16(ks, off, 0, 0), 0);
     } else if constexpr (T::DS == 4) {
-      r.ks = make_uint2(*reinterpret_cast<const uint32_t*>(src), 0);
+      r.ks = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(ks, off, 0, 0), 0);
     } else {
-      r.ks = *reinterpret_cast<const uint2*>(src);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ks, off, 0, 0);
+      r.ks = make_uint2(v[0], v[1]);
     }
   }
 }
@@ -251,20 +279,17 @@ template <int D>
 __device__ __forceinline__ void load_v(const AttnArgs& a, int64_t bkv, int n0, int nblk_valid,
                                        int nblk_cap, int tid, VRegs<D>& r) {
   using T = PrefillTile<D>;
+  const int b0 = n0 / 32;
+  const int64_t blk0 = bkv * nblk_cap + b0;
+  const uint32_t blks = (uint32_t)(nblk_valid - b0);
+  const auto vc = buffer_rsrc(a.v_codes + blk0 * D * 16, blks * D * 16);
+  const auto vs = buffer_rsrc(a.v_scales + blk0 * D, blks * D);
 #pragma unroll
   for (int i = 0; i < T::VC_T; i++) {
     const int ci = tid + 256 * i;
-    if (ci < T::VC) {
-      const int blk = ci / D, ch = ci % D;
-      const int gb = min(n0 / 32 + blk, nblk_valid - 1);
-      r.vc[i] = *reinterpret_cast<const uint4*>(a.v_codes + ((bkv * nblk_cap + gb) * D + ch) * 16);
-    }
+    if (ci < T::VC) r.vc[i] = buffer_load16(vc, (uint32_t)ci * 16u);
   }
-  if (tid < T::VS_W) {
-    const int blk = (tid * 4) / D, off = (tid * 4) % D;
-    const int gb = min(n0 / 32 + blk, nblk_valid - 1);
-    r.vs = *reinterpret_cast<const uint32_t*>(a.v_scales + (bkv * nblk_cap + gb) * D + off);
-  }
+  if (tid < T::VS_W) r.vs = __builtin_amdgcn_raw_buffer_load_b32(vs, (uint32_t)tid * 4u, 0, 0);
 }
 
 template <int D>
@@ -425,6 +450,7 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   const float c = a.sm_log2;
 
   float m_run = -INFINITY;
+  uint4 pk = make_uint4(0, 0, 0, 0);
   v16f acc[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
@@ -454,8 +480,11 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // One pipeline step: scores of tile kt are in (c0, c1); the next tile's go
   // to (n0r, n1r).  The loop below alternates the two register sets, so no
   // copies are needed; registers of a tile a wave does not compute are never
-  // read (the softmax of that tile is skipped as well).
-  auto step = [&](int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
+  // read (the softmax of that tile is skipped as well).  P is the parity of
+  // kt, a compile-time constant, so every LDS address is a per-lane base plus
+  // an immediate offset.
+  auto step = [&](auto parity, int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
+    constexpr int P = decltype(parity)::value;
     const int n0 = kt * kBN;
     const bool more_k = kt + 2 < n_tiles, more_v = kt + 1 < n_tiles;
     if (more_k) load_k<D>(a, bkv, n0 + 2 * kBN, L, tid, kpre);
@@ -463,12 +492,12 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
 
     // scores of the next tile go to the matrix core first
     if (more_v && n0 + kBN < wave_end)
-      qk_step<D>(lds_k + ((kt + 1) & 1) * T::LDS_K, qa, qsw, n, h, n0r, n1r);
+      qk_step<D>(lds_k + (1 - P) * T::LDS_K, qa, qsw, n, h, n0r, n1r);
     __builtin_amdgcn_sched_barrier(0);
 
     if (n0 < wave_end) {  // uniform per wave
       if (n0 + kBN > wave_full) mask_scores(c0, c1, n0 + 32 * h, row_lim);
-      const SoftmaxStep st = softmax_step(c0, c1, m_run, c, a.tau);
+      const SoftmaxStep st = softmax_step(c0, c1, m_run, c, a.tau, pk);
       // rescale only when some row's max moved (multiplying by 1 is exact)
       if (__any(st.alpha != 1.0f)) {
 #pragma unroll
@@ -477,7 +506,7 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
       }
 
       // ---- [acc | l] += P_hat [V | 1]
-      const uint8_t* vbuf = lds_v + (kt & 1) * T::LDS_V;
+      const uint8_t* vbuf = lds_v + P * T::LDS_V;
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         const int ch = 32 * cc + n;
@@ -487,8 +516,8 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
       }
       accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
     }
-    if (more_k) store_k<D>(lds_k + (kt & 1) * T::LDS_K, tid, kpre);
-    if (more_v) store_v<D>(lds_v + ((kt + 1) & 1) * T::LDS_V, tid, vpre);
+    if (more_k) store_k<D>(lds_k + P * T::LDS_K, tid, kpre);
+    if (more_v) store_v<D>(lds_v + (1 - P) * T::LDS_V, tid, vpre);
     // Every load of this step has been consumed by now; saying so on all
     // paths keeps the compiler from assuming a load skipped by a branch is
     // still in flight, which would make the next step's prefetch loads wait
@@ -500,8 +529,8 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   v16f sa0, sa1, sb0, sb1;
   if (0 < wave_end) qk_step<D>(lds_k, qa, qsw, n, h, sa0, sa1);
   for (int kt = 0; kt < n_tiles; kt += 2) {
-    step(kt, sa0, sa1, sb0, sb1);
-    if (kt + 1 < n_tiles) step(kt + 1, sb0, sb1, sa0, sa1);
+    step(std::integral_constant<int, 0>{}, kt, sa0, sa1, sb0, sb1);
+    if (kt + 1 < n_tiles) step(std::integral_constant<int, 1>{}, kt + 1, sb0, sb1, sa0, sa1);
   }
 
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
@@ -614,6 +643,7 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_spli
   const uint4 ones = make_uint4(one_bits, one_bits, one_bits, one_bits);
   const float c = a.sm_log2;
   float m_run = -INFINITY;
+  uint4 pk = make_uint4(0, 0, 0, 0);
   v16f acc[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
@@ -638,7 +668,7 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_spli
       }
     }
     if (n0 + kBN > s1) mask_scores(t0, t1, n0 + 32 * h, s1);
-    const SoftmaxStep st = softmax_step(t0, t1, m_run, c, a.tau);
+    const SoftmaxStep st = softmax_step(t0, t1, m_run, c, a.tau, pk);
     if (__any(st.alpha != 1.0f)) {
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
