@@ -180,153 +180,6 @@ __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row, int h,
   }
 }
 
-// ---------------------------------------------------------------------------
-// Prefill: one workgroup = 128 queries of one (batch, query head); 4 waves of
-// 32 queries share 64-key K / V tiles staged in LDS.
-//
-// Software pipeline.  Step kt of a wave issues the Q K^T MFMAs of tile kt+1
-// first, then runs the softmax of tile kt (whose scores came out of the
-// previous step) and its P V MFMAs: the matrix core computes the next scores
-// while the vector ALU does the exponentials and FP4 conversions.  K is
-// therefore staged one tile ahead of V: during step kt the LDS holds K of
-// tile kt+1 and V of tile kt, and the bytes of K tile kt+2 / V tile kt+1 are
-// in flight into registers; they are written to the free buffers at the end
-// of the step and one barrier per step publishes them.
-//
-// K rows are stored in LDS in the order the MFMA A operand reads them (row
-// 32t + n of a buffer holds key perm_row(t, n)) with a padded stride of
-// d/2 + 16 bytes, so the 16-byte reads of 8 neighbouring lanes fall in
-// distinct bank groups.
-// ---------------------------------------------------------------------------
-template <int D>
-struct PrefillTile {
-  static constexpr int DB = D / 2;               // code bytes per K row
-  static constexpr int DS = D / 32;              // scale bytes per K row
-  static constexpr int RS = DB + 16;             // padded LDS stride of a K row
-  static constexpr int KC = kBN * DB / 16;       // 16-byte K code chunks per tile
-  static constexpr int VC = 2 * D;               // 16-byte V code chunks per tile
-  static constexpr int KC_T = (KC + 255) / 256;  // per thread
-  static constexpr int VC_T = (VC + 255) / 256;
-  static constexpr int VS_W = 2 * D / 4;         // 4-byte V scale words per tile
-  static constexpr int LDS_K = kBN * RS + kBN * DS;   // codes + scales of one K tile
-  static constexpr int LDS_V = VC * 16 + 2 * D;       // codes + scales of one V tile
-};
-
-// LDS row of key r in the read order of the QK A operand.
-__device__ __forceinline__ int k_lds_row(int r) {
-  return 32 * ((r >> 4) & 1) + 8 * ((r >> 2) & 3) + 4 * (r >> 5) + (r & 3);
-}
-
-template <int D>
-struct KRegs {
-  uint4 kc[PrefillTile<D>::KC_T];
-  uint2 ks;  // DS scale bytes of one K row (threads < 64)
-};
-
-template <int D>
-struct VRegs {
-  uint4 vc[PrefillTile<D>::VC_T];
-  uint32_t vs;  // one 4-byte word of V scales
-};
-
-// Raw buffer resource (stride 0) over `bytes` bytes from `base`: the
-// hardware range check turns every load at or past `bytes` into zeros.  The
-// third descriptor word is the gfx9-family default (32-bit data format).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Global loads of a 64-key tile starting at n0.  A tile's K codes, K scales,
-// V codes and V scales are each one contiguous run of bytes, so thread tid
-// loads chunk tid (+ 256 i) of each at a fixed lane offset from a uniform
-// tile base.  The buffer resources end at the last valid key (K) / block
-// (V): rows and blocks past them read as zeros (E2M1 zeros with the E8M0
-// byte 0, i.e. finite), their scores are masked and their P is zero, so
-// they never contribute.  No per-lane clamping or 64-bit address math.
-template <int D>
-__device__ __forceinline__ void load_k(const AttnArgs& a, int64_t bkv, int n0, int L, int tid,
-                                       KRegs<D>& r) {
-  using T = PrefillTile<D>;
-  const int64_t row0 = bkv * a.cap + n0;
-  const uint32_t rows = (uint32_t)(L - n0);
-  const auto kc = buffer_rsrc(a.k_codes + row0 * T::DB, rows * T::DB);
-  const auto ks = buffer_rsrc(a.k_scales + row0 * T::DS, rows * T::DS);
-#pragma unroll
-  for (int i = 0; i < T::KC_T; i++) {
-    const int ci = tid + 256 * i;
-    if (ci < T::KC) r.kc[i] = buffer_load16(kc, (uint32_t)ci * 16u);
-  }
-  if (tid < kBN) {
-    const uint32_t off = (uint32_t)tid * T::DS;
-    if constexpr (T::DS == 2) {
-      r.ks = make_uint2(__builtin_amdgcn_raw_buffer_load_b16(ks, off, 0, 0), 0);
-    } else if constexpr (T::DS == 4) {
-      r.ks = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(ks, off, 0, 0), 0);
-    } else {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ks, off, 0, 0);
-      r.ks = make_uint2(v[0], v[1]);
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_v(const AttnArgs& a, int64_t bkv, int n0, int nblk_valid,
-                                       int nblk_cap, int tid, VRegs<D>& r) {
-  using T = PrefillTile<D>;
-  const int b0 = n0 / 32;
-  const int64_t blk0 = bkv * nblk_cap + b0;
-  const uint32_t blks = (uint32_t)(nblk_valid - b0);
-  const auto vc = buffer_rsrc(a.v_codes + blk0 * D * 16, blks * D * 16);
-  const auto vs = buffer_rsrc(a.v_scales + blk0 * D, blks * D);
-#pragma unroll
-  for (int i = 0; i < T::VC_T; i++) {
-    const int ci = tid + 256 * i;
-    if (ci < T::VC) r.vc[i] = buffer_load16(vc, (uint32_t)ci * 16u);
-  }
-  if (tid < T::VS_W) r.vs = __builtin_amdgcn_raw_buffer_load_b32(vs, (uint32_t)tid * 4u, 0, 0);
-}
-
-template <int D>
-__device__ __forceinline__ void store_k(uint8_t* buf, int tid, const KRegs<D>& r) {
-  using T = PrefillTile<D>;
-  uint8_t* ks = buf + kBN * T::RS;
-#pragma unroll
-  for (int i = 0; i < T::KC_T; i++) {
-    const int ci = tid + 256 * i;
-    if (ci < T::KC) {
-      const int row = ci / (T::DB / 16), off = (ci % (T::DB / 16)) * 16;
-      *reinterpret_cast<uint4*>(buf + k_lds_row(row) * T::RS + off) = r.kc[i];
-    }
-  }
-  if (tid < kBN) {
-    uint8_t* dst = ks + k_lds_row(tid) * T::DS;
-    if constexpr (T::DS == 2) {
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)r.ks.x;
-    } else if constexpr (T::DS == 4) {
-      *reinterpret_cast<uint32_t*>(dst) = r.ks.x;
-    } else {
-      *reinterpret_cast<uint2*>(dst) = r.ks;
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_v(uint8_t* buf, int tid, const VRegs<D>& r) {
-  using T = PrefillTile<D>;
-#pragma unroll
-  for (int i = 0; i < T::VC_T; i++) {
-    const int ci = tid + 256 * i;
-    if (ci < T::VC) *reinterpret_cast<uint4*>(buf + ci * 16) = r.vc[i];
-  }
-  if (tid < T::VS_W) *reinterpret_cast<uint32_t*>(buf + T::VC * 16 + tid * 4) = r.vs;
-}
-
 // Scale operand of K block (2j + h) of a row whose DS scale bytes start at p:
 // the 32-bit word holding it, shifted by 8h so that byte 2*(j%2) is the one.
 template <int DS>
@@ -347,22 +200,194 @@ __device__ __forceinline__ v16f mfma_fp4_sel(const uint4& a, const uint4& b, con
                                                          OPSEL, sb);
 }
 
-// S^T = K Q^T for the two 32-key tiles of a 64-key step held in one K buffer.
+// ---------------------------------------------------------------------------
+// Prefill: one workgroup = 128 queries of one (batch, query head); 4 waves of
+// 32 queries share 64-key K / V tiles staged in LDS.
+//
+// Software pipeline.  Step kt of a wave issues the Q K^T MFMAs of tile kt+1
+// first, then runs the softmax of tile kt (whose scores came out of the
+// previous step) and its P V MFMAs: the matrix core computes the next scores
+// while the vector ALU does the exponentials and FP4 conversions.
+//
+// Staging.  K and V tiles go from memory straight into LDS (buffer loads
+// with the LDS destination: no registers, no LDS store instructions) through
+// rings of three buffers.  Step kt reads K tile kt+1 and V tile kt and issues
+// the loads of K tile kt+3 and V tile kt+2 into the buffers the previous
+// step finished with; before its closing barrier it waits only for the loads
+// issued one step earlier (K tile kt+2, V tile kt+1), so every load has two
+// steps of compute to arrive.  Each wave loads a quarter of every tile and
+// issues the same number of loads each step (past the last tile with an
+// empty descriptor range), so a fixed vmcnt(N) wait is exact.
+//
+// The loads are written in inline asm: the compiler then neither makes LDS
+// reads of other buffers wait for them nor drains them at the barrier, and
+// the explicit vector-memory waits below are the synchronisation.  They have
+// no register results.
+//
+// K layout in LDS: dense rows of d/2 bytes in the order the MFMA A operand
+// reads them (row R = 32t + n holds key perm_row(t, n)), the 16-byte chunks
+// of row R XOR-swizzled by k_swz(R) so that the 16-byte reads of
+// neighbouring lanes fall in distinct banks; the scale bytes follow in the
+// same row order, max(d/32, 4) bytes per row.  V keeps its global layout
+// (key-blocked, channel-major).
+// The permutation and the swizzle are applied on the global side: lane i of
+// a load writes LDS bytes 16i .. 16i+15 and fetches whatever belongs there.
+// ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void qk_step(const uint8_t* kbuf, const uint4 (&qa)[D / 64],
+struct PrefillTile {
+  static constexpr int DB = D / 2;    // code bytes per K row
+  static constexpr int DS = D / 32;   // scale bytes per K row
+  static constexpr int NCH = DB / 16; // 16-byte chunks per K row
+  static constexpr int RPB_SHIFT = D == 64 ? 2 : (D == 128 ? 1 : 0);  // log2(K rows per 128 B)
+  static constexpr int KSS = DS < 4 ? 4 : DS;        // LDS slot of one row's K scales
+  static constexpr int KS_OFF = kBN * DB;            // K scales within a K stage
+  static constexpr int K_BYTES = KS_OFF + kBN * KSS; // one K stage
+  static constexpr int VS_OFF = 2 * D * 16;          // V scales within a V stage
+  static constexpr int V_BYTES = VS_OFF + 2 * D;     // one V stage
+  // Per wave and tile: 16-byte K / V code chunks, K scale lanes (one row per
+  // lane, two lanes per row when a row has 8 scale bytes) and 4-byte V scale
+  // words.
+  static constexpr int KC_W = DB;
+  static constexpr int VC_W = D / 2;
+  static constexpr int KS_W = DS == 8 ? 32 : 16;
+  static constexpr int VS_W = D / 8;
+  static constexpr int KC_I = (KC_W + 63) / 64;  // load instructions for them
+  static constexpr int VC_I = (VC_W + 63) / 64;
+  static constexpr int N_LOADS = KC_I + VC_I + 2;  // per wave and step
+  static_assert(N_LOADS < 16, "vmcnt encoding below assumes fewer than 16");
+};
+
+template <int D>
+__device__ __forceinline__ int k_swz(int R) {
+  using T = PrefillTile<D>;
+  return ((R >> T::RPB_SHIFT) ^ (R >> 3)) & (T::NCH - 1);
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0) over `bytes` bytes from `base`: loads at
+// or past `bytes` return zeros.  Word 3 is the gfx9-family default format.
+__device__ __forceinline__ v4i buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+
+// Memory -> LDS, 16 / 4 bytes per lane: lane i writes LDS bytes
+// [lds + size*i, lds + size*(i+1)) with the bytes at `off` of the buffer.
+// (Lane placement pinned by the LDS-load probe.)
+__device__ __forceinline__ void load_lds16(v4i desc, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(off), "s"(desc) : "memory");
+}
+__device__ __forceinline__ void load_lds4(v4i desc, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(off), "s"(desc) : "memory");
+}
+// 2 bytes per lane, written zero-extended as a dword at lds + 4i.
+__device__ __forceinline__ void load_lds2(v4i desc, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(off), "s"(desc) : "memory");
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding).
+#define HIFA4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
+// Per-lane source offsets of a wave's share of a tile (loop invariant).
+template <int D>
+struct TileLanes {
+  uint32_t kc[PrefillTile<D>::KC_I];
+  uint32_t ks;
+};
+
+template <int D>
+__device__ __forceinline__ TileLanes<D> tile_lanes(int w, int lane) {
+  using T = PrefillTile<D>;
+  TileLanes<D> tl;
+#pragma unroll
+  for (int i = 0; i < T::KC_I; i++) {
+    const int b = w * T::KC_W + 64 * i + lane;  // chunk index in LDS order
+    const int R = b / T::NCH, pos = b % T::NCH;
+    const int key = perm_row(R >> 5, R & 31);
+    tl.kc[i] = (uint32_t)(key * T::DB + ((pos ^ k_swz<D>(R)) * 16));
+  }
+  {
+    // the wave's 16 rows 16w .. 16w + 15 (LDS order); 8-byte rows take two
+    // lanes of 4 bytes each
+    const int R = 16 * w + (T::DS == 8 ? lane >> 1 : lane);
+    tl.ks = (uint32_t)(perm_row(R >> 5, R & 31) * T::DS + (T::DS == 8 ? 4 * (lane & 1) : 0));
+  }
+  return tl;
+}
+
+// Issue the wave's loads of K tile `tile` into the K stage at `stage`.
+template <int D>
+__device__ __forceinline__ void issue_k(const AttnArgs& a, int64_t bkv, int tile, int n_tiles,
+                                        int L, uint32_t stage, int w, int lane,
+                                        const TileLanes<D>& tl) {
+  using T = PrefillTile<D>;
+  const int n0 = tile * kBN;
+  const uint32_t rows = tile < n_tiles ? (uint32_t)(L - n0) : 0u;
+  const int64_t row0 = bkv * a.cap + n0;
+  const v4i kc = buffer_desc(a.k_codes + row0 * T::DB, rows * T::DB);
+  const v4i ks = buffer_desc(a.k_scales + row0 * T::DS, rows * T::DS);
+#pragma unroll
+  for (int i = 0; i < T::KC_I; i++)
+    if (64 * i + lane < T::KC_W) load_lds16(kc, tl.kc[i], stage + (w * T::KC_W + 64 * i) * 16);
+  if (lane < T::KS_W) {
+    const uint32_t dst = stage + T::KS_OFF + 16 * w * T::KSS;
+    if constexpr (T::DS == 2)
+      load_lds2(ks, tl.ks, dst);  // one row's 2 bytes, zero-extended into its 4-byte slot
+    else
+      load_lds4(ks, tl.ks, dst);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void issue_v(const AttnArgs& a, int64_t bkv, int tile, int n_tiles,
+                                        int nblk_valid, int nblk_cap, uint32_t stage, int w,
+                                        int lane) {
+  using T = PrefillTile<D>;
+  const int b0 = 2 * tile;
+  const uint32_t blks = tile < n_tiles ? (uint32_t)(nblk_valid - b0) : 0u;
+  const int64_t blk0 = bkv * nblk_cap + b0;
+  const v4i vc = buffer_desc(a.v_codes + blk0 * D * 16, blks * D * 16);
+  const v4i vs = buffer_desc(a.v_scales + blk0 * D, blks * D);
+#pragma unroll
+  for (int i = 0; i < T::VC_I; i++) {
+    const int c = w * T::VC_W + 64 * i;
+    if (64 * i + lane < T::VC_W) load_lds16(vc, (uint32_t)(c + lane) * 16u, stage + c * 16);
+  }
+  const int sw = w * T::VS_W;
+  if (lane < T::VS_W) load_lds4(vs, (uint32_t)(sw + lane) * 4u, stage + T::VS_OFF + sw * 4);
+}
+
+// S^T = K Q^T for the two 32-key tiles of a 64-key step held in one K stage.
+// koff[t][j]: the lane's byte offset of its 16-byte A operand chunk.
+template <int D>
+__device__ __forceinline__ void qk_step(const uint8_t* kbuf, const uint32_t (&koff)[2][D / 64],
+                                        const uint4 (&qa)[D / 64],
                                         const int (&qsw)[(D / 64 + 1) / 2], int n, int h,
                                         v16f& s0, v16f& s1) {
   using T = PrefillTile<D>;
   constexpr int NJ = D / 64;
-  const uint8_t* ks = kbuf + kBN * T::RS;
+  const uint8_t* ks = kbuf + T::KS_OFF;
   s0 = v16f{};
   s1 = v16f{};
 #pragma unroll
   for (int j = 0; j < NJ; j++) {
-    const uint4 k0 = *reinterpret_cast<const uint4*>(kbuf + n * T::RS + 32 * j + 16 * h);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(kbuf + (32 + n) * T::RS + 32 * j + 16 * h);
-    const int ks0 = k_scale_word<T::DS>(ks + n * T::DS, j, h);
-    const int ks1 = k_scale_word<T::DS>(ks + (32 + n) * T::DS, j, h);
+    const uint4 k0 = *reinterpret_cast<const uint4*>(kbuf + koff[0][j]);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(kbuf + koff[1][j]);
+    const int ks0 = k_scale_word<T::DS>(ks + n * T::KSS, j, h);
+    const int ks1 = k_scale_word<T::DS>(ks + (32 + n) * T::KSS, j, h);
     if (j % 2 == 0) {
       s0 = mfma_fp4_sel<0>(k0, qa[j], s0, ks0, qsw[j / 2]);
       s1 = mfma_fp4_sel<0>(k1, qa[j], s1, ks1, qsw[j / 2]);
@@ -383,11 +408,12 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   constexpr int DB = T::DB, DS = T::DS;
   constexpr int NJ = D / 64;  // QK MFMAs per 32-key tile
   constexpr int NC = D / 32;  // P V channel tiles
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2 * T::LDS_K];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * T::LDS_V];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[3 * T::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[3 * T::V_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
 
   // Work item.  Linear order: kv head fastest (so the query heads of one GQA
@@ -407,28 +433,10 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   const int L = a.Sk;
   const int64_t bhq = (int64_t)b * a.Hq + hq;
   const int64_t bkv = (int64_t)b * a.Hkv + g;
-  const int q_wave0 = qt * kBR + wave * 32;
+  const int q_wave0 = qt * kBR + w * 32;
   const int q = q_wave0 + n;
   const int nblk_valid = (L + 31) / 32;
   const int nblk_cap = (a.cap + 31) / 32;
-
-  // Q operand (B of S^T = K Q^T): query q, K blocks of 32 along d; its scale
-  // bytes packed so that MFMA j reads byte 2*(j%2) of word j/2.
-  uint4 qa[NJ];
-  int qsw[(NJ + 1) / 2];
-  if (q < a.Sq) {
-    const uint8_t* qc = a.q_codes + (bhq * a.Sq + q) * DB;
-    const uint8_t* qsc = a.q_scales + (bhq * a.Sq + q) * DS;
-#pragma unroll
-    for (int j = 0; j < NJ; j++) qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
-#pragma unroll
-    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = k_scale_word<DS>(qsc, j, h);
-  } else {
-#pragma unroll
-    for (int j = 0; j < NJ; j++) qa[j] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = 0;
-  }
 
   // Key ranges: the workgroup stages every tile any of its rows can see; a
   // wave computes only tiles its own rows can see; tiles below wave_full are
@@ -445,6 +453,56 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   const int row_lim = kCausal ? min(L, q + L - a.Sq + 1) : L;  // keys < row_lim visible
 
+  // Prologue loads: K tiles 0, 1, 2 and V tiles 0, 1 (the ring's steady
+  // state).  They are issued back to back, so waiting for all of them (and
+  // the Q operand) costs little over waiting for K0, V0, K1, and it tells
+  // the compiler that no load it knows of is still in flight in the loop.
+  const TileLanes<D> tl = tile_lanes<D>(w, lane);
+  const uint32_t k_base = lds_addr(lds_k), v_base = lds_addr(lds_v);
+  issue_k<D>(a, bkv, 0, n_tiles, L, k_base, w, lane, tl);
+  issue_v<D>(a, bkv, 0, n_tiles, nblk_valid, nblk_cap, v_base, w, lane);
+  issue_k<D>(a, bkv, 1, n_tiles, L, k_base + T::K_BYTES, w, lane, tl);
+  issue_v<D>(a, bkv, 1, n_tiles, nblk_valid, nblk_cap, v_base + T::V_BYTES, w, lane);
+  issue_k<D>(a, bkv, 2, n_tiles, L, k_base + 2 * T::K_BYTES, w, lane, tl);
+  // Q operand (B of S^T = K Q^T): query q, K blocks of 32 along d; its scale
+  // bytes packed so that MFMA j reads byte 2*(j%2) of word j/2 (raw words
+  // here, shifted for the lane's half once the loads have landed).
+  uint4 qa[NJ];
+  uint32_t qsw_raw[(NJ + 1) / 2];
+  if (q < a.Sq) {
+    const uint8_t* qc = a.q_codes + (bhq * a.Sq + q) * DB;
+    const uint8_t* qsc = a.q_scales + (bhq * a.Sq + q) * DS;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
+#pragma unroll
+    for (int j = 0; j < NJ; j += 2) {
+      if constexpr (DS == 2)
+        qsw_raw[j / 2] = *reinterpret_cast<const uint16_t*>(qsc);
+      else
+        qsw_raw[j / 2] = reinterpret_cast<const uint32_t*>(qsc)[j >> 1];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; j++) qa[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; j += 2) qsw_raw[j / 2] = 0;
+  }
+  HIFA4_WAIT_VMCNT(0);
+  __syncthreads();
+  int qsw[(NJ + 1) / 2];
+#pragma unroll
+  for (int j = 0; j < NJ; j += 2) qsw[j / 2] = (int)(qsw_raw[j / 2] >> (8 * h));
+
+  // The lane's K operand offsets within a stage (row 32t + n, chunk 2j + h).
+  uint32_t koff[2][NJ];
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const int R = 32 * t + n;
+      koff[t][j] = (uint32_t)(R * DB + (((2 * j + h) ^ k_swz<D>(R)) * 16));
+    }
+
   const uint32_t one_bits = n == 0 ? 0x22222222u : 0u;  // E2M1 1.0 in every nibble of row 0
   const uint4 ones = make_uint4(one_bits, one_bits, one_bits, one_bits);
   const float c = a.sm_log2;
@@ -456,43 +514,19 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
   v16f accl = v16f{};
 
-  // prologue: K tiles 0 and 1, V tile 0; scores of tile 0
-  KRegs<D> kpre;
-  VRegs<D> vpre;
-  if (n_tiles > 0) {
-    load_k<D>(a, bkv, 0, L, tid, kpre);
-    load_v<D>(a, bkv, 0, nblk_valid, nblk_cap, tid, vpre);
-    store_k<D>(lds_k, tid, kpre);
-    store_v<D>(lds_v, tid, vpre);
-    if (n_tiles > 1) {
-      load_k<D>(a, bkv, kBN, L, tid, kpre);
-      store_k<D>(lds_k + T::LDS_K, tid, kpre);
-    }
-  }
-  // Drain every outstanding load on all paths into the loop.  Without it the
-  // compiler must assume the Q operand loads may still be in flight at the
-  // loop header (the prologue's loads are conditional) and makes the Q K^T
-  // MFMAs of each step wait on the vector-memory counter, i.e. on the
-  // prefetch loads issued just before them.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // One pipeline step: scores of tile kt are in (c0, c1); the next tile's go
-  // to (n0r, n1r).  The loop below alternates the two register sets, so no
-  // copies are needed; registers of a tile a wave does not compute are never
-  // read (the softmax of that tile is skipped as well).  P is the parity of
-  // kt, a compile-time constant, so every LDS address is a per-lane base plus
-  // an immediate offset.
-  auto step = [&](auto parity, int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
-    constexpr int P = decltype(parity)::value;
+  // One pipeline step on tile kt.  RP = kt mod 3 (ring slot), a compile-time
+  // constant, so every LDS address is a per-lane base plus an immediate.
+  // Scores of tile kt are in (c0, c1); the next tile's go to (n0r, n1r).
+  auto step = [&](auto ring, int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
+    constexpr int RP = decltype(ring)::value;
     const int n0 = kt * kBN;
-    const bool more_k = kt + 2 < n_tiles, more_v = kt + 1 < n_tiles;
-    if (more_k) load_k<D>(a, bkv, n0 + 2 * kBN, L, tid, kpre);
-    if (more_v) load_v<D>(a, bkv, n0 + kBN, nblk_valid, nblk_cap, tid, vpre);
+    issue_k<D>(a, bkv, kt + 3, n_tiles, L, k_base + RP * T::K_BYTES, w, lane, tl);
+    issue_v<D>(a, bkv, kt + 2, n_tiles, nblk_valid, nblk_cap,
+               v_base + ((RP + 2) % 3) * T::V_BYTES, w, lane);
 
     // scores of the next tile go to the matrix core first
-    if (more_v && n0 + kBN < wave_end)
-      qk_step<D>(lds_k + (1 - P) * T::LDS_K, qa, qsw, n, h, n0r, n1r);
+    if (kt + 1 < n_tiles && n0 + kBN < wave_end)
+      qk_step<D>(lds_k + ((RP + 1) % 3) * T::K_BYTES, koff, qa, qsw, n, h, n0r, n1r);
     __builtin_amdgcn_sched_barrier(0);
 
     if (n0 < wave_end) {  // uniform per wave
@@ -506,32 +540,42 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
       }
 
       // ---- [acc | l] += P_hat [V | 1]
-      const uint8_t* vbuf = lds_v + P * T::LDS_V;
+      const uint8_t* vbuf = lds_v + RP * T::V_BYTES;
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         const int ch = 32 * cc + n;
         const uint4 va = *reinterpret_cast<const uint4*>(vbuf + (h * D + ch) * 16);
-        const int vs = vbuf[T::VC * 16 + h * D + ch];
+        const int vs = vbuf[T::VS_OFF + h * D + ch];
         acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
       }
       accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
     }
-    if (more_k) store_k<D>(lds_k + P * T::LDS_K, tid, kpre);
-    if (more_v) store_v<D>(lds_v + (1 - P) * T::LDS_V, tid, vpre);
-    // Every load of this step has been consumed by now; saying so on all
-    // paths keeps the compiler from assuming a load skipped by a branch is
-    // still in flight, which would make the next step's prefetch loads wait
-    // for one another.
-    __builtin_amdgcn_s_waitcnt(0);
+    // K tile kt+2 and V tile kt+1 (issued one step ago) have landed; this
+    // step's loads stay in flight.
+    HIFA4_WAIT_VMCNT(T::N_LOADS);
     __syncthreads();
   };
 
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
   v16f sa0, sa1, sb0, sb1;
-  if (0 < wave_end) qk_step<D>(lds_k, qa, qsw, n, h, sa0, sa1);
-  for (int kt = 0; kt < n_tiles; kt += 2) {
-    step(std::integral_constant<int, 0>{}, kt, sa0, sa1, sb0, sb1);
-    if (kt + 1 < n_tiles) step(std::integral_constant<int, 1>{}, kt + 1, sb0, sb1, sa0, sa1);
+  if (0 < wave_end) qk_step<D>(lds_k, koff, qa, qsw, n, h, sa0, sa1);
+  for (int kt = 0; kt < n_tiles; kt += 6) {
+    step(R0{}, kt, sa0, sa1, sb0, sb1);
+    if (kt + 1 >= n_tiles) break;
+    step(R1{}, kt + 1, sb0, sb1, sa0, sa1);
+    if (kt + 2 >= n_tiles) break;
+    step(R2{}, kt + 2, sa0, sa1, sb0, sb1);
+    if (kt + 3 >= n_tiles) break;
+    step(R0{}, kt + 3, sb0, sb1, sa0, sa1);
+    if (kt + 4 >= n_tiles) break;
+    step(R1{}, kt + 4, sa0, sa1, sb0, sb1);
+    if (kt + 5 >= n_tiles) break;
+    step(R2{}, kt + 5, sb0, sb1, sa0, sa1);
   }
+  // No load may still be writing this workgroup's LDS when it exits.
+  HIFA4_WAIT_VMCNT(0);
 
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
   const float lsum = __shfl(accl[0], n);

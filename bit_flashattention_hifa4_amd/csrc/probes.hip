@@ -1,7 +1,8 @@
 // probes.hip -- diagnostic kernels that pin down gfx950 instruction behaviour
 // the attention kernels rely on: the operand / scale / accumulator lane
 // layouts of the scaled-FP4 and bf16 MFMAs, the rounding of the packed FP4
-// convert, and the issue rates of v_exp_f32 and the FP4 MFMA.
+// convert, the lane placement of memory -> LDS buffer loads, and the issue
+// rates of v_exp_f32 and the FP4 MFMA.
 //
 // Built into its own library (libhifa4_probes.so); the tests call it to check
 // those facts against independent host-side expectations.  Every kernel reads
@@ -112,6 +113,41 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* out, int iters) {
   out[blockIdx.x * blockDim.x + l] = t;
 }
 
+
+// Memory -> LDS buffer loads (the LDS-destination form): one wave loads
+// `size`-byte elements, lane i from source byte offset size*i, with M0 = 64;
+// the LDS window is pre-filled with 0xEE and copied out afterwards, so the
+// host sees where each lane's bytes landed.  The window (1 KiB + 64) covers
+// every placement the sizes allow.
+template <int kSize>
+__global__ __launch_bounds__(64) void lds_dma_kernel(const uint8_t* src, uint8_t* out) {
+  __shared__ __attribute__((aligned(16))) uint8_t win[64 + 16 * 64];
+  const int l = threadIdx.x;
+  for (int i = l; i < (int)sizeof(win); i += 64) win[i] = 0xEE;
+  __syncthreads();
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const uint64_t p = reinterpret_cast<uint64_t>(src);
+  v4i d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  d[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFFu));
+  d[2] = 16 * 64;
+  d[3] = 0x00020000;
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>(win + 64));
+  const uint32_t off = (uint32_t)(kSize * l);
+  if constexpr (kSize == 1)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(d) : "memory");
+  else if constexpr (kSize == 2)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(d) : "memory");
+  else if constexpr (kSize == 4)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(d) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(d) : "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = l; i < (int)sizeof(win); i += 64) out[i] = win[i];
+}
+
 int status(hipError_t e) { return e == hipSuccess ? 0 : -(int)e; }
 
 }  // namespace
@@ -191,6 +227,18 @@ int probe_mfma_rate(float* out, int n_blocks, int iters, void* stream) {
   if (n_blocks <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_rate_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, out,
                      iters);
+  return status(hipGetLastError());
+}
+
+int probe_lds_dma(const uint8_t* src, uint8_t* out, int size, void* stream) {
+  auto s = (hipStream_t)stream;
+  switch (size) {
+    case 1: hipLaunchKernelGGL(lds_dma_kernel<1>, dim3(1), dim3(64), 0, s, src, out); break;
+    case 2: hipLaunchKernelGGL(lds_dma_kernel<2>, dim3(1), dim3(64), 0, s, src, out); break;
+    case 4: hipLaunchKernelGGL(lds_dma_kernel<4>, dim3(1), dim3(64), 0, s, src, out); break;
+    case 16: hipLaunchKernelGGL(lds_dma_kernel<16>, dim3(1), dim3(64), 0, s, src, out); break;
+    default: return -1;
+  }
   return status(hipGetLastError());
 }
 

@@ -58,6 +58,12 @@ HIFA4_PROBE_API int probe_half_swap(const float* x, float* out, int n_waves, voi
 HIFA4_PROBE_API int probe_exp2_rate(float* out, int n_blocks, int iters, void* stream);
 HIFA4_PROBE_API int probe_mfma_rate(float* out, int n_blocks, int iters, void* stream);
 
+/* One wave of memory -> LDS buffer loads of `size` bytes per lane (1, 2, 4 or
+ * 16), lane i reading src bytes [size*i, size*(i+1)) (src: 1024 bytes), with
+ * M0 = LDS window + 64.  out: the 1088-byte window afterwards (pre-filled
+ * with 0xEE), so the caller sees each lane's placement. */
+HIFA4_PROBE_API int probe_lds_dma(const uint8_t* src, uint8_t* out, int size, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,10 @@ result with a host computation of the hypothesised semantics:
     8 * (l // 32) .. + 7;
   * v_cvt_scalef32_pk_fp4_f32 rounds x / scale to nearest-even E2M1 with
     saturation, like the oracle's encoder, and writes the selected byte.
+  * a memory -> LDS buffer load of `size` bytes per lane writes lane i's
+    bytes at M0 + size * i for 4 and 16 bytes; the 1- and 2-byte forms write
+    a zero-extended dword at M0 + 4 * i (the prefill kernel stages K / V
+    tiles with the 16-, 4- and 2-byte forms).
 Also measures the v_exp_f32 and FP4 MFMA issue rates (printed, loosely bounded).
 Set HIFA4_PROBE_DUMP=<dir> to save raw operands / results for offline study.
 """
@@ -44,6 +48,7 @@ def lib():
     l.probe_half_swap.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_exp2_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    l.probe_lds_dma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return l
 
 
@@ -271,3 +276,24 @@ def test_issue_rates_report(lib):
     print("fp4 32x32x64 MFMA: %.3g TFLOP/s (%.1f%% of 10.066 PFLOP/s), %.1f cycles per MFMA per SIMD"
           % (flops / t / 1e12, flops / t / 10.066e15 * 100, t * 2.4e9 * 1024 / mfmas))
     assert per_cu_clk > 4 and flops / t > 1e15
+
+
+@pytest.mark.parametrize("size", [1, 2, 4, 16])
+def test_lds_dma_lane_placement(lib, size):
+    """4- and 16-byte forms: lane i's bytes land at M0 + size*i.  The 1- and
+    2-byte forms write a whole dword per lane, at M0 + 4*i, zero-extended."""
+    src = torch.tensor((np.arange(1024) * 7 + 3) % 251, dtype=torch.uint8, device="cuda")
+    out = torch.empty(64 + 16 * 64, dtype=torch.uint8, device="cuda")
+    assert lib.probe_lds_dma(src.data_ptr(), out.data_ptr(), size, _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    s = src.cpu().numpy()
+    _dump("lds_dma_%d" % size, src=s, window=got)
+    exp = np.full_like(got, 0xEE)
+    stride = max(size, 4)
+    for i in range(64):
+        slot = np.zeros(stride, np.uint8)
+        slot[:size] = s[size * i: size * (i + 1)]
+        exp[64 + stride * i: 64 + stride * (i + 1)] = slot
+    bad = np.nonzero(got != exp)[0]
+    assert bad.size == 0, "placement differs at window bytes %s" % bad[:16]
