@@ -60,9 +60,9 @@ __device__ __forceinline__ int perm_row(int t, int m) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One online-softmax step on the 32 scores a lane holds for its query
-// (already masked with -inf).  Updates m_run, rescales the accumulators and
-// returns the packed P operand plus its E8M0 byte.
+// Result of an online-softmax step on the 32 scores a lane holds for its
+// query: the packed P operand, its E8M0 byte and the accumulators' rescale
+// factor.
 struct SoftmaxStep {
   uint4 p_codes;
   int p_scale;
@@ -100,15 +100,22 @@ __device__ __forceinline__ float max_with_half_swap(float x) {
   return fmax_(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Softmax step on the lane's 32 scores held in the two QK accumulators (tile
-// t, register r <-> key 32h + 16t + r), in place: the scores are replaced by
-// P before packing, so no copies of the accumulators are made.  Masked
-// scores are -inf on entry.
+// Softmax on the lane's 32 scores held in the two QK accumulators (tile t,
+// register r <-> key 32h + 16t + r), in place: the scores are replaced by P
+// before packing, so no copies of the accumulators are made.  Masked scores
+// are -inf on entry.
 //
-// `pk` is the previous step's packed P: every byte of it is overwritten, it
-// only gives the partial-write converts a register to start from.
-__device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m_run, float c,
-                                                    float tau, uint4& pk) {
+// The two halves of a softmax step, so that the Q K^T MFMAs of the next tile
+// can be issued between them: softmax_max() finds the new running max and
+// the rescale factor, softmax_exp() turns the scores into P and packs it.
+struct SoftmaxMax {
+  float m_use;  // the frame P is taken in (0 while the row has seen no key)
+  float bmc;    // fl(block max of S * c)
+  float alpha;  // rescale factor of the accumulators
+};
+
+__device__ __forceinline__ SoftmaxMax softmax_max(const v16f& s0, const v16f& s1, float& m_run,
+                                                  float c, float tau) {
   float ma = s0[0], mb = s1[0];
 #pragma unroll
   for (int r = 1; r < 16; r++) {
@@ -116,19 +123,29 @@ __device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m
     mb = fmax_(mb, s1[r]);
   }
   const float bm = fmax_(ma, mb);
-  const float bmc = bm * c;  // contraction is off in this file: a rounded product
-  const float rmc = max_with_half_swap(bmc);
+  SoftmaxMax x;
+  x.bmc = bm * c;  // contraction is off in this file: a rounded product
+  const float rmc = max_with_half_swap(x.bmc);
   const float m_new = rmc > m_run + tau ? rmc : m_run;
-  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-  SoftmaxStep st;
-  st.alpha = fast_exp2(m_run - m_use);
+  x.m_use = m_new == -INFINITY ? 0.0f : m_new;
+  x.alpha = fast_exp2(m_run - x.m_use);
+  m_run = m_new;
+  return x;
+}
+
+// `pk` is the previous step's packed P: every byte of it is overwritten, it
+// only gives the partial-write converts a register to start from.
+__device__ __forceinline__ SoftmaxStep softmax_exp(v16f& s0, v16f& s1, const SoftmaxMax& x,
+                                                   float c, uint4& pk) {
 #pragma unroll
   for (int r = 0; r < 16; r++) {
-    s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -m_use));
-    s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -m_use));
+    s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -x.m_use));
+    s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -x.m_use));
   }
-  const float pmax = fast_exp2(bmc - m_use);
+  const float pmax = fast_exp2(x.bmc - x.m_use);
   const uint32_t sb = e8m0_from_amax(pmax);
+  SoftmaxStep st;
+  st.alpha = x.alpha;
   st.p_scale = (int)sb;
   const float scale = e8m0_to_float(sb);
   uint32_t w[4] = {pk.x, pk.y, pk.z, pk.w};
@@ -136,26 +153,40 @@ __device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m
   for (int q = 0; q < 4; q++) {
     const v16f& src = q < 2 ? s0 : s1;
     const int o = 8 * (q & 1);
-    uint32_t x = w[q];
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 0], src[o + 1], scale, 0);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 2], src[o + 3], scale, 1);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 4], src[o + 5], scale, 2);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, src[o + 6], src[o + 7], scale, 3);
-    w[q] = x;
+    uint32_t v = w[q];
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, src[o + 0], src[o + 1], scale, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, src[o + 2], src[o + 3], scale, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, src[o + 4], src[o + 5], scale, 2);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, src[o + 6], src[o + 7], scale, 3);
+    w[q] = v;
   }
   st.p_codes = make_uint4(w[0], w[1], w[2], w[3]);
   pk = st.p_codes;
-  m_run = m_new;
   return st;
 }
 
-// Mask keys >= lim (key of element (t, r) is kb + 16t + r) with -inf.
+// Whole step (decode): max phase then exp phase.
+__device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m_run, float c,
+                                                    float tau, uint4& pk) {
+  const SoftmaxMax x = softmax_max(s0, s1, m_run, c, tau);
+  return softmax_exp(s0, s1, x, c, pk);
+}
+
+// Mask keys >= lim (key of element (t, r) is kb + 16t + r) with -inf.  The
+// keep / drop decision is the sign of (lim - 1 - key), spread over the word
+// by an arithmetic shift and merged with a bitfield select: no compare
+// masks, which would each take a pair of scalar registers.
+__device__ __forceinline__ float keep_or_neg_inf(float x, int last_minus_key) {
+  const uint32_t drop = (uint32_t)(last_minus_key >> 31);  // all ones if key > last
+  return __uint_as_float((__float_as_uint(x) & ~drop) | (0xFF800000u & drop));
+}
+
 __device__ __forceinline__ void mask_scores(v16f& s0, v16f& s1, int kb, int lim) {
-  const int rem = lim - kb;  // elements r < rem stay
+  const int rem = lim - 1 - kb;  // element r is kept iff r <= rem
 #pragma unroll
   for (int r = 0; r < 16; r++) {
-    if (r >= rem) s0[r] = -INFINITY;
-    if (16 + r >= rem) s1[r] = -INFINITY;
+    s0[r] = keep_or_neg_inf(s0[r], rem - r);
+    s1[r] = keep_or_neg_inf(s1[r], rem - 16 - r);
   }
 }
 
@@ -281,21 +312,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(p));
 }
 
-// Memory -> LDS, 16 / 4 bytes per lane: lane i writes LDS bytes
-// [lds + size*i, lds + size*(i+1)) with the bytes at `off` of the buffer.
-// (Lane placement pinned by the LDS-load probe.)
-__device__ __forceinline__ void load_lds16(v4i desc, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(off), "s"(desc) : "memory");
+// Memory -> LDS, 16 / 4 / 2 bytes per lane, from buffer offset soff + off:
+// lane i writes LDS bytes [lds + size*i, lds + size*(i+1)); the 2-byte form
+// writes a zero-extended dword at lds + 4i.  The range check counts soff, so
+// one descriptor over a head's valid keys serves every tile.  (Placement and
+// range behaviour are pinned by the LDS-load probes.)
+// M0 = lds + LDS_IMM: the per-stage part of the LDS address is an immediate,
+// so a ring needs only one register per wave for each kind of load.
+template <int LDS_IMM>
+__device__ __forceinline__ void load_lds16(v4i desc, uint32_t off, int soff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(off), "s"(desc), "s"(soff), "n"(LDS_IMM) : "memory");
 }
-__device__ __forceinline__ void load_lds4(v4i desc, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(off), "s"(desc) : "memory");
+template <int LDS_IMM>
+__device__ __forceinline__ void load_lds4(v4i desc, uint32_t off, int soff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(off), "s"(desc), "s"(soff), "n"(LDS_IMM) : "memory");
 }
-// 2 bytes per lane, written zero-extended as a dword at lds + 4i.
-__device__ __forceinline__ void load_lds2(v4i desc, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(off), "s"(desc) : "memory");
+template <int LDS_IMM>
+__device__ __forceinline__ void load_lds2(v4i desc, uint32_t off, int soff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_ushort %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(off), "s"(desc), "s"(soff), "n"(LDS_IMM) : "memory");
 }
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -328,72 +365,120 @@ __device__ __forceinline__ TileLanes<D> tile_lanes(int w, int lane) {
   return tl;
 }
 
-// Issue the wave's loads of K tile `tile` into the K stage at `stage`.
+// Descriptors of one (batch, kv head): K codes / scales over the L valid
+// keys, V codes / scales over the valid 32-key blocks.
+struct HeadDescs {
+  v4i kc, ks, vc, vs;
+};
+
 template <int D>
-__device__ __forceinline__ void issue_k(const AttnArgs& a, int64_t bkv, int tile, int n_tiles,
-                                        int L, uint32_t stage, int w, int lane,
-                                        const TileLanes<D>& tl) {
+__device__ __forceinline__ HeadDescs head_descs(const AttnArgs& a, int64_t bkv, int L,
+                                                int nblk_valid, int nblk_cap) {
   using T = PrefillTile<D>;
-  const int n0 = tile * kBN;
-  const uint32_t rows = tile < n_tiles ? (uint32_t)(L - n0) : 0u;
-  const int64_t row0 = bkv * a.cap + n0;
-  const v4i kc = buffer_desc(a.k_codes + row0 * T::DB, rows * T::DB);
-  const v4i ks = buffer_desc(a.k_scales + row0 * T::DS, rows * T::DS);
-#pragma unroll
-  for (int i = 0; i < T::KC_I; i++)
-    if (64 * i + lane < T::KC_W) load_lds16(kc, tl.kc[i], stage + (w * T::KC_W + 64 * i) * 16);
+  HeadDescs hd;
+  const int64_t row0 = bkv * a.cap;
+  const int64_t blk0 = bkv * nblk_cap;
+  hd.kc = buffer_desc(a.k_codes + row0 * T::DB, (uint32_t)L * T::DB);
+  hd.ks = buffer_desc(a.k_scales + row0 * T::DS, (uint32_t)L * T::DS);
+  hd.vc = buffer_desc(a.v_codes + blk0 * D * 16, (uint32_t)nblk_valid * D * 16);
+  hd.vs = buffer_desc(a.v_scales + blk0 * D, (uint32_t)nblk_valid * D);
+  return hd;
+}
+
+// A tile past the last one the workgroup needs reads nothing: its offset is
+// put past every descriptor's range (the loads still count in vmcnt).
+constexpr int kPastEnd = 0x7FFFFFF0;
+
+// The wave's LDS destinations in stage 0 (other stages: + an immediate).
+struct WaveDst {
+  uint32_t kc, ks, vc, vs;
+};
+
+template <int D>
+__device__ __forceinline__ WaveDst wave_dst(uint32_t k_base, uint32_t v_base, int w) {
+  using T = PrefillTile<D>;
+  WaveDst d;
+  d.kc = k_base + w * T::KC_W * 16;
+  d.ks = k_base + T::KS_OFF + 16 * w * T::KSS;
+  d.vc = v_base + w * T::VC_W * 16;
+  d.vs = v_base + T::VS_OFF + w * T::VS_W * 4;
+  return d;
+}
+
+// Issue the wave's loads of K tile `tile` into K stage KST.
+template <int D, int KST>
+__device__ __forceinline__ void issue_k(const HeadDescs& hd, int tile, int n_tiles,
+                                        const WaveDst& wd, int lane, const TileLanes<D>& tl) {
+  using T = PrefillTile<D>;
+  constexpr int SB = KST * T::K_BYTES;
+  const bool live = tile < n_tiles;
+  const int soc = live ? tile * kBN * T::DB : kPastEnd;
+  const int sos = live ? tile * kBN * T::DS : kPastEnd;
+  if (T::KC_W >= 64 || lane < T::KC_W) load_lds16<SB>(hd.kc, tl.kc[0], soc, wd.kc);
+  if constexpr (T::KC_I > 1) load_lds16<SB + 1024>(hd.kc, tl.kc[1], soc, wd.kc);
+  static_assert(T::KC_I <= 2, "at most two K code loads per wave");
   if (lane < T::KS_W) {
-    const uint32_t dst = stage + T::KS_OFF + 16 * w * T::KSS;
     if constexpr (T::DS == 2)
-      load_lds2(ks, tl.ks, dst);  // one row's 2 bytes, zero-extended into its 4-byte slot
+      load_lds2<SB>(hd.ks, tl.ks, sos, wd.ks);  // one row's 2 bytes, zero-extended into its slot
     else
-      load_lds4(ks, tl.ks, dst);
+      load_lds4<SB>(hd.ks, tl.ks, sos, wd.ks);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void issue_v(const AttnArgs& a, int64_t bkv, int tile, int n_tiles,
-                                        int nblk_valid, int nblk_cap, uint32_t stage, int w,
-                                        int lane) {
+template <int D, int VST>
+__device__ __forceinline__ void issue_v(const HeadDescs& hd, int tile, int n_tiles,
+                                        const WaveDst& wd, int lane, uint32_t vlane,
+                                        uint32_t vslane) {
   using T = PrefillTile<D>;
-  const int b0 = 2 * tile;
-  const uint32_t blks = tile < n_tiles ? (uint32_t)(nblk_valid - b0) : 0u;
-  const int64_t blk0 = bkv * nblk_cap + b0;
-  const v4i vc = buffer_desc(a.v_codes + blk0 * D * 16, blks * D * 16);
-  const v4i vs = buffer_desc(a.v_scales + blk0 * D, blks * D);
-#pragma unroll
-  for (int i = 0; i < T::VC_I; i++) {
-    const int c = w * T::VC_W + 64 * i;
-    if (64 * i + lane < T::VC_W) load_lds16(vc, (uint32_t)(c + lane) * 16u, stage + c * 16);
-  }
-  const int sw = w * T::VS_W;
-  if (lane < T::VS_W) load_lds4(vs, (uint32_t)(sw + lane) * 4u, stage + T::VS_OFF + sw * 4);
+  constexpr int SB = VST * T::V_BYTES;
+  const bool live = tile < n_tiles;
+  const int soc = live ? tile * 2 * D * 16 : kPastEnd;
+  const int sos = live ? tile * 2 * D : kPastEnd;
+  // vlane = (w * VC_W + lane) * 16 and vslane = (w * VS_W + lane) * 4: the
+  // lane's code chunk and scale word in the wave's share (V keeps its layout)
+  if (T::VC_W >= 64 || lane < T::VC_W) load_lds16<SB>(hd.vc, vlane, soc, wd.vc);
+  if constexpr (T::VC_I > 1) load_lds16<SB + 1024>(hd.vc, vlane + 1024, soc, wd.vc);
+  static_assert(T::VC_I <= 2, "at most two V code loads per wave");
+  if (lane < T::VS_W) load_lds4<SB>(hd.vs, vslane, sos, wd.vs);
 }
 
-// S^T = K Q^T for the two 32-key tiles of a 64-key step held in one K stage.
-// koff[t][j]: the lane's byte offset of its 16-byte A operand chunk.
+// K operands of the two 32-key tiles of a 64-key step, read from one K stage:
+// koff[t][j] is the lane's byte offset of its 16-byte A chunk (row 32t + n,
+// chunk 2j + h, swizzled).
 template <int D>
-__device__ __forceinline__ void qk_step(const uint8_t* kbuf, const uint32_t (&koff)[2][D / 64],
-                                        const uint4 (&qa)[D / 64],
-                                        const int (&qsw)[(D / 64 + 1) / 2], int n, int h,
-                                        v16f& s0, v16f& s1) {
+struct KOps {
+  uint4 k[2][D / 64];
+  int ks[2][D / 64];
+};
+
+template <int D>
+__device__ __forceinline__ void qk_load(const uint8_t* kbuf, const uint32_t (&koff)[2][D / 64],
+                                        int n, int h, KOps<D>& o) {
   using T = PrefillTile<D>;
-  constexpr int NJ = D / 64;
   const uint8_t* ks = kbuf + T::KS_OFF;
+#pragma unroll
+  for (int j = 0; j < D / 64; j++) {
+    o.k[0][j] = *reinterpret_cast<const uint4*>(kbuf + koff[0][j]);
+    o.k[1][j] = *reinterpret_cast<const uint4*>(kbuf + koff[1][j]);
+    o.ks[0][j] = k_scale_word<T::DS>(ks + n * T::KSS, j, h);
+    o.ks[1][j] = k_scale_word<T::DS>(ks + (32 + n) * T::KSS, j, h);
+  }
+}
+
+// S^T = K Q^T for the two tiles.
+template <int D>
+__device__ __forceinline__ void qk_mfma(const KOps<D>& o, const uint4 (&qa)[D / 64],
+                                        const int (&qsw)[(D / 64 + 1) / 2], v16f& s0, v16f& s1) {
   s0 = v16f{};
   s1 = v16f{};
 #pragma unroll
-  for (int j = 0; j < NJ; j++) {
-    const uint4 k0 = *reinterpret_cast<const uint4*>(kbuf + koff[0][j]);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(kbuf + koff[1][j]);
-    const int ks0 = k_scale_word<T::DS>(ks + n * T::KSS, j, h);
-    const int ks1 = k_scale_word<T::DS>(ks + (32 + n) * T::KSS, j, h);
+  for (int j = 0; j < D / 64; j++) {
     if (j % 2 == 0) {
-      s0 = mfma_fp4_sel<0>(k0, qa[j], s0, ks0, qsw[j / 2]);
-      s1 = mfma_fp4_sel<0>(k1, qa[j], s1, ks1, qsw[j / 2]);
+      s0 = mfma_fp4_sel<0>(o.k[0][j], qa[j], s0, o.ks[0][j], qsw[j / 2]);
+      s1 = mfma_fp4_sel<0>(o.k[1][j], qa[j], s1, o.ks[1][j], qsw[j / 2]);
     } else {
-      s0 = mfma_fp4_sel<2>(k0, qa[j], s0, ks0, qsw[j / 2]);
-      s1 = mfma_fp4_sel<2>(k1, qa[j], s1, ks1, qsw[j / 2]);
+      s0 = mfma_fp4_sel<2>(o.k[0][j], qa[j], s0, o.ks[0][j], qsw[j / 2]);
+      s1 = mfma_fp4_sel<2>(o.k[1][j], qa[j], s1, o.ks[1][j], qsw[j / 2]);
     }
   }
 }
@@ -458,12 +543,15 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // the Q operand) costs little over waiting for K0, V0, K1, and it tells
   // the compiler that no load it knows of is still in flight in the loop.
   const TileLanes<D> tl = tile_lanes<D>(w, lane);
-  const uint32_t k_base = lds_addr(lds_k), v_base = lds_addr(lds_v);
-  issue_k<D>(a, bkv, 0, n_tiles, L, k_base, w, lane, tl);
-  issue_v<D>(a, bkv, 0, n_tiles, nblk_valid, nblk_cap, v_base, w, lane);
-  issue_k<D>(a, bkv, 1, n_tiles, L, k_base + T::K_BYTES, w, lane, tl);
-  issue_v<D>(a, bkv, 1, n_tiles, nblk_valid, nblk_cap, v_base + T::V_BYTES, w, lane);
-  issue_k<D>(a, bkv, 2, n_tiles, L, k_base + 2 * T::K_BYTES, w, lane, tl);
+  const HeadDescs hd = head_descs<D>(a, bkv, L, nblk_valid, nblk_cap);
+  const WaveDst wd = wave_dst<D>(lds_addr(lds_k), lds_addr(lds_v), w);
+  const uint32_t vlane = (uint32_t)(w * T::VC_W + lane) * 16u;
+  const uint32_t vslane = (uint32_t)(w * T::VS_W + lane) * 4u;
+  issue_k<D, 0>(hd, 0, n_tiles, wd, lane, tl);
+  issue_v<D, 0>(hd, 0, n_tiles, wd, lane, vlane, vslane);
+  issue_k<D, 1>(hd, 1, n_tiles, wd, lane, tl);
+  issue_v<D, 1>(hd, 1, n_tiles, wd, lane, vlane, vslane);
+  issue_k<D, 2>(hd, 2, n_tiles, wd, lane, tl);
   // Q operand (B of S^T = K Q^T): query q, K blocks of 32 along d; its scale
   // bytes packed so that MFMA j reads byte 2*(j%2) of word j/2 (raw words
   // here, shifted for the lane's half once the loads have landed).
@@ -517,21 +605,31 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // One pipeline step on tile kt.  RP = kt mod 3 (ring slot), a compile-time
   // constant, so every LDS address is a per-lane base plus an immediate.
   // Scores of tile kt are in (c0, c1); the next tile's go to (n0r, n1r).
+  // Order within the step: the LDS reads of the next tile's K operands go
+  // first; their latency is covered by the scalar work of issuing this
+  // step's loads and by the max phase of the softmax; then the Q K^T MFMAs,
+  // which run on the matrix core during the exponentials.
   auto step = [&](auto ring, int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
     constexpr int RP = decltype(ring)::value;
     const int n0 = kt * kBN;
-    issue_k<D>(a, bkv, kt + 3, n_tiles, L, k_base + RP * T::K_BYTES, w, lane, tl);
-    issue_v<D>(a, bkv, kt + 2, n_tiles, nblk_valid, nblk_cap,
-               v_base + ((RP + 2) % 3) * T::V_BYTES, w, lane);
+    const bool do_qk = kt + 1 < n_tiles && n0 + kBN < wave_end;  // uniform per wave
+    const bool do_sm = n0 < wave_end;
+    KOps<D> ko;
+    if (do_qk) qk_load<D>(lds_k + ((RP + 1) % 3) * T::K_BYTES, koff, n, h, ko);
+    issue_k<D, RP>(hd, kt + 3, n_tiles, wd, lane, tl);
+    issue_v<D, (RP + 2) % 3>(hd, kt + 2, n_tiles, wd, lane, vlane, vslane);
 
-    // scores of the next tile go to the matrix core first
-    if (kt + 1 < n_tiles && n0 + kBN < wave_end)
-      qk_step<D>(lds_k + ((RP + 1) % 3) * T::K_BYTES, koff, qa, qsw, n, h, n0r, n1r);
+    SoftmaxMax sx;
+    if (do_sm) {
+      if (n0 + kBN > wave_full) mask_scores(c0, c1, n0 + 32 * h, row_lim);
+      sx = softmax_max(c0, c1, m_run, c, a.tau);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_qk) qk_mfma<D>(ko, qa, qsw, n0r, n1r);
     __builtin_amdgcn_sched_barrier(0);
 
-    if (n0 < wave_end) {  // uniform per wave
-      if (n0 + kBN > wave_full) mask_scores(c0, c1, n0 + 32 * h, row_lim);
-      const SoftmaxStep st = softmax_step(c0, c1, m_run, c, a.tau, pk);
+    if (do_sm) {
+      const SoftmaxStep st = softmax_exp(c0, c1, sx, c, pk);
       // rescale only when some row's max moved (multiplying by 1 is exact)
       if (__any(st.alpha != 1.0f)) {
 #pragma unroll
@@ -556,11 +654,15 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     __syncthreads();
   };
 
+  v16f sa0, sa1, sb0, sb1;
+  if (0 < wave_end) {
+    KOps<D> ko;
+    qk_load<D>(lds_k, koff, n, h, ko);
+    qk_mfma<D>(ko, qa, qsw, sa0, sa1);
+  }
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
   using R2 = std::integral_constant<int, 2>;
-  v16f sa0, sa1, sb0, sb1;
-  if (0 < wave_end) qk_step<D>(lds_k, koff, qa, qsw, n, h, sa0, sa1);
   for (int kt = 0; kt < n_tiles; kt += 6) {
     step(R0{}, kt, sa0, sa1, sb0, sb1);
     if (kt + 1 >= n_tiles) break;

@@ -148,6 +148,37 @@ __global__ __launch_bounds__(64) void lds_dma_kernel(const uint8_t* src, uint8_t
   for (int i = l; i < (int)sizeof(win); i += 64) out[i] = win[i];
 }
 
+
+// Raw buffer range check: one wave loads dword i from voffset 4i with the
+// given soffset and num_records (src must hold soffset + 256 bytes); lanes
+// whose load is out of range read 0.  The first 64 outputs come from a
+// register load, the next 64 from the memory -> LDS form.
+__global__ __launch_bounds__(64) void buffer_range_kernel(const uint32_t* src, uint32_t* out,
+                                                          int soffset, int num_records) {
+  __shared__ __attribute__((aligned(16))) uint32_t win[64];
+  const int l = threadIdx.x;
+  win[l] = 0xEEEEEEEEu;
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, num_records, 0x00020000);
+  out[l] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(4 * l), soffset, 0);
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const uint64_t p = reinterpret_cast<uint64_t>(src);
+  v4i d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  d[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFFu));
+  d[2] = __builtin_amdgcn_readfirstlane(num_records);
+  d[3] = 0x00020000;
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>(win));
+  const int so = __builtin_amdgcn_readfirstlane(soffset);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               ::"s"(m0), "v"((uint32_t)(4 * l)), "s"(d), "s"(so) : "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  out[64 + l] = win[l];
+}
+
 int status(hipError_t e) { return e == hipSuccess ? 0 : -(int)e; }
 
 }  // namespace
@@ -239,6 +270,14 @@ int probe_lds_dma(const uint8_t* src, uint8_t* out, int size, void* stream) {
     case 16: hipLaunchKernelGGL(lds_dma_kernel<16>, dim3(1), dim3(64), 0, s, src, out); break;
     default: return -1;
   }
+  return status(hipGetLastError());
+}
+
+int probe_buffer_range(const uint32_t* src, uint32_t* out, int soffset, int num_records,
+                       void* stream) {
+  if (soffset < 0 || (soffset & 3) || num_records < 0) return -1;
+  hipLaunchKernelGGL(buffer_range_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, src, out,
+                     soffset, num_records);
   return status(hipGetLastError());
 }
 

@@ -64,6 +64,13 @@ HIFA4_PROBE_API int probe_mfma_rate(float* out, int n_blocks, int iters, void* s
  * with 0xEE), so the caller sees each lane's placement. */
 HIFA4_PROBE_API int probe_lds_dma(const uint8_t* src, uint8_t* out, int size, void* stream);
 
+/* Raw buffer range check with an SGPR offset: lane i loads the dword at
+ * voffset 4i, soffset `soffset`, from a descriptor over src with
+ * `num_records` bytes (src must hold soffset + 256 readable bytes).
+ * out[0..64): register loads, out[64..128): the memory -> LDS form. */
+HIFA4_PROBE_API int probe_buffer_range(const uint32_t* src, uint32_t* out, int soffset,
+                                       int num_records, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,8 @@ def lib():
     l.probe_exp2_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_lds_dma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    l.probe_buffer_range.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
     return l
 
 
@@ -297,3 +299,25 @@ def test_lds_dma_lane_placement(lib, size):
         exp[64 + stride * i: 64 + stride * (i + 1)] = slot
     bad = np.nonzero(got != exp)[0]
     assert bad.size == 0, "placement differs at window bytes %s" % bad[:16]
+
+
+@pytest.mark.parametrize("soffset,num_records", [(0, 128), (64, 128), (64, 1024), (256, 300)])
+def test_buffer_range_check_with_sgpr_offset(lib, soffset, num_records):
+    """The raw-buffer range check counts the SGPR offset: lane i is in range
+    iff soffset + 4i + 4 <= num_records (register and memory -> LDS forms).
+    The prefill kernel relies on it: one descriptor per (batch, kv head) over
+    the valid keys, the tile offset in soffset."""
+    src = torch.arange(1, 1 + 512, dtype=torch.int32, device="cuda")
+    out = torch.zeros(128, dtype=torch.int32, device="cuda")
+    assert lib.probe_buffer_range(src.data_ptr(), out.data_ptr(), soffset, num_records,
+                                  _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64)
+    lanes = np.arange(64)
+    data = soffset // 4 + lanes + 1
+    with_so = np.where(4 * lanes + soffset + 4 <= num_records, data, 0)
+    without_so = np.where(4 * lanes + 4 <= num_records, data, 0)
+    for name, part in (("register", got[:64]), ("lds", got[64:])):
+        print("%s soffset=%d num_records=%d: counts soffset %s, ignores it %s" % (
+            name, soffset, num_records, (part == with_so).all(), (part == without_so).all()))
+        assert (part == with_so).all()
