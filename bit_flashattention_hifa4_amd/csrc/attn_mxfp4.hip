@@ -285,6 +285,7 @@ struct PrefillTile {
   static constexpr int KC_I = (KC_W + 63) / 64;  // load instructions for them
   static constexpr int VC_I = (VC_W + 63) / 64;
   static constexpr int N_LOADS = KC_I + VC_I + 2;  // per wave and step
+  static constexpr int STAGES = 4;                 // ring depth (K and V)
   static_assert(N_LOADS < 16, "vmcnt encoding below assumes fewer than 16");
 };
 
@@ -483,6 +484,25 @@ __device__ __forceinline__ void qk_mfma(const KOps<D>& o, const uint4 (&qa)[D / 
   }
 }
 
+// V operands of one tile for the P V MFMAs: lane (n, h) takes channel
+// 32cc + n of key block h (16 code bytes) and its scale byte.
+template <int D>
+struct VOps {
+  uint4 va[D / 32];
+  int vs[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void v_load(const uint8_t* vbuf, int n, int h, VOps<D>& o) {
+  using T = PrefillTile<D>;
+#pragma unroll
+  for (int cc = 0; cc < D / 32; cc++) {
+    const int ch = 32 * cc + n;
+    o.va[cc] = *reinterpret_cast<const uint4*>(vbuf + (h * D + ch) * 16);
+    o.vs[cc] = vbuf[T::VS_OFF + h * D + ch];
+  }
+}
+
 template <int D>
 constexpr int prefill_min_blocks() { return D >= 256 ? 1 : 2; }  // also used by decode
 
@@ -493,8 +513,8 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   constexpr int DB = T::DB, DS = T::DS;
   constexpr int NJ = D / 64;  // QK MFMAs per 32-key tile
   constexpr int NC = D / 32;  // P V channel tiles
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[3 * T::K_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[3 * T::V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[T::STAGES * T::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[T::STAGES * T::V_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -552,6 +572,10 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   issue_k<D, 1>(hd, 1, n_tiles, wd, lane, tl);
   issue_v<D, 1>(hd, 1, n_tiles, wd, lane, vlane, vslane);
   issue_k<D, 2>(hd, 2, n_tiles, wd, lane, tl);
+  // The first step's deferred P V (of "tile -1", P = 0) reads V stage 3:
+  // give it finite scales.
+  for (int i = tid; i < 2 * D; i += 256) lds_v[3 * T::V_BYTES + T::VS_OFF + i] = 0;
+
   // Q operand (B of S^T = K Q^T): query q, K blocks of 32 along d; its scale
   // bytes packed so that MFMA j reads byte 2*(j%2) of word j/2 (raw words
   // here, shifted for the lane's half once the loads have landed).
@@ -601,55 +625,69 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
   v16f accl = v16f{};
+  // P_hat of the previous tile, whose P V MFMAs run during this step
+  uint4 pend_p = make_uint4(0, 0, 0, 0);
+  int pend_s = 127;
 
-  // One pipeline step on tile kt.  RP = kt mod 3 (ring slot), a compile-time
-  // constant, so every LDS address is a per-lane base plus an immediate.
+  // [acc | l] += P_hat [V | 1] for one tile.
+  auto pv_mfma = [&](const VOps<D>& vo, const uint4& p, int ps) {
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) acc[cc] = mfma_fp4_32x32x64(vo.va[cc], p, acc[cc], vo.vs[cc], ps);
+    accl = mfma_fp4_32x32x64(ones, p, accl, ones_scale, ps);
+  };
+
+  // One pipeline step on tile kt, RP = kt mod 4 (ring slot, a compile-time
+  // constant: every LDS address is a per-lane base plus an immediate).
   // Scores of tile kt are in (c0, c1); the next tile's go to (n0r, n1r).
-  // Order within the step: the LDS reads of the next tile's K operands go
-  // first; their latency is covered by the scalar work of issuing this
-  // step's loads and by the max phase of the softmax; then the Q K^T MFMAs,
-  // which run on the matrix core during the exponentials.
+  //   1. LDS reads: K operands of tile kt+1, V operands of tile kt-1;
+  //   2. loads of K tile kt+3 and V tile kt+2 into the ring;
+  //   3. max phase of tile kt (running max, rescale factor);
+  //   4. one block with the Q K^T MFMAs of tile kt+1, the P V MFMAs of tile
+  //      kt-1 (its P_hat was packed last step) and the exponentials and
+  //      packing of tile kt, interleaved so the matrix core works while
+  //      the vector ALU does;
+  //   5. rescale of the accumulators (after tile kt-1's P V: frames match);
+  //   6. wait for the loads issued last step, barrier.
+  // The core block has no branches: a wave whose rows see no key of tile kt
+  // masks all its scores (P = 0, the running max stays), and the products
+  // of a tile that does not exist read finite stale LDS and are discarded.
   auto step = [&](auto ring, int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
     constexpr int RP = decltype(ring)::value;
+    constexpr int NS = T::STAGES;
     const int n0 = kt * kBN;
-    const bool do_qk = kt + 1 < n_tiles && n0 + kBN < wave_end;  // uniform per wave
-    const bool do_sm = n0 < wave_end;
+    const bool do_sm = n0 < wave_end;  // uniform per wave
     KOps<D> ko;
-    if (do_qk) qk_load<D>(lds_k + ((RP + 1) % 3) * T::K_BYTES, koff, n, h, ko);
-    issue_k<D, RP>(hd, kt + 3, n_tiles, wd, lane, tl);
-    issue_v<D, (RP + 2) % 3>(hd, kt + 2, n_tiles, wd, lane, vlane, vslane);
+    qk_load<D>(lds_k + ((RP + 1) % NS) * T::K_BYTES, koff, n, h, ko);
+    VOps<D> vo;
+    v_load<D>(lds_v + ((RP + NS - 1) % NS) * T::V_BYTES, n, h, vo);
+    issue_k<D, (RP + 3) % NS>(hd, kt + 3, n_tiles, wd, lane, tl);
+    issue_v<D, (RP + 2) % NS>(hd, kt + 2, n_tiles, wd, lane, vlane, vslane);
 
-    SoftmaxMax sx;
-    if (do_sm) {
-      if (n0 + kBN > wave_full) mask_scores(c0, c1, n0 + 32 * h, row_lim);
-      sx = softmax_max(c0, c1, m_run, c, a.tau);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (do_qk) qk_mfma<D>(ko, qa, qsw, n0r, n1r);
+    if (!do_sm || n0 + kBN > wave_full)
+      mask_scores(c0, c1, n0 + 32 * h, do_sm ? row_lim : 0);
+    const SoftmaxMax sx = softmax_max(c0, c1, m_run, c, a.tau);
     __builtin_amdgcn_sched_barrier(0);
 
-    if (do_sm) {
-      const SoftmaxStep st = softmax_exp(c0, c1, sx, c, pk);
-      // rescale only when some row's max moved (multiplying by 1 is exact)
-      if (__any(st.alpha != 1.0f)) {
+    qk_mfma<D>(ko, qa, qsw, n0r, n1r);
+    pv_mfma(vo, pend_p, pend_s);
+    const SoftmaxStep st = softmax_exp(c0, c1, sx, c, pk);
 #pragma unroll
-        for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
-        accl[0] *= st.alpha;
-      }
-
-      // ---- [acc | l] += P_hat [V | 1]
-      const uint8_t* vbuf = lds_v + RP * T::V_BYTES;
-#pragma unroll
-      for (int cc = 0; cc < NC; cc++) {
-        const int ch = 32 * cc + n;
-        const uint4 va = *reinterpret_cast<const uint4*>(vbuf + (h * D + ch) * 16);
-        const int vs = vbuf[T::VS_OFF + h * D + ch];
-        acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
-      }
-      accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
+    for (int i = 0; i < NJ * 2 + NC + 1; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then eight VALU
     }
-    // K tile kt+2 and V tile kt+1 (issued one step ago) have landed; this
-    // step's loads stay in flight.
+    __builtin_amdgcn_sched_barrier(0);
+
+    // rescale only when some row's max moved (multiplying by 1 is exact)
+    if (__any(st.alpha != 1.0f)) {
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
+      accl[0] *= st.alpha;
+    }
+    pend_p = st.p_codes;
+    pend_s = st.p_scale;
+    // K tile kt+2 and V tile kt (issued one and two steps ago) have landed;
+    // this step's loads stay in flight.
     HIFA4_WAIT_VMCNT(T::N_LOADS);
     __syncthreads();
   };
@@ -663,18 +701,21 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
   using R2 = std::integral_constant<int, 2>;
-  for (int kt = 0; kt < n_tiles; kt += 6) {
+  using R3 = std::integral_constant<int, 3>;
+  for (int kt = 0; kt < n_tiles; kt += 4) {
     step(R0{}, kt, sa0, sa1, sb0, sb1);
     if (kt + 1 >= n_tiles) break;
     step(R1{}, kt + 1, sb0, sb1, sa0, sa1);
     if (kt + 2 >= n_tiles) break;
     step(R2{}, kt + 2, sa0, sa1, sb0, sb1);
     if (kt + 3 >= n_tiles) break;
-    step(R0{}, kt + 3, sb0, sb1, sa0, sa1);
-    if (kt + 4 >= n_tiles) break;
-    step(R1{}, kt + 4, sa0, sa1, sb0, sb1);
-    if (kt + 5 >= n_tiles) break;
-    step(R2{}, kt + 5, sb0, sb1, sa0, sa1);
+    step(R3{}, kt + 3, sb0, sb1, sa0, sa1);
+  }
+  // the last tile's P V
+  if (n_tiles > 0) {
+    VOps<D> vo;
+    v_load<D>(lds_v + ((n_tiles - 1) % T::STAGES) * T::V_BYTES, n, h, vo);
+    pv_mfma(vo, pend_p, pend_s);
   }
   // No load may still be writing this workgroup's LDS when it exits.
   HIFA4_WAIT_VMCNT(0);
