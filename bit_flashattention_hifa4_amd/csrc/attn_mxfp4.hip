@@ -665,18 +665,27 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
 
     if (!do_sm || n0 + kBN > wave_full)
       mask_scores(c0, c1, n0 + 32 * h, do_sm ? row_lim : 0);
-    const SoftmaxMax sx = softmax_max(c0, c1, m_run, c, a.tau);
+    SoftmaxMax sx = softmax_max(c0, c1, m_run, c, a.tau);
+    // Order anchors (empty asm, no instructions): the products below may
+    // not be hoisted above the max phase, and the rescale test may not be
+    // hoisted above the exponentials; otherwise the MFMAs end up clustered
+    // instead of interleaved with the vector work.
+    asm volatile("" : "+v"(qa[0].x), "+v"(pend_p.x) : "v"(sx.m_use));
     __builtin_amdgcn_sched_barrier(0);
 
     qk_mfma<D>(ko, qa, qsw, n0r, n1r);
     pv_mfma(vo, pend_p, pend_s);
-    const SoftmaxStep st = softmax_exp(c0, c1, sx, c, pk);
+    SoftmaxStep st = softmax_exp(c0, c1, sx, c, pk);
 #pragma unroll
     for (int i = 0; i < NJ * 2 + NC + 1; i++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then eight VALU
     }
     __builtin_amdgcn_sched_barrier(0);
+    // ... and the Q K^T products may not sink past this step's barrier into
+    // the next step, where the max phase would wait for them.
+    asm volatile("" : "+v"(st.alpha), "+v"(n0r[0]), "+v"(n1r[0])
+                 : "v"(st.p_codes.x), "v"(st.p_codes.y), "v"(st.p_codes.z), "v"(st.p_codes.w));
 
     // rescale only when some row's max moved (multiplying by 1 is exact)
     if (__any(st.alpha != 1.0f)) {
