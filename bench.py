@@ -16,8 +16,10 @@ GB/s, the split-K decode on 64 sequences with 1k-32k MXFP4 cache entries (HBM
 GB/s, split + merge), and the bf16 FlashAttention baseline on the same prefill
 (time ratio = the measured counterpart of the pages' projected latency cut).
 
-`roofline` is for the dominant kernel (the fused prefill attention), timed
-with HIP events on the stream it is launched on; `traffic` comes from the
+Every timed region follows at least 200 ms of untimed launches of the same
+work (the GPU's clocks ramp up under sustained load), then the W warm-up
+steps.  `roofline` is for the dominant kernel (the fused prefill attention),
+timed with HIP events on the stream it is launched on; `traffic` comes from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/ when that summary was
 taken on the current kernel source, else null.  `cpu_baseline` times the CPU
 oracle (test infrastructure) on a bounded sample of the same workload.
@@ -61,6 +63,29 @@ def read_traffic():
     if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha():
         return None
     return float(m_b.group(1))
+
+
+def settle(fn, torch, min_ms=200.0):
+    """Run fn untimed until the GPU has been busy for min_ms.  MI355X raises its
+    clocks over the first few tens of ms of sustained load (measured: a launch
+    takes ~15% longer in the first 10 ms than after 35 ms), so a short warm-up
+    alone would time the ramp instead of the sustained rate."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
+def copy_calibration(torch, dev, nbytes=256 << 20, reps=3):
+    """A plain device copy of known size (nbytes read, nbytes written), for scaling the
+    profiler's FETCH_SIZE / WRITE_SIZE counters; run only with --copy-calibration."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: %d x %d bytes" % (reps, nbytes))
 
 
 def time_events(fn, n, torch):
@@ -111,6 +136,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (for profiler byte-counter scaling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -147,7 +174,12 @@ def main():
     def attend():
         hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse, rescale_threshold=tau)
 
+    def step():
+        quantise()
+        attend()
+
     # ---- headline: K timed steps of (quantise + attention)
+    settle(step, torch)
     for _ in range(args.warmup):
         quantise()
         attend()
@@ -190,8 +222,7 @@ def main():
         blse = torch.empty_like(lse)
         f = lambda: hb.bf16_attn_fwd(q, k, v, causal=cfg.causal, out=bout, lse=blse,
                                      rescale_threshold=tau)
-        for _ in range(3):
-            f()
+        settle(f, torch)
         b_ms = np.array(time_events(f, max(5, args.steps // 2), torch))
         extra["bf16_attention_ms_avg"] = float(b_ms.mean())
         extra["bf16_attention_tflops"] = flops / (b_ms.mean() * 1e-3) / 1e12
@@ -204,6 +235,9 @@ def main():
     # ---- split-K decode against the long MXFP4 cache
     if not args.no_decode:
         extra.update(decode_leg(W, hb, torch, np, dev, args))
+
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
 
     cpu = None
     if not args.no_cpu:
@@ -256,9 +290,7 @@ def decode_leg(W, hb, torch, np, dev, args):
     ws = torch.empty(hb.hifa4_attn_workspace_size(p), dtype=torch.uint8, device=dev)
     f = lambda: hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, out=out, lse=lse, workspace=ws,
                                   rescale_threshold=hb.RESCALE_THRESHOLD_FAST)
-    for _ in range(5):
-        f()
-    torch.cuda.synchronize()
+    settle(f, torch)
     d_ms = np.array(time_events(f, max(10, args.steps), torch))
     # algorithmic bytes: valid-token K (codes + scales), V blocks covering the valid
     # tokens, bf16 Q and O
