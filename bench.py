@@ -11,8 +11,12 @@ the whole hot path over that batch: Smooth-QK + MXFP4 quantisation of Q, K, V
 HBM.  `value` = algorithmic attention flops (4 d per unmasked query-key pair)
 per second of step time.
 
-Also reported (in "extra"): the attention kernel alone, the quantise kernel's
-GB/s, the split-K decode on 64 sequences with 1k-32k MXFP4 cache entries (HBM
+The attention runs with the lazy-rescale threshold 8 (log2 units; the running
+max moves only when a tile's max exceeds it by more than that, and P_hat is
+defined in that frame; the CPU oracle takes the same value).
+
+Also reported (in "extra"): the attention kernel alone, the same kernel with
+threshold 0 (the FlashAttention-2 frame), the quantise kernel's GB/s, the split-K decode on 64 sequences with 1k-32k MXFP4 cache entries (HBM
 GB/s, split + merge), and the bf16 FlashAttention baseline on the same prefill
 (time ratio = the measured counterpart of the pages' projected latency cut).
 
@@ -215,6 +219,15 @@ def main():
         "flops_per_step": flops,
         "kernel_source_sha256_16": kernel_source_sha(),
     }
+
+    # ---- the same attention in the FlashAttention-2 frame (rescale threshold 0)
+    f0 = lambda: hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse, rescale_threshold=0.0)
+    settle(f0, torch)
+    z_ms = np.array(time_events(f0, max(5, args.steps // 2), torch))
+    extra["attention_tau0_ms_avg"] = float(z_ms.mean())
+    extra["attention_tau0_tflops"] = flops / (z_ms.mean() * 1e-3) / 1e12
+    log("attention with rescale threshold 0: %.3f ms (%.1f TFLOP/s)"
+        % (z_ms.mean(), extra["attention_tau0_tflops"]))
 
     # ---- bf16 FlashAttention baseline on the same inputs
     if not args.no_bf16:
