@@ -99,8 +99,9 @@ hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
 
 size_t decode_workspace(const hifa4_attn_params* p, int cap, int chunk) {
   if (p->Sq != 1 || chunk <= 0) return 0;
-  const int64_t n_chunks = (cap + chunk - 1) / chunk;
-  return (size_t)p->B * p->Hq * n_chunks * (p->d + 2) * sizeof(float);
+  const int64_t per = (int64_t)chunk * hifa4::attn_decode_chunks_per_part();
+  const int64_t n_parts = (cap + per - 1) / per;
+  return (size_t)p->B * p->Hq * n_parts * (p->d + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -284,7 +285,10 @@ hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4
   a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)d);
   a.sm_log2 = a.sm_scale * 1.4426950408889634f;
   a.chunk = chunk;
-  a.n_chunks = chunk ? (cap + chunk - 1) / chunk : 0;
+  {
+    const int64_t per = (int64_t)chunk * hifa4::attn_decode_chunks_per_part();
+    a.n_parts = chunk ? (int)((cap + per - 1) / per) : 0;
+  }
   a.tau = p->rescale_threshold;
   hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
                             : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);

@@ -318,22 +318,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // writes a zero-extended dword at lds + 4i.  The range check counts soff, so
 // one descriptor over a head's valid keys serves every tile.  (Placement and
 // range behaviour are pinned by the LDS-load probes.)
-// M0 = lds + LDS_IMM: the per-stage part of the LDS address is an immediate,
-// so a ring needs only one register per wave for each kind of load.
+// M0 = lds + LDS_IMM (the per-stage part of the address as a constant).
+// The asm sets M0 with s_mov, which leaves SCC alone: the compiler does not
+// model an SCC clobber and may keep a pending s_cselect condition in SCC
+// across the statement.  M0 holds nothing else in these kernels.
 template <int LDS_IMM>
 __device__ __forceinline__ void load_lds16(v4i desc, uint32_t off, int soff, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(off), "s"(desc), "s"(soff), "n"(LDS_IMM) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds + LDS_IMM), "v"(off), "s"(desc), "s"(soff) : "memory");
 }
 template <int LDS_IMM>
 __device__ __forceinline__ void load_lds4(v4i desc, uint32_t off, int soff, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(off), "s"(desc), "s"(soff), "n"(LDS_IMM) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds + LDS_IMM), "v"(off), "s"(desc), "s"(soff) : "memory");
 }
 template <int LDS_IMM>
 __device__ __forceinline__ void load_lds2(v4i desc, uint32_t off, int soff, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %0, %4\n\tbuffer_load_ushort %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(off), "s"(desc), "s"(soff), "n"(LDS_IMM) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds"
+               :: "s"(lds + LDS_IMM), "v"(off), "s"(desc), "s"(soff) : "memory");
 }
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -740,71 +742,109 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
 }
 
 // ---------------------------------------------------------------------------
-// Decode (Sq == 1), split-K: one wave = one chunk of `a.chunk` keys of one
-// (batch, kv head) against the G query heads of that group (the MFMA's 32
-// query columns, G used).  Each wave starts from a fresh state and writes its
-// partial (m, l, acc[d]) to the workspace; the merge kernel combines them.
-// K / V operands are loaded straight from global memory (each byte is read
-// once), one 64-key tile ahead of the one being computed, so a wave always
-// has a tile of HBM reads in flight behind its MFMA / softmax work.  Rows
-// and blocks past the valid keys are clamped to the last valid one (finite
-// data, masked scores, zero P).
+// Decode (Sq == 1), split-K.  A workgroup takes kWaves consecutive chunks of
+// `a.chunk` keys of one (batch, kv head); each wave runs one chunk from a
+// fresh online-softmax state against the G query heads of the group (the
+// MFMA's 32 query columns, G used), and the waves' results are combined in
+// LDS with the log-sum-exp rule into one partial (m, l, acc[d]) per query
+// head and workgroup; the merge kernel combines the workgroups.
+//
+// Decode reads every K / V byte once, so it is bound by how many bytes are
+// in flight.  Each wave streams its chunk through a private two-stage LDS
+// ring with memory -> LDS buffer loads (no registers held by loads in
+// flight): while tile t is computed from registers, tiles t+1 and t+2 are
+// loading.  The loads of tile t+2 go into tile t's stage as soon as its
+// operands are in registers.  The K layout in a stage is the prefill one
+// (rows in MFMA read order, swizzled chunks), so the operand reads are
+// shared with prefill.  Keys past the chunk read real data or zeros (past
+// the sequence: descriptor range) and are masked.
 // ---------------------------------------------------------------------------
 template <int D>
-struct DecTile {
-  uint4 k0[D / 64], k1[D / 64];
-  uint32_t ks0[(D / 64 + 1) / 2], ks1[(D / 64 + 1) / 2];  // raw scale words (shifted at use)
-  uint4 va[D / 32];
-  int vs[D / 32];
+struct DecStage {
+  using T = PrefillTile<D>;
+  static constexpr int BYTES = T::K_BYTES + T::V_BYTES;  // K then V of one 64-key tile
+  static constexpr int KC_I = kBN * T::DB / 1024;        // 1 KB K code loads per tile
+  static constexpr int VC_I = 2 * D * 16 / 1024;         // 1 KB V code loads per tile
+  static constexpr int KS_I = T::DS == 8 ? 2 : 1;        // K scale loads (2 or 4 bytes a lane)
+  static constexpr int VS_I = D == 256 ? 2 : 1;          // V scale loads (4 bytes a lane)
+  static constexpr int N_LOADS = KC_I + VC_I + KS_I + VS_I;
+  static_assert(2 * N_LOADS < 64, "vmcnt counts up to 63");
 };
 
-// Raw 32-bit word holding the scale byte of K block 2j + h of a row.
-template <int DS>
-__device__ __forceinline__ uint32_t k_scale_raw(const uint8_t* p, int j) {
-  if constexpr (DS == 2) {
-    return *reinterpret_cast<const uint16_t*>(p);
-  } else {
-    return reinterpret_cast<const uint32_t*>(p)[j >> 1];
+// s_waitcnt immediate for vmcnt(n), other counters untouched (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14]).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+// lgkmcnt(0) alone.
+constexpr int kLgkm0 = 0xC07F;
+
+// Per-lane source offsets of a whole tile's loads (loop invariant).
+template <int D>
+struct DecLanes {
+  uint32_t kc[DecStage<D>::KC_I];
+  uint32_t ks[DecStage<D>::KS_I];
+};
+
+template <int D>
+__device__ __forceinline__ DecLanes<D> dec_lanes(int lane) {
+  using T = PrefillTile<D>;
+  DecLanes<D> dl;
+#pragma unroll
+  for (int i = 0; i < DecStage<D>::KC_I; i++) {
+    const int b = 64 * i + lane;  // chunk index in LDS order
+    const int R = b / T::NCH, pos = b % T::NCH;
+    dl.kc[i] = (uint32_t)(perm_row(R >> 5, R & 31) * T::DB + ((pos ^ k_swz<D>(R)) * 16));
   }
+#pragma unroll
+  for (int i = 0; i < DecStage<D>::KS_I; i++) {
+    // one row per lane (two lanes per row for 8-byte rows)
+    const int R = T::DS == 8 ? 32 * i + (lane >> 1) : lane;
+    dl.ks[i] = (uint32_t)(perm_row(R >> 5, R & 31) * T::DS + (T::DS == 8 ? 4 * (lane & 1) : 0));
+  }
+  return dl;
 }
 
-// Loads of the 64-key tile at n0.  Keys past last_key (and V blocks past
-// last_blk) are clamped to it, so the load count is the same for every tile,
-// including the prefetch past the end of the chunk (a re-read of rows just
-// loaded).  A fixed count lets each step wait for exactly the tile it uses.
+// Issue the loads of the 64-key tile starting at key n0 (live) into the
+// stage at LDS address `st`; a dead tile reads nothing but still issues.
 template <int D>
-__device__ __forceinline__ void dec_load(const AttnArgs& a, int64_t bkv, int n0, int last_key,
-                                         int last_blk, int nblk_cap, int r0, int r1, int n,
-                                         int h, DecTile<D>& t) {
-  constexpr int DB = D / 2, DS = D / 32, NJ = D / 64, NC = D / 32;
-  const int64_t k0row = bkv * a.cap + min(n0 + r0, last_key);
-  const int64_t k1row = bkv * a.cap + min(n0 + r1, last_key);
-  const uint8_t* kc0 = a.k_codes + k0row * DB + 16 * h;
-  const uint8_t* kc1 = a.k_codes + k1row * DB + 16 * h;
+__device__ __forceinline__ void dec_issue(const HeadDescs& hd, int n0, bool live, uint32_t st,
+                                          int lane, const DecLanes<D>& dl) {
+  using T = PrefillTile<D>;
+  using S = DecStage<D>;
+  const int soc = live ? n0 * T::DB : kPastEnd;
+  const int sos = live ? n0 * T::DS : kPastEnd;
+  const int svc = live ? (n0 / 32) * D * 16 : kPastEnd;
+  const int svs = live ? (n0 / 32) * D : kPastEnd;
 #pragma unroll
-  for (int j = 0; j < NJ; j++) {
-    t.k0[j] = *reinterpret_cast<const uint4*>(kc0 + 32 * j);
-    t.k1[j] = *reinterpret_cast<const uint4*>(kc1 + 32 * j);
+  for (int i = 0; i < S::KC_I; i++) load_lds16<0>(hd.kc, dl.kc[i], soc, st + 1024 * i);
+#pragma unroll
+  for (int i = 0; i < S::KS_I; i++) {
+    if constexpr (T::DS == 2)
+      load_lds2<0>(hd.ks, dl.ks[i], sos, st + T::KS_OFF);
+    else
+      load_lds4<0>(hd.ks, dl.ks[i], sos, st + T::KS_OFF + 256 * i);
   }
+  const uint32_t sv = st + T::K_BYTES;
 #pragma unroll
-  for (int j = 0; j < NJ; j += 2) {
-    t.ks0[j / 2] = k_scale_raw<DS>(a.k_scales + k0row * DS, j);
-    t.ks1[j / 2] = k_scale_raw<DS>(a.k_scales + k1row * DS, j);
-  }
-  const int64_t vb = bkv * nblk_cap + min(n0 / 32 + h, last_blk);
+  for (int i = 0; i < S::VC_I; i++)
+    load_lds16<0>(hd.vc, (uint32_t)(1024 * i + 16 * lane), svc, sv + 1024 * i);
 #pragma unroll
-  for (int cc = 0; cc < NC; cc++) {
-    t.va[cc] = *reinterpret_cast<const uint4*>(a.v_codes + (vb * D + 32 * cc + n) * 16);
-    t.vs[cc] = a.v_scales[vb * D + 32 * cc + n];
+  for (int i = 0; i < S::VS_I; i++) {
+    if (D == 64 && lane >= 32) break;  // 128 scale bytes
+    load_lds4<0>(hd.vs, (uint32_t)(256 * i + 4 * lane), svs, sv + T::VS_OFF + 256 * i);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_split_kernel(AttnArgs a,
                                                                                   int ones_scale) {
-  constexpr int DB = D / 2, DS = D / 32, NJ = D / 64, NC = D / 32;
+  using T = PrefillTile<D>;
+  using S = DecStage<D>;
+  constexpr int DB = T::DB, DS = T::DS, NJ = D / 64, NC = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * 2 * S::BYTES];
+
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
   const int G = a.Hq / a.Hkv;
   const int bkv_i = blockIdx.y;
@@ -812,15 +852,24 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_spli
   const int64_t bkv = (int64_t)b * a.Hkv + g;
   int L = a.Sk;
   if (a.kv_lens) L = min(max(a.kv_lens[b], 0), a.Sk);
-  const int chunk_idx = blockIdx.x * kWaves + wave;
-  const int s0 = chunk_idx * a.chunk;
-  if (s0 >= L) return;  // uniform per wave; no barriers below
+  const int part = blockIdx.x;
+  if (part * kWaves * a.chunk >= L) return;  // uniform per workgroup
+  const int s0 = (part * kWaves + w) * a.chunk;
   const int s1 = min(L, s0 + a.chunk);
+  const int n_tiles = s0 < L ? (s1 - s0 + kBN - 1) / kBN : 0;  // uniform per wave
   const int nblk_cap = (a.cap + 31) / 32;
+  const int nblk_valid = (L + 31) / 32;
+
+  const HeadDescs hd = head_descs<D>(a, bkv, L, nblk_valid, nblk_cap);
+  const DecLanes<D> dl = dec_lanes<D>(lane);
+  uint8_t* ring = lds + w * 2 * S::BYTES;
+  const uint32_t ring_addr = lds_addr(ring);
+  dec_issue<D>(hd, s0, 0 < n_tiles, ring_addr, lane, dl);
+  dec_issue<D>(hd, s0 + kBN, 1 < n_tiles, ring_addr + S::BYTES, lane, dl);
 
   // Q operand: column n is query head g*G + n (zero for n >= G).
   uint4 qa[NJ];
-  int qsw[(NJ + 1) / 2];
+  uint32_t qsw_raw[(NJ + 1) / 2];
   if (n < G) {
     const int64_t row = ((int64_t)b * a.Hq + g * G + n);  // Sq == 1
     const uint8_t* qc = a.q_codes + row * DB;
@@ -828,13 +877,33 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_spli
 #pragma unroll
     for (int j = 0; j < NJ; j++) qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
 #pragma unroll
-    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = k_scale_word<DS>(qsc, j, h);
+    for (int j = 0; j < NJ; j += 2) {
+      if constexpr (DS == 2)
+        qsw_raw[j / 2] = *reinterpret_cast<const uint16_t*>(qsc);
+      else
+        qsw_raw[j / 2] = reinterpret_cast<const uint32_t*>(qsc)[j >> 1];
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < NJ; j++) qa[j] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = 0;
+    for (int j = 0; j < NJ; j += 2) qsw_raw[j / 2] = 0;
   }
+  // Q and both prologue tiles: the compiler then knows no load of its own is
+  // in flight in the loop.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  int qsw[(NJ + 1) / 2];
+#pragma unroll
+  for (int j = 0; j < NJ; j += 2) qsw[j / 2] = (int)(qsw_raw[j / 2] >> (8 * h));
+
+  uint32_t koff[2][NJ];
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const int R = 32 * t + n;
+      koff[t][j] = (uint32_t)(R * DB + (((2 * j + h) ^ k_swz<D>(R)) * 16));
+    }
   const uint32_t one_bits = n == 0 ? 0x22222222u : 0u;
   const uint4 ones = make_uint4(one_bits, one_bits, one_bits, one_bits);
   const float c = a.sm_log2;
@@ -844,52 +913,56 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_spli
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
   v16f accl = v16f{};
-  const int r0 = perm_row(0, n), r1 = perm_row(1, n);
-  const int last_key = s1 - 1, last_blk = (s1 - 1) / 32;
 
-  // one 64-key step on the tile in `cur`, with the next tile's loads issued
-  // into `nxt` first
-  auto step = [&](int n0, const DecTile<D>& cur, DecTile<D>& nxt) {
-    dec_load<D>(a, bkv, n0 + kBN, last_key, last_blk, nblk_cap, r0, r1, n, h, nxt);
-    v16f t0 = v16f{}, t1 = v16f{};
-#pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      const int ks0 = (int)(cur.ks0[j / 2] >> (8 * h)), ks1 = (int)(cur.ks1[j / 2] >> (8 * h));
-      if (j % 2 == 0) {
-        t0 = mfma_fp4_sel<0>(cur.k0[j], qa[j], t0, ks0, qsw[j / 2]);
-        t1 = mfma_fp4_sel<0>(cur.k1[j], qa[j], t1, ks1, qsw[j / 2]);
-      } else {
-        t0 = mfma_fp4_sel<2>(cur.k0[j], qa[j], t0, ks0, qsw[j / 2]);
-        t1 = mfma_fp4_sel<2>(cur.k1[j], qa[j], t1, ks1, qsw[j / 2]);
-      }
-    }
+  // One 64-key step on tile t (stage t % 2); SP is that parity.
+  auto step = [&](auto parity, int t) {
+    constexpr int SP = decltype(parity)::value;
+    const int n0 = s0 + t * kBN;
+    const uint8_t* st = ring + SP * S::BYTES;
+    // tile t has landed; tile t+1 may still be loading
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::N_LOADS));
+    KOps<D> ko;
+    qk_load<D>(st, koff, n, h, ko);
+    VOps<D> vo;
+    v_load<D>(st + T::K_BYTES, n, h, vo);
+    v16f t0, t1;
+    qk_mfma<D>(ko, qa, qsw, t0, t1);
+    // every read of this stage is done: refill it with tile t+2
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    dec_issue<D>(hd, n0 + 2 * kBN, t + 2 < n_tiles, ring_addr + SP * S::BYTES, lane, dl);
+
     if (n0 + kBN > s1) mask_scores(t0, t1, n0 + 32 * h, s1);
-    const SoftmaxStep st = softmax_step(t0, t1, m_run, c, a.tau, pk);
-    if (__any(st.alpha != 1.0f)) {
+    const SoftmaxStep sm = softmax_step(t0, t1, m_run, c, a.tau, pk);
+    if (__any(sm.alpha != 1.0f)) {
 #pragma unroll
-      for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
-      accl[0] *= st.alpha;
+      for (int cc = 0; cc < NC; cc++) acc[cc] *= sm.alpha;
+      accl[0] *= sm.alpha;
     }
 #pragma unroll
     for (int cc = 0; cc < NC; cc++)
-      acc[cc] = mfma_fp4_32x32x64(cur.va[cc], st.p_codes, acc[cc], cur.vs[cc], st.p_scale);
-    accl = mfma_fp4_32x32x64(ones, st.p_codes, accl, ones_scale, st.p_scale);
+      acc[cc] = mfma_fp4_32x32x64(vo.va[cc], sm.p_codes, acc[cc], vo.vs[cc], sm.p_scale);
+    accl = mfma_fp4_32x32x64(ones, sm.p_codes, accl, ones_scale, sm.p_scale);
   };
 
-  DecTile<D> ta, tb;
-  dec_load<D>(a, bkv, s0, last_key, last_blk, nblk_cap, r0, r1, n, h, ta);
-  for (int n0 = s0; n0 < s1; n0 += 2 * kBN) {
-    step(n0, ta, tb);
-    if (n0 + kBN < s1) step(n0 + kBN, tb, ta);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(P0{}, t);
+    if (t + 1 < n_tiles) step(P1{}, t + 1);
   }
+  // drain the loads still writing the ring before it is reused below
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
 
-  // partial row: [m, l, acc[0..D)] for (b, query head, chunk)
+  // Each wave's (m, l, acc) per query head -> LDS, then the log-sum-exp
+  // combination of the kWaves chunks -> one partial row per query head.
+  float* pw = reinterpret_cast<float*>(lds);  // [kWaves][G][D + 2]
   const float lsum = __shfl(accl[0], n);
   if (n < G) {
-    float* part = a.partials + (((int64_t)b * a.Hq + g * G + n) * a.n_chunks + chunk_idx) * (D + 2);
+    float* row = pw + ((int64_t)w * G + n) * (D + 2);
     if (h == 0) {
-      part[0] = m_run;
-      part[1] = lsum;
+      row[0] = m_run;
+      row[1] = lsum;
     }
 #pragma unroll
     for (int cc = 0; cc < NC; cc++)
@@ -897,15 +970,36 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_spli
       for (int g4 = 0; g4 < 4; g4++) {
         const int ch = 32 * cc + 8 * g4 + 4 * h;
 #pragma unroll
-        for (int i = 0; i < 4; i++) part[2 + ch + i] = acc[cc][4 * g4 + i];
+        for (int i = 0; i < 4; i++) row[2 + ch + i] = acc[cc][4 * g4 + i];
       }
+  }
+  __syncthreads();
+  for (int o = tid; o < G * (D + 2); o += 256) {
+    const int hh = o / (D + 2), k = o % (D + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ww++) M = fmaxf(M, pw[(ww * G + hh) * (D + 2)]);
+    float v;
+    if (k == 0) {
+      v = M;
+    } else {
+      v = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ww++) {
+          const float* r = pw + (ww * G + hh) * (D + 2);
+          v += fast_exp2(r[0] - M) * r[k];
+        }
+      }
+    }
+    a.partials[(((int64_t)b * a.Hq + g * G + hh) * a.n_parts + part) * (D + 2) + k] = v;
   }
 }
 
-// Log-sum-exp merge of the chunk partials: one wave per (batch, query head).
-// Lane i owns chunk i (and i + 64, ...) for the max and the normaliser (wave
-// reductions); the accumulators are combined channel-parallel, eight chunks
-// per round so that eight partial rows are in flight at once.
+// Log-sum-exp merge of the workgroup partials: one wave per (batch, query
+// head).  Lane i owns partial i (and i + 64, ...) for the max and the
+// normaliser (wave reductions); the accumulators are combined channel-
+// parallel, eight partials per round so that eight rows are in flight.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -928,8 +1022,8 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
   const int b = (int)(row / a.Hq);
   int L = a.Sk;
   if (a.kv_lens) L = min(max(a.kv_lens[b], 0), a.Sk);
-  const int nc = (L + a.chunk - 1) / a.chunk;
-  const float* part = a.partials + row * a.n_chunks * (D + 2);
+  const int nc = (L + kWaves * a.chunk - 1) / (kWaves * a.chunk);
+  const float* part = a.partials + row * a.n_parts * (D + 2);
   float M = -INFINITY;
   for (int i = lane; i < nc; i += 64) M = fmaxf(M, part[(int64_t)i * (D + 2)]);
   M = wave_max(M);
@@ -996,7 +1090,7 @@ template <int D>
 hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   if (a.Hq / a.Hkv > 32) return hipErrorNotSupported;  // one MFMA column per query head
-  const int wg_x = (a.n_chunks + kWaves - 1) / kWaves;
+  const int wg_x = a.n_parts;
   if (wg_x > 0) {
     hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(wg_x, a.B * a.Hkv), dim3(256), 0, stream,
                        a, kScaleOne);
@@ -1013,6 +1107,7 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
 
 int attn_block_n(int) { return kBN; }
 int attn_default_chunk(int) { return kDecodeChunk; }
+int attn_decode_chunks_per_part() { return kWaves; }
 
 hipError_t launch_attn_prefill_mxfp4(const AttnArgs& a, hipStream_t stream) {
   switch (a.d) {

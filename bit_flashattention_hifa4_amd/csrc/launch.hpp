@@ -43,8 +43,8 @@ struct AttnArgs {
   int out_fp16;
   float sm_log2;           // sm_scale * log2(e)
   float sm_scale;
-  int chunk;               // decode chunk (tokens)
-  int n_chunks;            // ceil(cap / chunk)
+  int chunk;               // decode chunk (tokens with a fresh softmax state)
+  int n_parts;             // decode partials per query row: ceil(cap / (chunk * chunks per part))
   float tau;               // lazy-rescale threshold, log2 units (0 = every increase)
 };
 
@@ -52,6 +52,8 @@ struct AttnArgs {
 int attn_block_n(int d);
 // Decode chunk the library picks when the caller passes 0.
 int attn_default_chunk(int d);
+// Decode chunks combined into one workspace partial (one per wave of a workgroup).
+int attn_decode_chunks_per_part();
 
 hipError_t launch_attn_prefill_mxfp4(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_decode_mxfp4(const AttnArgs& a, hipStream_t stream);

@@ -129,6 +129,9 @@ HIFA4_API size_t hifa4_attn_workspace_size(const hifa4_attn_params* p);
  * lse: device fp32 [B][Hq][Sq] natural-log sum-exp of the scaled scores
  *      (m + ln l; -inf for rows without a visible key), or NULL.
  * workspace: device scratch of hifa4_attn_workspace_size(p) bytes (may be NULL if 0).
+ *      Decode keeps there one fp32 partial row (m, l, acc[d]) per query head
+ *      and per group of four consecutive chunks (the chunks of one workgroup,
+ *      already merged with each other); prefill needs none.
  */
 HIFA4_API hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4_mx_tensor k,
                             hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,

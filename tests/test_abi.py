@@ -97,7 +97,8 @@ def test_schedule_and_workspace_are_host_queries(lib):
     bn, ch = hb.hifa4_attn_schedule(d)
     assert ch > 0 and ch % bn == 0
     need = hb.hifa4_attn_workspace_size(d)
-    assert need == 2 * 8 * (-(-8192 // ch)) * (128 + 2) * 4
+    # one fp32 (m, l, acc[128]) row per query head per group of four chunks
+    assert need == 2 * 8 * (-(-8192 // (4 * ch))) * (128 + 2) * 4
     d2 = _params(Sq=1, Sk=5000, decode_chunk=bn * 3)
     assert hb.hifa4_attn_schedule(d2)[1] == bn * 3
     assert hb.hifa4_attn_workspace_size(_params(d=100)) == 0   # invalid -> 0
