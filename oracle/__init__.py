@@ -97,7 +97,7 @@ def _open(path: str):
     lib.oracle_quantize_v.argtypes = [_F, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, _U8, _U8, _D]
     lib.oracle_attention.restype = ctypes.c_int
-    lib.oracle_attention.argtypes = [ctypes.POINTER(_AttnCfg), _D, _D, _D, _I32, _I64,
+    lib.oracle_attention.argtypes = [ctypes.POINTER(_AttnCfg), _D, _D, _D, _I32, _I32, _I64,
                                      ctypes.c_long, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
     return lib
 
@@ -203,12 +203,17 @@ def quantize_v(x, *, cap: int | None = None, quantise: bool = True):
 
 def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int = 64,
               chunk: int = 0, quant_p: bool = True, br: int = 128, kv_lens=None, rows=None,
+              chunk_phase=None,
               want_weights: bool = False, want_eps: bool = False, nthreads: int | None = None,
               tau: float = 0.0):
     """Online-softmax attention over dequantised (or exact) operands, fp64.
 
     q [B,Hq,Sq,d]; k, v [B,Hkv,Sk,d] (float64).  tau: lazy-rescale threshold
-    (log2 units, 0 = FlashAttention-2 frame).  Returns a dict with
+    (log2 units, 0 = FlashAttention-2 frame).  chunk > 0 splits each row's keys
+    into runs that start from a fresh softmax state and are merged with the
+    log-sum-exp rule; chunk_phase [B,Hkv] (keys, multiples of bc below chunk)
+    shifts that grid: a run starts at every key t > 0 with (t + phase) % chunk
+    == 0.  Returns a dict with
     o, o_naive, l, l_naive, lse (and w, eps_* when asked).  With ``rows`` (flat
     ids (b*Hq + h)*Sq + i) only those rows are computed, in that order.
     """
@@ -225,6 +230,10 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
     if kv_lens is not None:
         lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
         assert lens.shape == (B,) and (lens <= Sk).all()
+    ph = None
+    if chunk_phase is not None:
+        ph = np.ascontiguousarray(np.asarray(chunk_phase, dtype=np.int32))
+        assert ph.shape == (B, Hkv)
     rr = None
     n = B * Hq * Sq
     if rows is not None:
@@ -243,7 +252,7 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
         eps = [np.zeros((B, Hq, n_qt, n_kt)) for _ in range(4)]
     e = eps or [None] * 4
     rc = _load().oracle_attention(ctypes.byref(cfg), _ptr(q, _D), _ptr(k, _D), _ptr(v, _D),
-                                  _ptr(lens, _I32), _ptr(rr, _I64), n, _ptr(o, _D),
+                                  _ptr(lens, _I32), _ptr(ph, _I32), _ptr(rr, _I64), n, _ptr(o, _D),
                                   _ptr(lse, _D), _ptr(o_naive, _D), _ptr(l, _D), _ptr(ln, _D),
                                   _ptr(w, _D), _ptr(e[0], _D), _ptr(e[1], _D), _ptr(e[2], _D),
                                   _ptr(e[3], _D))

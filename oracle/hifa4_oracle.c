@@ -43,7 +43,11 @@
  *     t <= i + L - Sq, with L the key count of that sequence;
  *   - a row with no visible key outputs 0 with lse = -inf;
  *   - split-K decode runs the online softmax from a fresh state on each chunk
- *     and merges the partial (m, l, acc) with the log-sum-exp rule.
+ *     and merges the partial (m, l, acc) with the log-sum-exp rule; the chunk
+ *     grid of a (sequence, KV head) may be shifted by a phase (a multiple of
+ *     the key tile), so that a fresh state starts at every key t > 0 with
+ *     (t + phase) % chunk == 0: any cut of a sequence into runs is a valid
+ *     split, and the exact result does not depend on it.
  */
 #define _USE_MATH_DEFINES
 #include <math.h>
@@ -234,6 +238,7 @@ typedef struct {
   const oracle_attn_cfg* cfg;
   const double *q, *k, *v;
   const int32_t* kv_lens;
+  const int32_t* chunk_phase; /* [B][Hkv] keys, or NULL (all 0) */
   const int64_t* rows; /* NULL: all rows, else flattened (b*Hq + h)*Sq + i */
   long n_rows;
   double *o, *lse, *o_naive, *l_out, *l_naive_out, *w;
@@ -266,8 +271,11 @@ static void attn_row(attn_job* J, int b, int h, int i, size_t out, double* S, do
     for (int t = 0; t < c->Sk; t++) wr[t] = 0.0;
 
   long chunk = c->chunk > 0 ? c->chunk : (nvis > 0 ? nvis : 1);
-  for (long c0 = 0; c0 < nvis; c0 += chunk) {
-    long cend = c0 + chunk < nvis ? c0 + chunk : nvis;
+  long phase = (c->chunk > 0 && J->chunk_phase) ? J->chunk_phase[(size_t)b * c->Hkv + g] : 0;
+  for (long c0 = 0, cend; c0 < nvis; c0 = cend) {
+    /* the next grid point after c0: the smallest t > c0 with (t + phase) % chunk == 0 */
+    cend = ((c0 + phase) / chunk + 1) * chunk - phase;
+    if (cend > nvis) cend = nvis;
     double m = -INFINITY, l = 0.0, ln = 0.0;
     for (int j = 0; j < d; j++) acc_c[j] = 0.0;
     for (long t0 = c0; t0 < cend; t0 += c->bc) {
@@ -411,6 +419,8 @@ static void* attn_worker(void* arg) {
 /*
  * q: double [B][Hq][Sq][d]; k, v: double [B][Hkv][Sk][d] (dequantised MXFP4
  * values, or exact values for the exact mode).  kv_lens: [B] or NULL.
+ * chunk_phase: [B][Hkv] split phases in keys (multiples of bc below chunk), or
+ * NULL; used only with chunk > 0.
  * rows: NULL for every row, else n_rows flattened row ids (b*Hq + h)*Sq + i.
  * Outputs (each may be NULL), indexed by row id, or by position in `rows`
  * when a subset is given: o, o_naive [rows][d]; lse, l, l_naive [rows];
@@ -420,7 +430,8 @@ static void* attn_worker(void* arg) {
  * Returns 0, or -1 on a bad configuration.
  */
 int oracle_attention(const oracle_attn_cfg* cfg, const double* q, const double* k,
-                     const double* v, const int32_t* kv_lens, const int64_t* rows, long n_rows,
+                     const double* v, const int32_t* kv_lens, const int32_t* chunk_phase,
+                     const int64_t* rows, long n_rows,
                      double* o, double* lse, double* o_naive, double* l_out, double* l_naive_out,
                      double* w, double* eps_sum, double* eps_cnt, double* ph_sum,
                      double* p_sum) {
@@ -429,6 +440,9 @@ int oracle_attention(const oracle_attn_cfg* cfg, const double* q, const double* 
     return -1;
   if (cfg->quant_p && cfg->bc % 32 && cfg->bc < cfg->Sk) return -1;
   if (cfg->chunk > 0 && cfg->chunk % cfg->bc) return -1;
+  if (chunk_phase && cfg->chunk > 0)
+    for (long i = 0; i < (long)cfg->B * cfg->Hkv; i++)
+      if (chunk_phase[i] < 0 || chunk_phase[i] >= cfg->chunk || chunk_phase[i] % cfg->bc) return -1;
   attn_job J;
   memset(&J, 0, sizeof J);
   J.cfg = cfg;
@@ -436,6 +450,7 @@ int oracle_attention(const oracle_attn_cfg* cfg, const double* q, const double* 
   J.k = k;
   J.v = v;
   J.kv_lens = kv_lens;
+  J.chunk_phase = chunk_phase;
   J.rows = rows;
   J.n_rows = n_rows;
   J.o = o;

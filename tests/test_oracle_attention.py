@@ -262,6 +262,53 @@ def test_split_k_mxfp4_equals_merge_of_chunk_runs(chunk):
     assert np.abs(un["o"] - a["o"]).max() > 0
 
 
+@pytest.mark.parametrize("chunk,phases", [(128, [[0, 64], [64, 0]]), (192, [[128, 64], [0, 128]])])
+def test_split_phase_mxfp4_equals_merge_of_runs(chunk, phases):
+    # a phase shifts the fresh-state grid of one (sequence, KV head): the result is
+    # the log-sum-exp merge of separate runs over [0, chunk - phase),
+    # [chunk - phase, 2 chunk - phase), ... of that head's keys
+    qq = _quantised_case(12, B=2, Hq=4, Hkv=2, Sq=1, Sk=330)
+    q, k, v = qq["q_deq"], qq["k_deq"], qq["v_deq"]
+    lens = np.array([330, 201], dtype=np.int32)
+    ph = np.array(phases, dtype=np.int32)
+    a = oracle.attention(q, k, v, causal=True, bc=64, chunk=chunk, quant_p=True, kv_lens=lens,
+                         chunk_phase=ph)
+    for b in range(2):
+        for g in range(2):
+            L = int(lens[b])
+            cuts = [0] + [t for t in range(1, L) if (t + ph[b, g]) % chunk == 0] + [L]
+            qs = q[b:b + 1, 2 * g:2 * g + 2]
+            lses, outs = [], []
+            for c0, c1 in zip(cuts[:-1], cuts[1:]):
+                r = oracle.attention(qs, k[b:b + 1, g:g + 1, c0:c1], v[b:b + 1, g:g + 1, c0:c1],
+                                     causal=False, bc=64, quant_p=True)
+                lses.append(r["lse"])
+                outs.append(r["o"])
+            lse = np.logaddexp.reduce(np.stack(lses), axis=0)
+            o = sum(np.exp(l - lse)[..., None] * oc for l, oc in zip(lses, outs))
+            np.testing.assert_allclose(a["o"][b, 2 * g:2 * g + 2], o[0], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(a["lse"][b, 2 * g:2 * g + 2], lse[0], rtol=1e-12)
+    # the phase is a real parameter of the 4-bit result, not of the exact one
+    a0 = oracle.attention(q, k, v, causal=True, bc=64, chunk=chunk, quant_p=True, kv_lens=lens)
+    assert np.abs(a0["o"] - a["o"]).max() > 0
+    e1 = oracle.attention(q, k, v, causal=True, bc=64, chunk=chunk, quant_p=False, kv_lens=lens,
+                          chunk_phase=ph)
+    e0 = oracle.attention(q, k, v, causal=True, bc=64, chunk=0, quant_p=False, kv_lens=lens)
+    np.testing.assert_allclose(e1["o"], e0["o"], rtol=1e-12, atol=1e-13)
+
+
+def test_zero_phase_is_the_plain_chunk_grid():
+    qq = _quantised_case(13, B=1, Hq=4, Hkv=2, Sq=1, Sk=300)
+    q, k, v = qq["q_deq"], qq["k_deq"], qq["v_deq"]
+    a = oracle.attention(q, k, v, causal=False, bc=64, chunk=128, quant_p=True)
+    b = oracle.attention(q, k, v, causal=False, bc=64, chunk=128, quant_p=True,
+                         chunk_phase=np.zeros((1, 2), np.int32))
+    np.testing.assert_array_equal(a["o"], b["o"])
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, causal=False, bc=64, chunk=128, quant_p=True,
+                         chunk_phase=np.full((1, 2), 32, np.int32))
+
+
 def test_kv_lens_equals_sliced_cache():
     qq = _quantised_case(6, B=2, Hq=4, Hkv=2, Sq=3, Sk=260)
     q, k, v = qq["q_deq"], qq["k_deq"], qq["v_deq"]

@@ -50,6 +50,10 @@ MUTANTS = [
      "double m_new = smax > m ? smax : m;", 0),
     ("lazy_threshold_in_natural_units", "double m_new = smax > m + c->tau * M_LN2 ? smax : m;",
      "double m_new = smax > m + c->tau ? smax : m;", 0),
+    ("split_phase_sign_flipped", "cend = ((c0 + phase) / chunk + 1) * chunk - phase;",
+     "cend = ((c0 + phase) / chunk + 1) * chunk + phase;", 0),
+    ("split_phase_ignored", "cend = ((c0 + phase) / chunk + 1) * chunk - phase;",
+     "cend = (c0 / chunk + 1) * chunk;", 0),
     ("dot_product_drops_last_channel", "for (int j = 0; j < d; j++) s += qr[j] * kr[j];",
      "for (int j = 0; j < d - 1; j++) s += qr[j] * kr[j];", 0),
 ]
@@ -77,6 +81,7 @@ def _pin_checks():
         TA.test_inconsistent_normaliser_is_coherent_row_scaling,
         lambda: TA.test_split_k_mxfp4_equals_merge_of_chunk_runs(64),
         lambda: TA.test_split_k_exact_equals_unsplit(128),
+        lambda: TA.test_split_phase_mxfp4_equals_merge_of_runs(128, [[0, 64], [64, 0]]),
     ]
     return checks
 
