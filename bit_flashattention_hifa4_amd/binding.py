@@ -8,7 +8,8 @@ the tensors are not on the GPU, the calls raise.
 
 The Python names match the C entry points: ``hifa4_quantize_qkv``,
 ``hifa4_attn_fwd``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
-``hifa4_attn_workspace_size``, ``hifa4_status_string``, ``hifa4_last_error``.
+``hifa4_attn_decode_piece_tiles``, ``hifa4_attn_workspace_size``,
+``hifa4_status_string``, ``hifa4_last_error``.
 """
 from __future__ import annotations
 
@@ -88,6 +89,8 @@ def load_library(path: str = LIB_PATH):
     lib.hifa4_attn_schedule.restype = st
     lib.hifa4_attn_schedule.argtypes = [ctypes.POINTER(AttnParamsC), ctypes.POINTER(i32),
                                         ctypes.POINTER(i32)]
+    lib.hifa4_attn_decode_piece_tiles.restype = i32
+    lib.hifa4_attn_decode_piece_tiles.argtypes = [ctypes.POINTER(AttnParamsC), ctypes.c_int64]
     lib.hifa4_status_string.restype = ctypes.c_char_p
     lib.hifa4_status_string.argtypes = [st]
     lib.hifa4_last_error.restype = ctypes.c_char_p
@@ -218,6 +221,10 @@ def hifa4_attn_schedule(params: AttnParamsC) -> tuple[int, int]:
     _check(load_library().hifa4_attn_schedule(ctypes.byref(params), ctypes.byref(bn),
                                               ctypes.byref(ch)))
     return bn.value, ch.value
+
+
+def hifa4_attn_decode_piece_tiles(params: AttnParamsC, total_tiles: int) -> int:
+    return int(load_library().hifa4_attn_decode_piece_tiles(ctypes.byref(params), int(total_tiles)))
 
 
 def hifa4_attn_fwd(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,

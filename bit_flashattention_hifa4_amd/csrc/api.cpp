@@ -86,22 +86,32 @@ hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
   *chunk = 0;
   if (p->Sq == 1) {
     const int bn = hifa4::attn_block_n(p->d);
-    int c = p->decode_chunk ? p->decode_chunk : hifa4::attn_default_chunk(p->d);
-    if (c <= 0 || c % bn)
-      return fail(HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk %d is not a positive multiple of %d",
+    if (p->decode_chunk < 0 || p->decode_chunk % bn)
+      return fail(HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk %d is not 0 or a positive multiple of %d",
                   p->decode_chunk, bn);
-    *chunk = c;
+    // tile and piece indices of the decode schedule are 32-bit
+    const int64_t pairs = (int64_t)p->B * p->Hkv;
+    if (pairs * ((p->Sk + bn - 1) / bn) + pairs >= ((int64_t)1 << 31))
+      return fail(HIFA4_ERR_UNSUPPORTED, "decode problem too large (B*Hkv*ceil(Sk/%d) >= 2^31)", bn);
+    *chunk = p->decode_chunk;
   } else if (p->decode_chunk) {
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk is only meaningful with Sq == 1");
   }
   return HIFA4_OK;
 }
 
-size_t decode_workspace(const hifa4_attn_params* p, int cap, int chunk) {
-  if (p->Sq != 1 || chunk <= 0) return 0;
-  const int64_t per = (int64_t)chunk * hifa4::attn_decode_chunks_per_part();
-  const int64_t n_parts = (cap + per - 1) / per;
-  return (size_t)p->B * p->Hq * n_parts * (p->d + 2) * sizeof(float);
+// Decode partial rows: one per (piece, pair) run, at row piece + pair, so at
+// most (pieces + pairs - 1) rows of G query heads x (m, l, 2 unused, acc[d]).
+size_t decode_workspace(const hifa4_attn_params* p, int chunk) {
+  if (p->Sq != 1) return 0;
+  const int bn = hifa4::attn_block_n(p->d);
+  const int64_t pairs = (int64_t)p->B * p->Hkv;
+  const int64_t max_tiles = pairs * ((p->Sk + bn - 1) / bn);
+  if (max_tiles == 0) return 0;
+  const int64_t pieces = chunk > 0 ? (max_tiles + chunk / bn - 1) / (chunk / bn)
+                                   : hifa4::attn_decode_waves(p->d);
+  const int64_t rows = pieces + pairs - 1;
+  return (size_t)rows * (p->Hq / p->Hkv) * (p->d + 4) * sizeof(float);
 }
 
 }  // namespace
@@ -206,7 +216,8 @@ size_t hifa4_attn_workspace_size(const hifa4_attn_params* p) {
     g_last_error = saved;
     return 0;
   }
-  return decode_workspace(p, cap, chunk);
+  (void)cap;
+  return decode_workspace(p, chunk);
 }
 
 hifa4_status hifa4_attn_schedule(const hifa4_attn_params* p, int32_t* block_n,
@@ -218,6 +229,17 @@ hifa4_status hifa4_attn_schedule(const hifa4_attn_params* p, int32_t* block_n,
   if (block_n) *block_n = hifa4::attn_block_n(p->d);
   if (chunk_tokens) *chunk_tokens = chunk;
   return HIFA4_OK;
+}
+
+int32_t hifa4_attn_decode_piece_tiles(const hifa4_attn_params* p, int64_t total_tiles) {
+  int cap, chunk;
+  const std::string saved = g_last_error;
+  if (check_params(p, &cap, &chunk) != HIFA4_OK || p->Sq != 1 || total_tiles < 0 ||
+      total_tiles >= ((int64_t)1 << 31)) {
+    g_last_error = saved;
+    return 0;
+  }
+  return hifa4::decode_piece_tiles(chunk, hifa4::attn_decode_waves(p->d), (int)total_tiles);
 }
 
 hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4_mx_tensor k,
@@ -242,7 +264,7 @@ hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4
   if (lse && !aligned16(lse)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
   if (p->kv_lens && !aligned16(p->kv_lens))
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_lens is not 16-byte aligned");
-  const size_t need = decode_workspace(p, cap, chunk);
+  const size_t need = decode_workspace(p, chunk);
   if (workspace_bytes < need)
     return fail(HIFA4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
                 need);
@@ -285,10 +307,7 @@ hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4
   a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)d);
   a.sm_log2 = a.sm_scale * 1.4426950408889634f;
   a.chunk = chunk;
-  {
-    const int64_t per = (int64_t)chunk * hifa4::attn_decode_chunks_per_part();
-    a.n_parts = chunk ? (int)((cap + per - 1) / per) : 0;
-  }
+  a.dec_waves = hifa4::attn_decode_waves(d);
   a.tau = p->rescale_threshold;
   hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
                             : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -48,9 +49,9 @@ namespace hifa4 {
 namespace {
 
 constexpr int kBN = 64;            // keys per online-softmax step (the P frame tile)
+static_assert(kBN == 64, "decode_piece_tiles counts 64-key tiles");
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kBR = 32 * kWaves;   // queries per prefill workgroup
-constexpr int kDecodeChunk = 512;  // tokens per decode wave (fresh state), default
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Row of the 64-key step that A-operand row m of 32-key tile t loads.
@@ -742,22 +743,20 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
 }
 
 // ---------------------------------------------------------------------------
-// Decode (Sq == 1), split-K.  A workgroup takes kWaves consecutive chunks of
-// `a.chunk` keys of one (batch, kv head); each wave runs one chunk from a
-// fresh online-softmax state against the G query heads of the group (the
-// MFMA's 32 query columns, G used), and the waves' results are combined in
-// LDS with the log-sum-exp rule into one partial (m, l, acc[d]) per query
-// head and workgroup; the merge kernel combines the workgroups.
+// Decode (Sq == 1), split-K over a balanced schedule (below).  A wave runs
+// the online softmax of one run of key tiles of one (sequence, KV head)
+// against the G query heads of the group (the MFMA's 32 query columns, G
+// used) and writes one partial (m, l, acc[d]) per query head; the merge
+// kernel combines the runs of a pair with the log-sum-exp rule.
 //
 // Decode reads every K / V byte once, so it is bound by how many bytes are
-// in flight.  Each wave streams its chunk through a private two-stage LDS
-// ring with memory -> LDS buffer loads (no registers held by loads in
-// flight): while tile t is computed from registers, tiles t+1 and t+2 are
-// loading.  The loads of tile t+2 go into tile t's stage as soon as its
-// operands are in registers.  The K layout in a stage is the prefill one
-// (rows in MFMA read order, swizzled chunks), so the operand reads are
-// shared with prefill.  Keys past the chunk read real data or zeros (past
-// the sequence: descriptor range) and are masked.
+// in flight.  Each wave streams its tiles through a private LDS ring with
+// memory -> LDS buffer loads (no registers held by loads in flight): while
+// tile t is computed from registers, the ring's other stages are loading, and
+// tile t's stage is refilled as soon as its operands are in registers.  The
+// K layout in a stage is the prefill one (rows in MFMA read order, swizzled
+// chunks), so the operand reads are shared with prefill.  Keys past the
+// sequence read zeros (descriptor range) and are masked.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DecStage {
@@ -834,68 +833,167 @@ __device__ __forceinline__ void dec_issue(const HeadDescs& hd, int n0, bool live
   }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split-K schedule.  Pair s = (sequence b, KV head g), s = b * Hkv + g,
+// has tiles(L_b) = ceil(L_b / 64) key tiles; the pairs' tiles laid end to end
+// (sequence outer) form one sequence of `total` tiles, cut into pieces of
+// decode_piece_tiles(...) tiles.  Wave w of the persistent grid takes pieces
+// w, w + W, ...; a piece runs the online softmax from a fresh state and
+// restarts where it crosses into the next pair.  Each (piece, pair) run leaves
+// one partial row per query head of the pair at workspace row piece + s, which
+// is unique: a later piece never covers an earlier pair.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int dec_len(const AttnArgs& a, int b) {
+  if (b >= a.B) return 0;
+  return a.kv_lens ? min(max(a.kv_lens[b], 0), a.Sk) : a.Sk;
+}
+
+__device__ __forceinline__ int dec_tiles(int L) { return (L + kBN - 1) / kBN; }
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_scan_i(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Tiles of all pairs, and of the pairs of the sequences before b.
+struct DecTotals {
+  int total, before;
+};
+
+__device__ __forceinline__ DecTotals dec_totals(const AttnArgs& a, int b, int lane) {
+  int tot = 0, bef = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int nt = dec_tiles(dec_len(a, bb));
+    tot += nt;
+    bef += bb < b ? nt : 0;
+  }
+  return {uniform(wave_sum_i(tot) * a.Hkv), uniform(wave_sum_i(bef) * a.Hkv)};
+}
+
+// Where a wave stands in the tile sequence: pair (b, g) with L keys and nt
+// tiles, and the tile lt within it.
+struct DecCursor {
+  int b, g, lt, nt, L;
+};
+
+// The pair and tile of flattened tile t < total: a wave-parallel search over
+// the sequences' tile counts, 64 sequences at a time.
+__device__ DecCursor dec_locate(const AttnArgs& a, int t, int lane) {
+  DecCursor c{0, 0, 0, 1, 0};
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int L = dec_len(a, bb);
+    const int nt = dec_tiles(L);
+    const int incl = base + wave_scan_i(nt * a.Hkv, lane);
+    const uint64_t hit = __ballot(bb < a.B && incl > t);
+    if (hit) {
+      const int i = __builtin_ctzll(hit);  // first sequence whose pairs reach past t
+      c.b = b0 + i;
+      c.L = __shfl(L, i);
+      c.nt = __shfl(nt, i);
+      const int off = t - (__shfl(incl, i) - c.nt * a.Hkv);
+      c.g = off / c.nt;
+      c.lt = off - c.g * c.nt;
+      break;
+    }
+    base = __shfl(incl, 63);
+  }
+  return {uniform(c.b), uniform(c.g), uniform(c.lt), uniform(c.nt), uniform(c.L)};
+}
+
+// The first tile of the next pair that has any (the caller knows one exists).
+__device__ __forceinline__ void dec_next_pair(const AttnArgs& a, DecCursor& c) {
+  c.lt = 0;
+  if (++c.g < a.Hkv) return;
+  c.g = 0;
+  do {
+    ++c.b;
+    c.L = dec_len(a, c.b);
+    c.nt = dec_tiles(c.L);
+  } while (c.nt == 0 && c.b + 1 < a.B);
+}
+
 template <int D>
-__global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_split_kernel(AttnArgs a,
-                                                                                  int ones_scale) {
+__device__ __forceinline__ HeadDescs dec_descs(const AttnArgs& a, const DecCursor& c) {
+  return head_descs<D>(a, (int64_t)c.b * a.Hkv + c.g, c.L, (c.L + 31) / 32, (a.cap + 31) / 32);
+}
+
+// Per-wave LDS ring of the decode kernel; the persistent grid has as many
+// waves per compute unit as the 160 KB of LDS holds rings (at most eight).
+template <int D>
+struct DecRing {
+  static constexpr int STAGES = D == 64 ? 4 : 2;  // about 35 KB of loads in flight per wave
+  static constexpr int BYTES = STAGES * DecStage<D>::BYTES;
+  static constexpr int WAVES_PER_CU = 163840 / BYTES < 8 ? 163840 / BYTES : 8;
+};
+constexpr int kComputeUnits = 256;  // MI355X
+
+// Partial row of one query head: m (log2 units), l, two unused floats, acc[d].
+template <int D>
+__device__ __forceinline__ void dec_flush(const AttnArgs& a, int prow, int G, int n, int h,
+                                          float m_run, const v16f& accl, const v16f* acc) {
+  constexpr int NC = D / 32;
+  const float lsum = __shfl(accl[0], n);
+  if (n < G) {
+    float* row = a.partials + ((int64_t)prow * G + n) * (D + 4);
+    if (h == 0) {
+      row[0] = m_run;
+      row[1] = lsum;
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        const int ch = 32 * cc + 8 * g4 + 4 * h;
+        *reinterpret_cast<float4*>(row + 4 + ch) =
+            make_float4(acc[cc][4 * g4], acc[cc][4 * g4 + 1], acc[cc][4 * g4 + 2], acc[cc][4 * g4 + 3]);
+      }
+  }
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int D>
+__global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_kernel(AttnArgs a,
+                                                                              int ones_scale) {
   using T = PrefillTile<D>;
   using S = DecStage<D>;
+  constexpr int NS = DecRing<D>::STAGES;
   constexpr int DB = T::DB, DS = T::DS, NJ = D / 64, NC = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * 2 * S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NS * S::BYTES];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x;
   const int h = lane >> 5, n = lane & 31;
   const int G = a.Hq / a.Hkv;
-  const int bkv_i = blockIdx.y;
-  const int b = bkv_i / a.Hkv, g = bkv_i % a.Hkv;
-  const int64_t bkv = (int64_t)b * a.Hkv + g;
-  int L = a.Sk;
-  if (a.kv_lens) L = min(max(a.kv_lens[b], 0), a.Sk);
-  const int part = blockIdx.x;
-  if (part * kWaves * a.chunk >= L) return;  // uniform per workgroup
-  const int s0 = (part * kWaves + w) * a.chunk;
-  const int s1 = min(L, s0 + a.chunk);
-  const int n_tiles = s0 < L ? (s1 - s0 + kBN - 1) / kBN : 0;  // uniform per wave
-  const int nblk_cap = (a.cap + 31) / 32;
-  const int nblk_valid = (L + 31) / 32;
+  const int total = dec_totals(a, 0, lane).total;
+  const int pt = decode_piece_tiles(a.chunk, a.dec_waves, total);
+  const int n_pieces = (total + pt - 1) / pt;
+  if ((int)blockIdx.x >= n_pieces) return;  // uniform per wave
 
-  const HeadDescs hd = head_descs<D>(a, bkv, L, nblk_valid, nblk_cap);
   const DecLanes<D> dl = dec_lanes<D>(lane);
-  uint8_t* ring = lds + w * 2 * S::BYTES;
   const uint32_t ring_addr = lds_addr(ring);
-  dec_issue<D>(hd, s0, 0 < n_tiles, ring_addr, lane, dl);
-  dec_issue<D>(hd, s0 + kBN, 1 < n_tiles, ring_addr + S::BYTES, lane, dl);
-
-  // Q operand: column n is query head g*G + n (zero for n >= G).
-  uint4 qa[NJ];
-  uint32_t qsw_raw[(NJ + 1) / 2];
-  if (n < G) {
-    const int64_t row = ((int64_t)b * a.Hq + g * G + n);  // Sq == 1
-    const uint8_t* qc = a.q_codes + row * DB;
-    const uint8_t* qsc = a.q_scales + row * DS;
-#pragma unroll
-    for (int j = 0; j < NJ; j++) qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
-#pragma unroll
-    for (int j = 0; j < NJ; j += 2) {
-      if constexpr (DS == 2)
-        qsw_raw[j / 2] = *reinterpret_cast<const uint16_t*>(qsc);
-      else
-        qsw_raw[j / 2] = reinterpret_cast<const uint32_t*>(qsc)[j >> 1];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NJ; j++) qa[j] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NJ; j += 2) qsw_raw[j / 2] = 0;
-  }
-  // Q and both prologue tiles: the compiler then knows no load of its own is
-  // in flight in the loop.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  int qsw[(NJ + 1) / 2];
-#pragma unroll
-  for (int j = 0; j < NJ; j += 2) qsw[j / 2] = (int)(qsw_raw[j / 2] >> (8 * h));
-
   uint32_t koff[2][NJ];
 #pragma unroll
   for (int t = 0; t < 2; t++)
@@ -907,99 +1005,126 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_decode_spli
   const uint32_t one_bits = n == 0 ? 0x22222222u : 0u;
   const uint4 ones = make_uint4(one_bits, one_bits, one_bits, one_bits);
   const float c = a.sm_log2;
-  float m_run = -INFINITY;
-  uint4 pk = make_uint4(0, 0, 0, 0);
-  v16f acc[NC];
-#pragma unroll
-  for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
-  v16f accl = v16f{};
 
-  // One 64-key step on tile t (stage t % 2); SP is that parity.
-  auto step = [&](auto parity, int t) {
-    constexpr int SP = decltype(parity)::value;
-    const int n0 = s0 + t * kBN;
-    const uint8_t* st = ring + SP * S::BYTES;
-    // tile t has landed; tile t+1 may still be loading
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::N_LOADS));
-    KOps<D> ko;
-    qk_load<D>(st, koff, n, h, ko);
-    VOps<D> vo;
-    v_load<D>(st + T::K_BYTES, n, h, vo);
-    v16f t0, t1;
-    qk_mfma<D>(ko, qa, qsw, t0, t1);
-    // every read of this stage is done: refill it with tile t+2
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
-    dec_issue<D>(hd, n0 + 2 * kBN, t + 2 < n_tiles, ring_addr + SP * S::BYTES, lane, dl);
-
-    if (n0 + kBN > s1) mask_scores(t0, t1, n0 + 32 * h, s1);
-    const SoftmaxStep sm = softmax_step(t0, t1, m_run, c, a.tau, pk);
-    if (__any(sm.alpha != 1.0f)) {
+  // Q operand of a pair: column n is query head g*G + n (zero for n >= G).
+  uint4 qa[NJ];
+  uint32_t qsw_raw[(NJ + 1) / 2];
+  int qsw[(NJ + 1) / 2];
+  auto load_q = [&](const DecCursor& cur) {
+    if (n < G) {
+      const int64_t row = (int64_t)cur.b * a.Hq + cur.g * G + n;  // Sq == 1
+      const uint8_t* qc = a.q_codes + row * DB;
+      const uint8_t* qsc = a.q_scales + row * DS;
 #pragma unroll
-      for (int cc = 0; cc < NC; cc++) acc[cc] *= sm.alpha;
-      accl[0] *= sm.alpha;
+      for (int j = 0; j < NJ; j++) qa[j] = *reinterpret_cast<const uint4*>(qc + 32 * j + 16 * h);
+#pragma unroll
+      for (int j = 0; j < NJ; j += 2) {
+        if constexpr (DS == 2)
+          qsw_raw[j / 2] = *reinterpret_cast<const uint16_t*>(qsc);
+        else
+          qsw_raw[j / 2] = reinterpret_cast<const uint32_t*>(qsc)[j >> 1];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; j++) qa[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; j += 2) qsw_raw[j / 2] = 0;
     }
+  };
+  auto shift_q = [&]() {
 #pragma unroll
-    for (int cc = 0; cc < NC; cc++)
-      acc[cc] = mfma_fp4_32x32x64(vo.va[cc], sm.p_codes, acc[cc], vo.vs[cc], sm.p_scale);
-    accl = mfma_fp4_32x32x64(ones, sm.p_codes, accl, ones_scale, sm.p_scale);
+    for (int j = 0; j < NJ; j += 2) qsw[j / 2] = (int)(qsw_raw[j / 2] >> (8 * h));
   };
 
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(P0{}, t);
-    if (t + 1 < n_tiles) step(P1{}, t + 1);
-  }
-  // drain the loads still writing the ring before it is reused below
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
+  uint4 pk = make_uint4(0, 0, 0, 0);
+  for (int piece = blockIdx.x; piece < n_pieces; piece += gridDim.x) {
+    const int t_beg = piece * pt, t_end = min(total, t_beg + pt);
+    DecCursor cc = dec_locate(a, t_beg, lane);  // pair of the tile being computed
+    DecCursor ic = cc;                           // pair of the next tile to load
+    HeadDescs hd = dec_descs<D>(a, ic);
+    int ti = t_beg;                              // next tile to load
+    // Load tile ti (nothing past the piece) into the stage at LDS address st.
+    auto issue = [&](uint32_t st) {
+      const bool live = ti < t_end;
+      dec_issue<D>(hd, ic.lt * kBN, live, st, lane, dl);
+      if (live && ti + 1 < t_end && ++ic.lt == ic.nt) {
+        dec_next_pair(a, ic);
+        hd = dec_descs<D>(a, ic);
+      }
+      ++ti;
+    };
+#pragma unroll
+    for (int s = 0; s < NS; s++) issue(ring_addr + s * S::BYTES);
+    load_q(cc);
+    // Q and the first tiles: the compiler then knows no load of its own is
+    // in flight in the loop.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    shift_q();
 
-  // Each wave's (m, l, acc) per query head -> LDS, then the log-sum-exp
-  // combination of the kWaves chunks -> one partial row per query head.
-  float* pw = reinterpret_cast<float*>(lds);  // [kWaves][G][D + 2]
-  const float lsum = __shfl(accl[0], n);
-  if (n < G) {
-    float* row = pw + ((int64_t)w * G + n) * (D + 2);
-    if (h == 0) {
-      row[0] = m_run;
-      row[1] = lsum;
-    }
+    float m_run = -INFINITY;
+    v16f acc[NC];
 #pragma unroll
-    for (int cc = 0; cc < NC; cc++)
+    for (int k = 0; k < NC; k++) acc[k] = v16f{};
+    v16f accl = v16f{};
+
+    // One 64-key step on tile t, held in stage SP.
+    auto step = [&](auto stage, int t) {
+      constexpr int SP = decltype(stage)::value;
+      const uint8_t* st = ring + SP * S::BYTES;
+      // tile t has landed; the NS - 1 tiles after it may still be loading
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * S::N_LOADS));
+      KOps<D> ko;
+      qk_load<D>(st, koff, n, h, ko);
+      VOps<D> vo;
+      v_load<D>(st + T::K_BYTES, n, h, vo);
+      v16f s_lo, s_hi;
+      qk_mfma<D>(ko, qa, qsw, s_lo, s_hi);
+      // every read of this stage is done: refill it
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      issue(ring_addr + SP * S::BYTES);
+
+      const bool pair_end = cc.lt + 1 == cc.nt;
+      if (pair_end && (cc.L & (kBN - 1))) mask_scores(s_lo, s_hi, cc.lt * kBN + 32 * h, cc.L);
+      const SoftmaxStep sm = softmax_step(s_lo, s_hi, m_run, c, a.tau, pk);
+      if (__any(sm.alpha != 1.0f)) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; g4++) {
-        const int ch = 32 * cc + 8 * g4 + 4 * h;
-#pragma unroll
-        for (int i = 0; i < 4; i++) row[2 + ch + i] = acc[cc][4 * g4 + i];
+        for (int k = 0; k < NC; k++) acc[k] *= sm.alpha;
+        accl[0] *= sm.alpha;
       }
-  }
-  __syncthreads();
-  for (int o = tid; o < G * (D + 2); o += 256) {
-    const int hh = o / (D + 2), k = o % (D + 2);
-    float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ww++) M = fmaxf(M, pw[(ww * G + hh) * (D + 2)]);
-    float v;
-    if (k == 0) {
-      v = M;
-    } else {
-      v = 0.0f;
-      if (M != -INFINITY) {
+      for (int k = 0; k < NC; k++)
+        acc[k] = mfma_fp4_32x32x64(vo.va[k], sm.p_codes, acc[k], vo.vs[k], sm.p_scale);
+      accl = mfma_fp4_32x32x64(ones, sm.p_codes, accl, ones_scale, sm.p_scale);
+
+      if (pair_end || t + 1 == t_end) {
+        dec_flush<D>(a, piece + cc.b * a.Hkv + cc.g, G, n, h, m_run, accl, acc);
+        m_run = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ww++) {
-          const float* r = pw + (ww * G + hh) * (D + 2);
-          v += fast_exp2(r[0] - M) * r[k];
+        for (int k = 0; k < NC; k++) acc[k] = v16f{};
+        accl = v16f{};
+        if (t + 1 < t_end) {
+          dec_next_pair(a, cc);
+          load_q(cc);
         }
+        // the partial stores, Q and the ring's loads in flight: the step-start
+        // wait counts only ring loads
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        shift_q();
+      } else {
+        ++cc.lt;
       }
-    }
-    a.partials[(((int64_t)b * a.Hq + g * G + hh) * a.n_parts + part) * (D + 2) + k] = v;
+    };
+    for (int t = t_beg; t < t_end; t += NS)
+      static_for<NS>([&](auto sp) {
+        if (t + decltype(sp)::value < t_end) step(sp, t + decltype(sp)::value);
+      });
   }
 }
 
-// Log-sum-exp merge of the workgroup partials: one wave per (batch, query
-// head).  Lane i owns partial i (and i + 64, ...) for the max and the
-// normaliser (wave reductions); the accumulators are combined channel-
-// parallel, eight partials per round so that eight rows are in flight.
+// Log-sum-exp merge of a pair's runs: one wave per (sequence, query head).
+// Lane i owns run i (and i + 64, ...) for the max and the normaliser (wave
+// reductions); the accumulators are combined channel-parallel, eight runs per
+// round so that eight rows are in flight.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -1015,21 +1140,30 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
   constexpr int CPL = (D + 63) / 64;  // channels per lane
-  constexpr int U = 8;                // chunks per round
+  constexpr int U = 8;                // runs per round
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);  // b * Hq + hq
   if (row >= (int64_t)a.B * a.Hq) return;
-  const int b = (int)(row / a.Hq);
-  int L = a.Sk;
-  if (a.kv_lens) L = min(max(a.kv_lens[b], 0), a.Sk);
-  const int nc = (L + kWaves * a.chunk - 1) / (kWaves * a.chunk);
-  const float* part = a.partials + row * a.n_parts * (D + 2);
+  const int b = (int)(row / a.Hq), hq = (int)(row % a.Hq);
+  const int G = a.Hq / a.Hkv, g = hq / G, hh = hq % G;
+  const DecTotals tt = dec_totals(a, b, lane);
+  const int nt = dec_tiles(dec_len(a, b));
+  const int64_t stride = (int64_t)G * (D + 4);  // between the rows of consecutive pieces
+  int nc = 0;
+  const float* part = a.partials;
+  if (nt > 0) {
+    const int pt = decode_piece_tiles(a.chunk, a.dec_waves, tt.total);
+    const int first = tt.before + g * nt;  // flattened index of the pair's first tile
+    const int j0 = first / pt;
+    nc = (first + nt - 1) / pt - j0 + 1;
+    part += ((int64_t)(j0 + b * a.Hkv + g) * G + hh) * (D + 4);
+  }
   float M = -INFINITY;
-  for (int i = lane; i < nc; i += 64) M = fmaxf(M, part[(int64_t)i * (D + 2)]);
+  for (int i = lane; i < nc; i += 64) M = fmaxf(M, part[i * stride]);
   M = wave_max(M);
   float lpart = 0.0f;
   for (int i = lane; i < nc; i += 64) {
-    const float* pr = part + (int64_t)i * (D + 2);
+    const float* pr = part + i * stride;
     lpart += fast_exp2(pr[0] - M) * pr[1];
   }
   const float lsum = M == -INFINITY ? 0.0f : wave_sum(lpart);
@@ -1041,12 +1175,12 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int i = min(i0 + u, nc - 1);
-      const float* pr = part + (int64_t)i * (D + 2);
+      const float* pr = part + i * stride;
       w[u] = (i0 + u < nc && M != -INFINITY) ? fast_exp2(pr[0] - M) : 0.0f;
 #pragma unroll
       for (int j = 0; j < CPL; j++) {
         const int ch = lane + 64 * j;
-        x[u][j] = ch < D ? pr[2 + ch] : 0.0f;
+        x[u][j] = ch < D ? pr[4 + ch] : 0.0f;
       }
     }
 #pragma unroll
@@ -1090,13 +1224,9 @@ template <int D>
 hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   if (a.Hq / a.Hkv > 32) return hipErrorNotSupported;  // one MFMA column per query head
-  const int wg_x = a.n_parts;
-  if (wg_x > 0) {
-    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3(wg_x, a.B * a.Hkv), dim3(256), 0, stream,
-                       a, kScaleOne);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(a.dec_waves), dim3(64), 0, stream, a, kScaleOne);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.B * a.Hq;
   hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3((unsigned)((rows + kWaves - 1) / kWaves)),
                      dim3(256), 0, stream, a);
@@ -1106,8 +1236,14 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 int attn_block_n(int) { return kBN; }
-int attn_default_chunk(int) { return kDecodeChunk; }
-int attn_decode_chunks_per_part() { return kWaves; }
+int attn_decode_waves(int d) {
+  switch (d) {
+    case 64: return kComputeUnits * DecRing<64>::WAVES_PER_CU;
+    case 128: return kComputeUnits * DecRing<128>::WAVES_PER_CU;
+    case 256: return kComputeUnits * DecRing<256>::WAVES_PER_CU;
+  }
+  return kComputeUnits;
+}
 
 hipError_t launch_attn_prefill_mxfp4(const AttnArgs& a, hipStream_t stream) {
   switch (a.d) {

@@ -43,17 +43,23 @@ struct AttnArgs {
   int out_fp16;
   float sm_log2;           // sm_scale * log2(e)
   float sm_scale;
-  int chunk;               // decode chunk (tokens with a fresh softmax state)
-  int n_parts;             // decode partials per query row: ceil(cap / (chunk * chunks per part))
+  int chunk;               // decode: tokens per piece given by the caller, 0 = balanced
+  int dec_waves;           // decode: waves of the persistent grid
   float tau;               // lazy-rescale threshold, log2 units (0 = every increase)
 };
 
 // Key tile width of the online-softmax frame for a head dim.
 int attn_block_n(int d);
-// Decode chunk the library picks when the caller passes 0.
-int attn_default_chunk(int d);
-// Decode chunks combined into one workspace partial (one per wave of a workgroup).
-int attn_decode_chunks_per_part();
+// Waves of the persistent decode grid for a head dim.
+int attn_decode_waves(int d);
+
+// Key tiles per decode piece: the caller's chunk (tokens, a multiple of the
+// 64-key tile), else an even share of the total over the grid's waves.
+__host__ __device__ inline int decode_piece_tiles(int chunk, int waves, int total_tiles) {
+  if (chunk > 0) return chunk / 64;
+  const int p = (total_tiles + waves - 1) / waves;
+  return p > 1 ? p : 1;
+}
 
 hipError_t launch_attn_prefill_mxfp4(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_decode_mxfp4(const AttnArgs& a, hipStream_t stream);

@@ -81,7 +81,9 @@ typedef struct hifa4_attn_params {
   int32_t kv_stride;  /* token capacity of the K/V buffers (>= Sk); 0 means Sk */
   const int32_t* kv_lens; /* device [B] per-sequence key count L (<= Sk), or NULL (L = Sk);
                              only with Sq == 1 */
-  int32_t decode_chunk;   /* split-K chunk in tokens (multiple of the key tile); 0 = library's choice */
+  int32_t decode_chunk;   /* decode piece length in tokens (a multiple of the key tile), or 0
+                             for the balanced split over the library's persistent grid
+                             (see hifa4_attn_fwd) */
   float rescale_threshold;  /* log2 units, >= 0.  A row's running max moves only when a key
                                tile's max exceeds it by more than this, so P may reach
                                2^threshold; 0 = move on every increase (P <= 1, the
@@ -120,18 +122,23 @@ HIFA4_API size_t hifa4_attn_workspace_size(const hifa4_attn_params* p);
  * MXFP4 in registers (blocks of 32 keys aligned to key 0); the normaliser
  * l = sum(P_hat) comes out of the P V MFMA through an all-ones value column
  * (P-Reordering with the fused normaliser).  The running max is updated once
- * per key tile (width from hifa4_attn_schedule).  Decode splits the keys into
- * chunks, runs each from a fresh state and merges (m, l, acc) with the
- * log-sum-exp rule.
+ * per key tile (width from hifa4_attn_schedule).
+ * Decode (Sq == 1) splits the keys and merges the runs' (m, l, acc) with the
+ * log-sum-exp rule.  The valid keys of all (sequence, KV head) pairs, pairs in
+ * order b * Hkv + g, are laid end to end as 64-key tiles (a pair has
+ * ceil(L_b / 64) tiles, the last possibly partial), T tiles in all, and cut
+ * into pieces of hifa4_attn_decode_piece_tiles(p, T) tiles: each piece runs
+ * from a fresh softmax state and restarts where it crosses into the next pair.
+ * So a fresh state starts at key t of pair s whenever t == 0 or
+ * (first_tile(s) * 64 + t) is a multiple of 64 * piece_tiles.
  * q, k, v: MX tensors from hifa4_quantize_qkv (T = Sq for q, kv_stride for k, v).
  * out: device [B][Hq][Sq][d] in out_dtype, O = acc / l (rows without any
  *      visible key are 0).
  * lse: device fp32 [B][Hq][Sq] natural-log sum-exp of the scaled scores
  *      (m + ln l; -inf for rows without a visible key), or NULL.
  * workspace: device scratch of hifa4_attn_workspace_size(p) bytes (may be NULL if 0).
- *      Decode keeps there one fp32 partial row (m, l, acc[d]) per query head
- *      and per group of four consecutive chunks (the chunks of one workgroup,
- *      already merged with each other); prefill needs none.
+ *      Decode keeps there one fp32 partial row (m, l, 2 unused, acc[d]) per
+ *      query head and per (piece, pair) run; prefill needs none.
  */
 HIFA4_API hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4_mx_tensor k,
                             hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,
@@ -148,12 +155,20 @@ HIFA4_API hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, 
                            const void* v, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* The key-tile width of the online-softmax frame (*block_n) and the split-K
- * chunk (*chunk_tokens, 0 for prefill) hifa4_attn_fwd uses for p.  P_hat
- * depends on both (and on p->rescale_threshold), so a reference
- * implementation needs them. */
+/* The key-tile width of the online-softmax frame (*block_n) and the decode
+ * piece length the caller asked for (*chunk_tokens: p->decode_chunk, 0 for
+ * the balanced split and for prefill) hifa4_attn_fwd uses for p.  P_hat
+ * depends on the frame and the split (and on p->rescale_threshold), so a
+ * reference implementation needs them. */
 HIFA4_API hifa4_status hifa4_attn_schedule(const hifa4_attn_params* p, int32_t* block_n,
                                  int32_t* chunk_tokens);
+
+/* Host query: tiles per decode piece for decode parameters p when the pairs
+ * hold total_tiles key tiles in all (sum over b of Hkv * ceil(L_b / 64)):
+ * p->decode_chunk / 64 if set, else max(1, ceil(total_tiles / W)) with W the
+ * waves of the library's persistent decode grid for p->d.  Returns 0 for
+ * invalid or prefill parameters (the error text is left unchanged). */
+HIFA4_API int32_t hifa4_attn_decode_piece_tiles(const hifa4_attn_params* p, int64_t total_tiles);
 
 /* Static text for a status code. */
 HIFA4_API const char* hifa4_status_string(hifa4_status s);

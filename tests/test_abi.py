@@ -91,17 +91,32 @@ def _attn(lib, params, ws=None, ws_bytes=0, out=0x70000000):
 def test_schedule_and_workspace_are_host_queries(lib):
     p = _params()
     bn, ch = hb.hifa4_attn_schedule(p)
-    assert bn in (32, 64, 128) and ch == 0
+    assert bn == 64 and ch == 0
     assert hb.hifa4_attn_workspace_size(p) == 0
+    assert hb.hifa4_attn_decode_piece_tiles(p, 100) == 0      # prefill: no decode schedule
+    # balanced decode: one partial row of G = 4 heads x (m, l, 2 unused, acc[128]) per
+    # (piece, pair) run, at row piece + pair: W + pairs - 1 rows for a W-wave grid
     d = _params(Sq=1, Sk=5000, kv_stride=8192)
     bn, ch = hb.hifa4_attn_schedule(d)
-    assert ch > 0 and ch % bn == 0
+    assert ch == 0
+    row_bytes = 4 * (128 + 4) * 4
     need = hb.hifa4_attn_workspace_size(d)
-    # one fp32 (m, l, acc[128]) row per query head per group of four chunks
-    assert need == 2 * 8 * (-(-8192 // (4 * ch))) * (128 + 2) * 4
+    assert need % row_bytes == 0
+    waves = need // row_bytes - 4 + 1                         # B * Hkv = 4 pairs
+    assert waves >= 256
+    for total in (0, 1, waves - 1, waves, waves + 1, 3 * waves, 79 * 4):
+        pt = hb.hifa4_attn_decode_piece_tiles(d, total)
+        assert pt == max(1, -(-total // waves))
+        assert -(-total // pt) <= waves                       # never more pieces than waves
+    # a caller's piece length: pieces of decode_chunk / 64 tiles over at most
+    # B * Hkv * ceil(Sk / 64) = 4 * 79 tiles
     d2 = _params(Sq=1, Sk=5000, decode_chunk=bn * 3)
     assert hb.hifa4_attn_schedule(d2)[1] == bn * 3
+    assert hb.hifa4_attn_decode_piece_tiles(d2, 1000) == 3
+    assert hb.hifa4_attn_workspace_size(d2) == (-(-(4 * 79) // 3) + 4 - 1) * row_bytes
+    assert hb.hifa4_attn_workspace_size(_params(Sq=1, Sk=0)) == 0   # no keys
     assert hb.hifa4_attn_workspace_size(_params(d=100)) == 0   # invalid -> 0
+    assert hb.hifa4_attn_decode_piece_tiles(_params(Sq=1, d=100), 10) == 0
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -110,6 +125,8 @@ def test_schedule_and_workspace_are_host_queries(lib):
     (dict(kv_lens=0x5000000), hb.HIFA4_ERR_UNSUPPORTED, "kv_lens"),
     (dict(decode_chunk=64), hb.HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk"),
     (dict(Sq=1, decode_chunk=100), hb.HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk"),
+    (dict(Sq=1, decode_chunk=-64), hb.HIFA4_ERR_INVALID_ARGUMENT, "decode_chunk"),
+    (dict(Sq=1, B=1 << 20, Hq=64, Hkv=64, Sk=1 << 20), hb.HIFA4_ERR_UNSUPPORTED, "too large"),
     (dict(kv_stride=64), hb.HIFA4_ERR_INVALID_ARGUMENT, "kv_stride"),
     (dict(sm_scale=float("nan")), hb.HIFA4_ERR_INVALID_ARGUMENT, "sm_scale"),
 ])

@@ -165,14 +165,35 @@ def _decode_case(cfg, lens, cap, chunk=0, tau=0.0):
     torch.cuda.synchronize()
     p = hb.make_params(B, Hq, Hkv, 1, cap, d, causal=True, kv_stride=cap, decode_chunk=chunk)
     bc, ch = hb.hifa4_attn_schedule(p)
-    return q, out.float().cpu().numpy(), lse.cpu().numpy(), bc, ch
+    assert ch == chunk
+    split = _decode_split(p, lens, Hkv)
+    return q, out.float().cpu().numpy(), lse.cpu().numpy(), bc, split
 
 
-def _decode_oracle(cfg, q, b, L, bc, chunk, tau=0.0):
+def _decode_split(p, lens, Hkv):
+    """The library's decode split as the oracle's chunk grid (include/hifa4.h):
+    pair (b, g) starts at flattened tile first = Hkv * sum(tiles before b) + g * tiles(L_b),
+    pieces are cut every pt tiles of the flattened sequence, so the pair's fresh states
+    start where (first * 64 + t) % (64 * pt) == 0, i.e. chunk 64 * pt with phase
+    64 * (first % pt)."""
+    nt = [-(-int(L) // 64) for L in lens]
+    pt = hb.hifa4_attn_decode_piece_tiles(p, Hkv * sum(nt))
+    assert pt >= 1
+    phases = np.zeros((len(lens), Hkv), np.int32)
+    first = 0
+    for b, n in enumerate(nt):
+        for g in range(Hkv):
+            phases[b, g] = 64 * (first % pt)
+            first += n
+    return 64 * pt, phases
+
+
+def _decode_oracle(cfg, q, b, L, bc, split, tau=0.0):
+    chunk, phases = split
     k, v = W.decode_kv(cfg, b, int(L))
     qq = oracle.quantize_qkv(W.to_f32(q[b:b + 1]), W.to_f32(k), W.to_f32(v), None)
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=bc, chunk=chunk,
-                           tau=tau)
+                           chunk_phase=phases[b:b + 1], tau=tau)
     vmax = np.abs(W.to_f32(v)).max()
     return ref, vmax
 
@@ -182,19 +203,44 @@ def test_decode_small_matches_oracle(chunk, tau):
     cfg = W.DecodeConfig("small_decode", 5, 8, 2, 128, 1, 700)
     lens = [700, 1, 64, 65, 333]
     print("decode parity: lens", lens, "chunk", chunk, "tau", tau, flush=True)
-    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=704, chunk=chunk, tau=tau)
-    assert ch == (chunk or ch) and ch % bc == 0
+    q, o, lse, bc, split = _decode_case(cfg, lens, cap=704, chunk=chunk, tau=tau)
     for b, L in enumerate(lens):
-        ref, vmax = _decode_oracle(cfg, q, b, L, bc, ch, tau=tau)
+        ref, vmax = _decode_oracle(cfg, q, b, L, bc, split, tau=tau)
         _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L))
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,lens,chunk", [
+    (64, 8, 8, [300, 1, 0, 129, 64], 0),          # G = 1
+    (64, 8, 2, [1, 64, 65, 130, 0, 3, 257], 1280),  # a piece spans several pairs
+    (256, 16, 2, [500, 63, 200], 0),              # G = 8
+    (256, 16, 2, [500, 63, 200], 320),            # pieces of 5 tiles straddle pairs
+    (128, 32, 1, [900, 450], 0),                  # G = 32, the whole MFMA width
+])
+def test_decode_head_dims_and_groups_match_oracle(d, Hq, Hkv, lens, chunk):
+    cfg = W.DecodeConfig("decode_d%d_g%d" % (d, Hq // Hkv), len(lens), Hq, Hkv, d, 0, max(lens))
+    cap = -(-max(lens) // 64) * 64
+    print("decode parity: d", d, "Hq", Hq, "Hkv", Hkv, "lens", lens, "chunk", chunk, flush=True)
+    q, o, lse, bc, split = _decode_case(cfg, lens, cap=cap, chunk=chunk, tau=FAST)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert not o[b].any() and np.isneginf(lse[b]).all()
+            continue
+        ref, vmax = _decode_oracle(cfg, q, b, L, bc, split, tau=FAST)
+        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode d=%d b=%d L=%d" % (d, b, L))
 
 
 def test_decode_zero_length_sequence_gives_zero_rows():
     cfg = W.DecodeConfig("zero_len", 2, 4, 1, 64, 0, 100)
-    q, o, lse, bc, ch = _decode_case(cfg, [0, 100], cap=128)
+    q, o, lse, bc, split = _decode_case(cfg, [0, 100], cap=128)
     assert not o[0].any() and np.isneginf(lse[0]).all()
-    ref, vmax = _decode_oracle(cfg, q, 1, 100, bc, ch)
+    ref, vmax = _decode_oracle(cfg, q, 1, 100, bc, split)
     _check_rows(o[1:2], lse[1:2], ref, vmax, "decode L=100 next to L=0")
+
+
+def test_decode_all_sequences_empty():
+    cfg = W.DecodeConfig("all_empty", 3, 4, 2, 128, 0, 64)
+    q, o, lse, bc, split = _decode_case(cfg, [0, 0, 0], cap=64)
+    assert not o.any() and np.isneginf(lse).all()
 
 
 def test_decode_full_size_sampled_sequences():
@@ -202,9 +248,10 @@ def test_decode_full_size_sampled_sequences():
     lens = W.decode_lengths(cfg)
     cap = int(-(-lens.max() // 64) * 64)
     print("full-size decode parity: sum(L) =", int(lens.sum()), flush=True)
-    q, o, lse, bc, ch = _decode_case(cfg, lens, cap=cap, tau=FAST)
+    q, o, lse, bc, split = _decode_case(cfg, lens, cap=cap, tau=FAST)
+    print("piece length", split[0], "keys", flush=True)
     for b in (0, int(np.argmax(lens)), int(np.argmin(lens)), 37):
-        ref, vmax = _decode_oracle(cfg, q, b, lens[b], bc, ch, tau=FAST)
+        ref, vmax = _decode_oracle(cfg, q, b, lens[b], bc, split, tau=FAST)
         _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, lens[b]))
 
 
