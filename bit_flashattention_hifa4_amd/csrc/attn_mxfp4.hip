@@ -1135,26 +1135,15 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
   }
 }
 
-// Log-sum-exp merge of a pair's runs: one wave per (sequence, query head).
-// Lane i owns run i (and i + 64, ...) for the max and the normaliser (wave
-// reductions); the accumulators are combined channel-parallel, eight runs per
-// round so that eight rows are in flight.
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
+// Log-sum-exp merge of a pair's runs: one wave per (sequence, query head),
+// lane i owning channels i, i + 64, ...  One pass over the runs, U at a time:
+// the U rows (m, l, acc) are loaded together, then folded into the running
+// (M, l, o) with the online rule, so a pair with at most U runs costs one
+// round trip to memory.
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
   constexpr int CPL = (D + 63) / 64;  // channels per lane
-  constexpr int U = 8;                // runs per round
+  constexpr int U = 16;               // runs per round
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);  // b * Hq + hq
   if (row >= (int64_t)a.B * a.Hq) return;
@@ -1172,35 +1161,40 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
     nc = (first + nt - 1) / pt - j0 + 1;
     part += ((int64_t)(j0 + b * a.Hkv + g) * G + hh) * (D + 4);
   }
-  float M = -INFINITY;
-  for (int i = lane; i < nc; i += 64) M = fmaxf(M, part[i * stride]);
-  M = wave_max(M);
-  float lpart = 0.0f;
-  for (int i = lane; i < nc; i += 64) {
-    const float* pr = part + i * stride;
-    lpart += fast_exp2(pr[0] - M) * pr[1];
-  }
-  const float lsum = M == -INFINITY ? 0.0f : wave_sum(lpart);
+  float M = -INFINITY, lsum = 0.0f;
   float o[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; j++) o[j] = 0.0f;
   for (int i0 = 0; i0 < nc; i0 += U) {
-    float w[U], x[U][CPL];
+    float mu[U], lu[U], x[U][CPL];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int i = min(i0 + u, nc - 1);
-      const float* pr = part + i * stride;
-      w[u] = (i0 + u < nc && M != -INFINITY) ? fast_exp2(pr[0] - M) : 0.0f;
+      const bool ok = i0 + u < nc;
+      const float* pr = part + (int64_t)(ok ? i0 + u : 0) * stride;
+      const float2 ml = *reinterpret_cast<const float2*>(pr);
+      mu[u] = ok ? ml.x : -INFINITY;
+      lu[u] = ml.y;
 #pragma unroll
       for (int j = 0; j < CPL; j++) {
         const int ch = lane + 64 * j;
         x[u][j] = ch < D ? pr[4 + ch] : 0.0f;
       }
     }
+    float Mn = M;
 #pragma unroll
-    for (int u = 0; u < U; u++)
+    for (int u = 0; u < U; u++) Mn = fmaxf(Mn, mu[u]);
+    const float keep = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+    lsum *= keep;
 #pragma unroll
-      for (int j = 0; j < CPL; j++) o[j] += w[u] * x[u][j];
+    for (int j = 0; j < CPL; j++) o[j] *= keep;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const float w = mu[u] == -INFINITY ? 0.0f : fast_exp2(mu[u] - Mn);
+      lsum += w * lu[u];
+#pragma unroll
+      for (int j = 0; j < CPL; j++) o[j] += w * x[u][j];
+    }
+    M = Mn;
   }
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
