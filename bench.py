@@ -140,6 +140,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the step variant with Q quantised by the quantise kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (for profiler byte-counter scaling)")
     args = ap.parse_args()
@@ -169,18 +171,32 @@ def main():
     out = torch.empty((cfg.B, cfg.Hq, cfg.S, cfg.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((cfg.B, cfg.Hq, cfg.S), dtype=torch.float32, device=dev)
     flops = cfg.flops()
-
-    def quantise():
-        hb.hifa4_quantize_qkv(q, k, v, smooth, out=mx)
-
     tau = hb.RESCALE_THRESHOLD_FAST
 
+    # The step: Smooth-QK + MXFP4 of K and V (one launch), then the attention
+    # kernel, which smooths and quantises its own Q rows in its prologue (the
+    # codes are bit-identical to quantising Q separately).
+    def quantise():
+        hb.hifa4_quantize_qkv(None, k, v, smooth, out=mx)
+
     def attend():
-        hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse, rescale_threshold=tau)
+        hb.hifa4_attn_fwd_qraw(q, smooth, mx, causal=cfg.causal, out=out, lse=lse,
+                               rescale_threshold=tau)
 
     def step():
         quantise()
         attend()
+
+    # the same step with Q quantised by the quantise kernel (reported in extra)
+    def quantise_qkv():
+        hb.hifa4_quantize_qkv(q, k, v, smooth, out=mx)
+
+    def attend_codes():
+        hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse, rescale_threshold=tau)
+
+    def step_unfused():
+        quantise_qkv()
+        attend_codes()
 
     # ---- headline: K timed steps of (quantise + attention), back to back
     settle(step, torch)
@@ -215,23 +231,49 @@ def main():
     a_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
     attn_avg = float(a_ms.mean())
     achieved = flops / (attn_avg * 1e-3) / 1e12
-    q_bytes = (cfg.B * (cfg.Hq + 2 * cfg.Hkv) * cfg.S * cfg.d) * (2 + 17 / 32) + cfg.Hkv * cfg.d * 4
+    q_bytes = (cfg.B * 2 * cfg.Hkv * cfg.S * cfg.d) * (2 + 17 / 32) + cfg.Hkv * cfg.d * 4
     log("step %.3f ms wall, %.3f ms GPU (quantise %.3f ms, attention %.3f ms): %.1f TFLOP/s step, "
         "%.1f attention" % (ms_per_step, gpu_ms_per_step, q_ms.mean(), attn_avg, value, achieved))
 
+    # ---- the unfused step (Q quantised by the quantise kernel, read back as codes)
+    unfused = {}
+    if not args.no_unfused:
+        settle(step_unfused, torch, 50.0)
+        evu = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1, e2 in evu:
+            e0.record()
+            quantise_qkv()
+            e1.record()
+            attend_codes()
+            e2.record()
+        torch.cuda.synchronize()
+        uq_ms = np.array([a.elapsed_time(b) for a, b, _ in evu])
+        ua_ms = np.array([b.elapsed_time(c) for _, b, c in evu])
+        u_ms = np.array([a.elapsed_time(c) for a, _, c in evu])
+        log("unfused step %.3f ms (quantise Q, K, V %.3f ms, attention on codes %.3f ms)"
+            % (u_ms.mean(), uq_ms.mean(), ua_ms.mean()))
+        unfused = {"unfused_step_ms_avg": float(u_ms.mean()),
+                   "unfused_quantize_qkv_ms_avg": float(uq_ms.mean()),
+                   "unfused_attention_ms_avg": float(ua_ms.mean())}
+
     extra = {
+        "step_definition": "hifa4_quantize_qkv(K, V) + hifa4_attn_fwd_qraw (Q smoothed and "
+                           "quantised in the attention prologue)",
         "step_gpu_ms": gpu_ms_per_step,
         "attention_ms_avg": attn_avg,
         "attention_ms_p10_p50_p90": [float(np.percentile(a_ms, p)) for p in (10, 50, 90)],
         "attention_tflops": achieved,
-        "quantize_ms_avg": float(q_ms.mean()),
-        "quantize_gbs": q_bytes / (q_ms.mean() * 1e-3) / 1e9,
+        "quantize_kv_ms_avg": float(q_ms.mean()),
+        "quantize_kv_gbs": q_bytes / (q_ms.mean() * 1e-3) / 1e9,
+        **unfused,
         "flops_per_step": flops,
         "kernel_source_sha256_16": kernel_source_sha(),
     }
 
     # ---- the same attention in the FlashAttention-2 frame (rescale threshold 0)
-    f0 = lambda: hb.hifa4_attn_fwd(mx, causal=cfg.causal, out=out, lse=lse, rescale_threshold=0.0)
+    f0 = lambda: hb.hifa4_attn_fwd_qraw(q, smooth, mx, causal=cfg.causal, out=out, lse=lse,
+                                        rescale_threshold=0.0)
     settle(f0, torch)
     z_ms = np.array(time_events(f0, max(5, args.steps // 2), torch))
     extra["attention_tau0_ms_avg"] = float(z_ms.mean())
@@ -282,7 +324,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "S": cfg.S, "d": cfg.d, "causal": cfg.causal, "rescale_threshold": tau,
-                   "step": "hifa4_quantize_qkv + hifa4_attn_fwd", "parallelism": "single GPU"},
+                   "step": "hifa4_quantize_qkv(K, V) + hifa4_attn_fwd_qraw",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MXFP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MXFP4_PEAK_TFLOPS,
                      "traffic": read_traffic()},

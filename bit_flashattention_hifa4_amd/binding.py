@@ -7,7 +7,7 @@ current HIP stream.  There is no CPU fallback: if the library is missing or
 the tensors are not on the GPU, the calls raise.
 
 The Python names match the C entry points: ``hifa4_quantize_qkv``,
-``hifa4_attn_fwd``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
+``hifa4_attn_fwd``, ``hifa4_attn_fwd_qraw``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
 ``hifa4_attn_decode_piece_tiles``, ``hifa4_attn_workspace_size``,
 ``hifa4_status_string``, ``hifa4_last_error``.
 """
@@ -83,6 +83,9 @@ def load_library(path: str = LIB_PATH):
     lib.hifa4_attn_fwd.restype = st
     lib.hifa4_attn_fwd.argtypes = [ctypes.POINTER(AttnParamsC), MxTensorC, MxTensorC, MxTensorC,
                                    vp, st, vp, vp, ctypes.c_size_t, vp]
+    lib.hifa4_attn_fwd_qraw.restype = st
+    lib.hifa4_attn_fwd_qraw.argtypes = [ctypes.POINTER(AttnParamsC), vp, st, vp, MxTensorC,
+                                        MxTensorC, vp, st, vp, vp, ctypes.c_size_t, vp]
     lib.bf16_attn_fwd.restype = st
     lib.bf16_attn_fwd.argtypes = [ctypes.POINTER(AttnParamsC), vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
@@ -254,6 +257,34 @@ def hifa4_attn_fwd(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,
                               _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
                               workspace.numel() if workspace is not None else 0,
                               _stream(stream)))
+    return out, lse
+
+
+def hifa4_attn_fwd_qraw(q: torch.Tensor, smooth: Optional[torch.Tensor], mx: MXQKV, *,
+                        causal: bool, sm_scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+                        lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                        rescale_threshold: float = 0.0, stream=None):
+    """Prefill with Q as bf16 / fp16 activations [B,Hq,Sq,d], smoothed and quantised inside
+    the kernel; mx holds the quantised K and V (its Q fields are not read).
+    Returns (out, lse or None)."""
+    B, Hq, Sq, d = q.shape
+    if q.dtype not in (torch.bfloat16, torch.float16) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 / fp16 tensor")
+    if (B, Hq, d) != (mx.B, mx.Hq, mx.d):
+        raise ValueError("q does not match the MX tensors")
+    if smooth is not None and (smooth.dtype != torch.float32 or tuple(smooth.shape) != (mx.Hkv, d)):
+        raise ValueError("smooth must be float32 [Hkv, d]")
+    p = make_params(B, Hq, mx.Hkv, Sq, mx.Sk, d, causal=causal, sm_scale=sm_scale,
+                    kv_stride=mx.kv_stride, rescale_threshold=rescale_threshold)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check(load_library().hifa4_attn_fwd_qraw(
+        ctypes.byref(p), _ptr(q), _dtype_code(q.dtype), _ptr(smooth),
+        MxTensorC(_ptr(mx.k_codes), _ptr(mx.k_scales)), MxTensorC(_ptr(mx.v_codes), _ptr(mx.v_scales)),
+        _ptr(out), _dtype_code(out.dtype), _ptr(lse), None, 0, _stream(stream)))
     return out, lse
 
 

@@ -114,6 +114,99 @@ size_t decode_workspace(const hifa4_attn_params* p, int chunk) {
   return (size_t)rows * (p->Hq / p->Hkv) * (p->d + 4) * sizeof(float);
 }
 
+// Shared body of hifa4_attn_fwd (q_raw == NULL: Q as MX codes) and
+// hifa4_attn_fwd_qraw (Q as bf16 / fp16 activations, quantised in the kernel).
+static hifa4_status attn_fwd_impl(const hifa4_attn_params* p, hifa4_mx_tensor q, const void* q_raw,
+                                  hifa4_dtype q_dtype, const float* smooth, hifa4_mx_tensor k,
+                                  hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int cap, chunk;
+  hifa4_status st = check_params(p, &cap, &chunk);
+  if (st != HIFA4_OK) return st;
+  if (q_raw) {
+    if (p->Sq == 1)
+      return fail(HIFA4_ERR_UNSUPPORTED, "Q from activations is supported for prefill (Sq > 1)");
+    if (q_dtype != HIFA4_BF16 && q_dtype != HIFA4_FP16)
+      return fail(HIFA4_ERR_INVALID_ARGUMENT, "q_dtype %d", (int)q_dtype);
+    // the kernel reads the Q fields only through q_raw
+    q.codes = static_cast<uint8_t*>(const_cast<void*>(q_raw));
+    q.scales = q.codes;
+  }
+  if (out_dtype != HIFA4_BF16 && out_dtype != HIFA4_FP16)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "out_dtype %d", (int)out_dtype);
+  const int d = p->d;
+  const int64_t rq = (int64_t)p->B * p->Hq * p->Sq;
+  const int64_t rcap = (int64_t)p->B * p->Hkv * cap;
+  if (rq == 0) return HIFA4_OK;
+  const void* ptrs[] = {q.codes, q.scales, k.codes, k.scales, v.codes, v.scales, out};
+  const char* names[] = {q_raw ? "q" : "q.codes", q_raw ? "q" : "q.scales", "k.codes", "k.scales",
+                         "v.codes", "v.scales", "out"};
+  for (int i = 0; i < 7; i++) {
+    if (!ptrs[i]) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+  }
+  if (lse && !aligned16(lse)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
+  if (smooth && !aligned16(smooth))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "smooth is not 16-byte aligned");
+  if (p->kv_lens && !aligned16(p->kv_lens))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_lens is not 16-byte aligned");
+  const size_t need = decode_workspace(p, chunk);
+  if (workspace_bytes < need)
+    return fail(HIFA4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
+                need);
+  if (need && !workspace) return fail(HIFA4_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (need && !aligned16(workspace))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+  const Span in[] = {{q_raw ? "q" : "q.codes", q.codes, q_raw ? rq * d * 2 : row_codes_bytes(rq, d)},
+                     {q_raw ? "smooth" : "q.scales", q_raw ? (const void*)smooth : q.scales,
+                      q_raw ? (smooth ? (int64_t)p->Hkv * d * 4 : 0) : row_scales_bytes(rq, d)},
+                     {"k.codes", k.codes, row_codes_bytes(rcap, d)},
+                     {"k.scales", k.scales, row_scales_bytes(rcap, d)},
+                     {"v.codes", v.codes, col_blocks((int64_t)p->B * p->Hkv, cap) * d * 16},
+                     {"v.scales", v.scales, col_blocks((int64_t)p->B * p->Hkv, cap) * d},
+                     {"kv_lens", p->kv_lens, p->kv_lens ? (int64_t)p->B * 4 : 0}};
+  const Span outs[] = {{"out", out, rq * d * 2},
+                       {"lse", lse, lse ? rq * 4 : 0},
+                       {"workspace", workspace, (int64_t)need}};
+  st = check_disjoint(in, 7, outs, 3);
+  if (st != HIFA4_OK) return st;
+
+  hifa4::AttnArgs a = {};
+  a.q_codes = q.codes;
+  a.q_scales = q.scales;
+  a.q_raw = static_cast<const uint16_t*>(q_raw);
+  a.smooth = q_raw ? smooth : nullptr;
+  a.q_raw_bf16 = q_dtype == HIFA4_BF16;
+  a.k_codes = k.codes;
+  a.k_scales = k.scales;
+  a.v_codes = v.codes;
+  a.v_scales = v.scales;
+  a.out = out;
+  a.lse = lse;
+  a.kv_lens = p->kv_lens;
+  a.partials = static_cast<float*>(workspace);
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.Sq = p->Sq;
+  a.Sk = p->Sk;
+  a.d = d;
+  a.cap = cap;
+  a.causal = p->causal ? 1 : 0;
+  a.out_fp16 = out_dtype == HIFA4_FP16;
+  a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)d);
+  a.sm_log2 = a.sm_scale * 1.4426950408889634f;
+  a.chunk = chunk;
+  a.dec_waves = hifa4::attn_decode_waves(d);
+  a.tau = p->rescale_threshold;
+  hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
+                            : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported)
+    return fail(HIFA4_ERR_UNSUPPORTED, "no kernel for this configuration");
+  return hip_status(e, "attention launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,75 +338,20 @@ int32_t hifa4_attn_decode_piece_tiles(const hifa4_attn_params* p, int64_t total_
 hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4_mx_tensor k,
                             hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  int cap, chunk;
-  hifa4_status st = check_params(p, &cap, &chunk);
-  if (st != HIFA4_OK) return st;
-  if (out_dtype != HIFA4_BF16 && out_dtype != HIFA4_FP16)
-    return fail(HIFA4_ERR_INVALID_ARGUMENT, "out_dtype %d", (int)out_dtype);
-  const int d = p->d;
-  const int64_t rq = (int64_t)p->B * p->Hq * p->Sq;
-  const int64_t rcap = (int64_t)p->B * p->Hkv * cap;
-  if (rq == 0) return HIFA4_OK;
-  const void* ptrs[] = {q.codes, q.scales, k.codes, k.scales, v.codes, v.scales, out};
-  const char* names[] = {"q.codes", "q.scales", "k.codes", "k.scales", "v.codes", "v.scales", "out"};
-  for (int i = 0; i < 7; i++) {
-    if (!ptrs[i]) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
-    if (!aligned16(ptrs[i])) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
-  }
-  if (lse && !aligned16(lse)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
-  if (p->kv_lens && !aligned16(p->kv_lens))
-    return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_lens is not 16-byte aligned");
-  const size_t need = decode_workspace(p, chunk);
-  if (workspace_bytes < need)
-    return fail(HIFA4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes,
-                need);
-  if (need && !workspace) return fail(HIFA4_ERR_INVALID_ARGUMENT, "workspace is NULL");
-  if (need && !aligned16(workspace))
-    return fail(HIFA4_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
-  const Span in[] = {{"q.codes", q.codes, row_codes_bytes(rq, d)},
-                     {"q.scales", q.scales, row_scales_bytes(rq, d)},
-                     {"k.codes", k.codes, row_codes_bytes(rcap, d)},
-                     {"k.scales", k.scales, row_scales_bytes(rcap, d)},
-                     {"v.codes", v.codes, col_blocks((int64_t)p->B * p->Hkv, cap) * d * 16},
-                     {"v.scales", v.scales, col_blocks((int64_t)p->B * p->Hkv, cap) * d},
-                     {"kv_lens", p->kv_lens, p->kv_lens ? (int64_t)p->B * 4 : 0}};
-  const Span outs[] = {{"out", out, rq * d * 2},
-                       {"lse", lse, lse ? rq * 4 : 0},
-                       {"workspace", workspace, (int64_t)need}};
-  st = check_disjoint(in, 7, outs, 3);
-  if (st != HIFA4_OK) return st;
+  return attn_fwd_impl(p, q, nullptr, HIFA4_BF16, nullptr, k, v, out, out_dtype, lse, workspace,
+                       workspace_bytes, stream);
+}
 
-  hifa4::AttnArgs a = {};
-  a.q_codes = q.codes;
-  a.q_scales = q.scales;
-  a.k_codes = k.codes;
-  a.k_scales = k.scales;
-  a.v_codes = v.codes;
-  a.v_scales = v.scales;
-  a.out = out;
-  a.lse = lse;
-  a.kv_lens = p->kv_lens;
-  a.partials = static_cast<float*>(workspace);
-  a.B = p->B;
-  a.Hq = p->Hq;
-  a.Hkv = p->Hkv;
-  a.Sq = p->Sq;
-  a.Sk = p->Sk;
-  a.d = d;
-  a.cap = cap;
-  a.causal = p->causal ? 1 : 0;
-  a.out_fp16 = out_dtype == HIFA4_FP16;
-  a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)d);
-  a.sm_log2 = a.sm_scale * 1.4426950408889634f;
-  a.chunk = chunk;
-  a.dec_waves = hifa4::attn_decode_waves(d);
-  a.tau = p->rescale_threshold;
-  hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
-                            : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);
-  if (e == hipErrorNotSupported)
-    return fail(HIFA4_ERR_UNSUPPORTED, "no kernel for this configuration");
-  return hip_status(e, "attention launch");
+hifa4_status hifa4_attn_fwd_qraw(const hifa4_attn_params* p, const void* q, hifa4_dtype q_dtype,
+                                 const float* smooth, hifa4_mx_tensor k, hifa4_mx_tensor v,
+                                 void* out, hifa4_dtype out_dtype, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!q) {
+    g_last_error.clear();
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "q is NULL");
+  }
+  return attn_fwd_impl(p, hifa4_mx_tensor{nullptr, nullptr}, q, q_dtype, smooth, k, v, out,
+                       out_dtype, lse, workspace, workspace_bytes, stream);
 }
 
 hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void* k,

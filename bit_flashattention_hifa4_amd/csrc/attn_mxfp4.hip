@@ -517,6 +517,64 @@ __device__ __forceinline__ void v_load(const uint8_t* vbuf, int n, int h, VOps<D
 template <int D>
 constexpr int prefill_min_blocks() { return D >= 256 ? 1 : 2; }  // also used by decode
 
+// Smooth-QK (Q * s in fp32) and MXFP4 of the lane's blocks 2j + h (j < D/64)
+// of query row `row`, from the bf16 / fp16 activations: the same arithmetic as
+// the quantise kernel (products, exact block max, E8M0 exponent, packed
+// convert), so the codes are bit-identical.  The scale byte of block 2j + h
+// goes to byte h + 2 (j % 2) of word j / 2, the quantise kernel's row layout
+// as the lane reads it.
+template <int D, bool kBf16>
+__device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, int hs, int h,
+                                                uint4 (&qa)[D / 64],
+                                                uint32_t (&qsw_raw)[(D / 64 + 1) / 2]) {
+  constexpr int NJ = D / 64;
+#pragma unroll
+  for (int j = 0; j < (NJ + 1) / 2; j++) qsw_raw[j] = 0;
+  const uint16_t* src = a.q_raw + row * D;
+  const float* sm = a.smooth ? a.smooth + (int64_t)hs * D : nullptr;
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
+    const int kb = 2 * j + h;  // 32-element block along d
+    const uint4* p = reinterpret_cast<const uint4*>(src + 32 * kb);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint4 w = p[i];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        v[8 * i + 2 * e] = elem<kBf16>(ws[e] & 0xFFFFu);
+        v[8 * i + 2 * e + 1] = elem<kBf16>(ws[e] >> 16);
+      }
+    }
+    if (sm != nullptr) {
+      const float4* sp = reinterpret_cast<const float4*>(sm + 32 * kb);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float4 f = sp[i];
+        v[4 * i] = v[4 * i] * f.x;
+        v[4 * i + 1] = v[4 * i + 1] * f.y;
+        v[4 * i + 2] = v[4 * i + 2] * f.z;
+        v[4 * i + 3] = v[4 * i + 3] * f.w;
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
+    const uint32_t sb = e8m0_from_amax(amax);
+    const float scale = e8m0_to_float(sb);
+    uint32_t wd[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const float e8[8] = {v[8 * q4], v[8 * q4 + 1], v[8 * q4 + 2], v[8 * q4 + 3],
+                           v[8 * q4 + 4], v[8 * q4 + 5], v[8 * q4 + 6], v[8 * q4 + 7]};
+      wd[q4] = encode8(e8, scale);
+    }
+    qa[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    qsw_raw[j / 2] |= sb << (8 * (h + 2 * (j % 2)));
+  }
+}
+
 template <int D, bool kCausal>
 __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_kernel(
     AttnArgs a, int ones_scale) {
@@ -592,7 +650,13 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // here, shifted for the lane's half once the loads have landed).
   uint4 qa[NJ];
   uint32_t qsw_raw[(NJ + 1) / 2];
-  if (q < a.Sq) {
+  if (q < a.Sq && a.q_raw) {
+    // Q from the activations: smoothed and quantised here
+    if (a.q_raw_bf16)
+      quantise_q_lane<D, true>(a, bhq * a.Sq + q, g, h, qa, qsw_raw);
+    else
+      quantise_q_lane<D, false>(a, bhq * a.Sq + q, g, h, qa, qsw_raw);
+  } else if (q < a.Sq) {
     const uint8_t* qc = a.q_codes + (bhq * a.Sq + q) * DB;
     const uint8_t* qsc = a.q_scales + (bhq * a.Sq + q) * DS;
 #pragma unroll

@@ -65,4 +65,26 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
   return (uint32_t)__half_as_ushort(__float2half_rn(f));
 }
 
+// Exact fp32 value of a bf16 (kBf16) or fp16 element.
+template <bool kBf16>
+__device__ __forceinline__ float elem(uint32_t bits16) {
+  if constexpr (kBf16) {
+    return bf16_bits_to_float(bits16);
+  } else {
+    return __half2float(__ushort_as_half((unsigned short)bits16));
+  }
+}
+
+// 8 elements -> 4 E2M1 code bytes (element 2i in the low nibble of byte i):
+// the gfx950 packed convert divides by the power-of-two scale, rounds to
+// nearest even and saturates at +-6.
+__device__ __forceinline__ uint32_t encode8(const float (&v)[8], float scale) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+  return w;
+}
+
 }  // namespace hifa4

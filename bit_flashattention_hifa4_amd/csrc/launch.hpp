@@ -36,6 +36,9 @@ struct AttnArgs {
   const uint8_t* v_scales;
   void* out;
   float* lse;
+  const uint16_t* q_raw;   // prefill: bf16 / fp16 Q quantised in the kernel (q_codes unused), or null
+  const float* smooth;     // with q_raw: Smooth-QK factors [Hkv][d], or null (s = 1)
+  int q_raw_bf16;          // with q_raw: 1 = bf16, 0 = fp16
   const int32_t* kv_lens;  // decode only, may be null
   float* partials;         // decode workspace
   int B, Hq, Hkv, Sq, Sk, d, cap;

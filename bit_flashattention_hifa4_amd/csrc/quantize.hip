@@ -37,28 +37,11 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool kBf16>
-__device__ __forceinline__ float elem(uint32_t bits16) {
-  if constexpr (kBf16) {
-    return bf16_bits_to_float(bits16);
-  } else {
-    return __half2float(__ushort_as_half((unsigned short)bits16));
-  }
-}
 
 // Value of the lane selected by a DPP quad_perm control within each quad.
 #define quad_xor(x, ctrl)                                                               \
   __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), (ctrl), 0xF, 0xF, false))
 
-// 8 elements -> 4 code bytes (element 2i in the low nibble of byte i).
-__device__ __forceinline__ uint32_t encode8(const float (&v)[8], float scale) {
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
-  return w;
-}
 
 // Row blocks (blocks of 32 along the head dim): four lanes share a block,
 // lane `lane4` handling elements 8*lane4 .. 8*lane4+7.  A lane processes

@@ -145,6 +145,23 @@ HIFA4_API hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tenso
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hifa4_attn_fwd for prefill (Sq > 1) with Q given as activations: q is device
+ * [B][Hq][Sq][d] in q_dtype (bf16 or fp16, contiguous, 16-byte aligned) and
+ * smooth the same Smooth-QK factors hifa4_quantize_qkv takes (device fp32
+ * [Hkv][d], or NULL for s = 1).  Each workgroup smooths and quantises its own
+ * query rows to MXFP4 in registers with the arithmetic of hifa4_quantize_qkv
+ * (Abstract, Smooth-QK), so the codes, and the output, are bit-identical to
+ * hifa4_quantize_qkv followed by hifa4_attn_fwd; the caller quantises only K
+ * and V, and Q is read once instead of being quantised, written and read
+ * back.  Other arguments, layouts and errors as for hifa4_attn_fwd; Sq == 1
+ * returns HIFA4_ERR_UNSUPPORTED.
+ */
+HIFA4_API hifa4_status hifa4_attn_fwd_qraw(const hifa4_attn_params* p, const void* q,
+                                 hifa4_dtype q_dtype, const float* smooth, hifa4_mx_tensor k,
+                                 hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * bf16 FlashAttention forward, the accuracy and latency baseline the pages
  * compare against (Abstract): bf16 MFMA products, fp32 softmax state, no
  * quantisation and no smoothing.  q [B][Hq][Sq][d], k / v [B][Hkv][kv_stride][d]

@@ -146,6 +146,23 @@ def test_attn_workspace_and_pointer_checks(lib):
                               hb.HIFA4_BF16, None, None, 0, None) == hb.HIFA4_ERR_INVALID_ARGUMENT
 
 
+def test_attn_qraw_validation(lib):
+    def call(params, q=0x10000000, q_dtype=hb.HIFA4_BF16, smooth=None):
+        return lib.hifa4_attn_fwd_qraw(ctypes.byref(params), q, q_dtype, smooth, _mx(0x20000000),
+                                       _mx(0x30000000), 0x70000000, hb.HIFA4_BF16, None, None, 0,
+                                       None)
+    assert call(_params(), q=None) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "q is NULL" in hb.hifa4_last_error()
+    assert call(_params(Sq=1)) == hb.HIFA4_ERR_UNSUPPORTED
+    assert "prefill" in hb.hifa4_last_error()
+    assert call(_params(), q_dtype=7) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert call(_params(), q=0x10000004) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "not 16-byte aligned" in hb.hifa4_last_error()
+    assert call(_params(), smooth=0x40000004) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "smooth" in hb.hifa4_last_error()
+    assert call(_params(d=32)) == hb.HIFA4_ERR_UNSUPPORTED
+
+
 def test_bf16_path_rejects_bad_arguments(lib):
     p = _params()
     assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x10, None, None,

@@ -275,3 +275,39 @@ def test_bf16_baseline_matches_exact_attention(case, tau):
     lerr = np.abs(lse.cpu().numpy()[fin] - ref["lse"][fin]).max()
     print("bf16 %s: max|O - exact| = %.4g (bound %.4g), lse %.3g" % (case, err, BF16_TOL * vmax, lerr))
     assert err <= BF16_TOL * vmax and lerr < 1e-2
+
+
+@pytest.mark.parametrize("case", SMALL + [(1, 32, 8, 640, 640, 128, True, "bf16", True, 0)],
+                         ids=lambda c: "x".join(str(v) for v in c))
+def test_prefill_with_q_from_activations_is_bit_identical(case):
+    """hifa4_attn_fwd_qraw quantises Q inside the kernel with the arithmetic of
+    hifa4_quantize_qkv, so it must reproduce quantise-then-attend bit for bit."""
+    B, Hq, Hkv, Sq, Sk, d, causal, dt, sm, stride = case
+    print("Q-from-activations parity:", case, flush=True)
+    inp = W.random_case(B, Hq, Hkv, Sq, Sk, d, dtype=dt, seed=3 + sum(case[:6]), rope_theta=1e4,
+                        n_outliers=2, smooth_alpha=0.5 if sm else None)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    s = torch.from_numpy(inp["smooth"]).cuda() if inp["smooth"] is not None else None
+    out_dt = torch.float16 if dt == "fp16" else torch.bfloat16
+    for tau in (0.0, FAST):
+        mx = hb.hifa4_quantize_qkv(q, k, v, s, kv_stride=stride)
+        o_ref, l_ref = hb.hifa4_attn_fwd(mx, causal=causal, out_dtype=out_dt, rescale_threshold=tau)
+        mkv = hb.alloc_mx(B, Hq, Hkv, Sq, stride or Sk, d)
+        hb.hifa4_quantize_qkv(None, k, v, s, kv_stride=stride, out=mkv)
+        o, l = hb.hifa4_attn_fwd_qraw(q, s, mkv, causal=causal, out_dtype=out_dt, rescale_threshold=tau)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(l, l_ref), "tau %g" % tau
+
+
+def test_prefill_with_q_from_activations_full_size():
+    cfg = W.QWEN3_8B
+    inp = W.prefill_inputs(cfg)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    s = torch.from_numpy(inp["smooth"]).cuda()
+    mx = hb.hifa4_quantize_qkv(q, k, v, s)
+    o_ref, l_ref = hb.hifa4_attn_fwd(mx, causal=True, rescale_threshold=FAST)
+    mkv = hb.alloc_mx(cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.S, cfg.d)
+    hb.hifa4_quantize_qkv(None, k, v, s, out=mkv)
+    o, l = hb.hifa4_attn_fwd_qraw(q, s, mkv, causal=True, rescale_threshold=FAST)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
