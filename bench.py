@@ -281,6 +281,17 @@ def main():
     log("attention with rescale threshold 0: %.3f ms (%.1f TFLOP/s)"
         % (z_ms.mean(), extra["attention_tau0_tflops"]))
 
+    # ---- the pages' ablation: the same attention with the non-reordered normaliser
+    #      (l summed from the fp32 P on the vector ALU, no ones column)
+    fd = lambda: hb.hifa4_attn_fwd_qraw(q, smooth, mx, causal=cfg.causal, out=out, lse=lse,
+                                        rescale_threshold=tau, normaliser=hb.NORMALISER_DIRECT)
+    settle(fd, torch)
+    d_ms = np.array(time_events(fd, max(5, args.steps // 2), torch))
+    extra["attention_direct_normaliser_ms_avg"] = float(d_ms.mean())
+    extra["p_reordering_over_direct_latency_ratio"] = attn_avg / float(d_ms.mean())
+    log("attention with the direct normaliser: %.3f ms (P-Reordering / direct latency %.3f)"
+        % (d_ms.mean(), extra["p_reordering_over_direct_latency_ratio"]))
+
     # ---- bf16 FlashAttention baseline on the same inputs
     if not args.no_bf16:
         bout = torch.empty_like(out)

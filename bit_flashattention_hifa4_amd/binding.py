@@ -56,7 +56,11 @@ class AttnParamsC(ctypes.Structure):
         ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float),
         ("kv_stride", ctypes.c_int32), ("kv_lens", ctypes.c_void_p),
         ("decode_chunk", ctypes.c_int32), ("rescale_threshold", ctypes.c_float),
+        ("normaliser", ctypes.c_int32),
     ]
+
+NORMALISER_P_REORDERING = 0   # l = sum(P_hat) through the ones column (the method)
+NORMALISER_DIRECT = 1         # l = sum(P) in fp32 on the vector ALU (the pages' comparison)
 
 
 _lib = None
@@ -208,11 +212,11 @@ def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
 
 
 def make_params(B, Hq, Hkv, Sq, Sk, d, *, causal, sm_scale=None, kv_stride=0, kv_lens=None,
-                decode_chunk=0, rescale_threshold=0.0) -> AttnParamsC:
+                decode_chunk=0, rescale_threshold=0.0, normaliser=0) -> AttnParamsC:
     return AttnParamsC(B, Hq, Hkv, Sq, Sk, d, 1 if causal else 0,
                        float(sm_scale) if sm_scale else 0.0, kv_stride,
                        _ptr(kv_lens) if kv_lens is not None else None, decode_chunk,
-                       float(rescale_threshold))
+                       float(rescale_threshold), int(normaliser))
 
 
 def hifa4_attn_workspace_size(params: AttnParamsC) -> int:
@@ -235,13 +239,13 @@ def hifa4_attn_fwd(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,
                    out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                    lse: Optional[torch.Tensor] = None, want_lse: bool = True,
                    workspace: Optional[torch.Tensor] = None, rescale_threshold: float = 0.0,
-                   stream=None):
+                   normaliser: int = 0, stream=None):
     """Fused MXFP4 attention on quantised operands; returns (out, lse or None)."""
     if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != mx.B):
         raise ValueError("kv_lens must be int32 [B]")
     p = make_params(mx.B, mx.Hq, mx.Hkv, mx.Sq, mx.Sk, mx.d, causal=causal, sm_scale=sm_scale,
                     kv_stride=mx.kv_stride, kv_lens=kv_lens, decode_chunk=decode_chunk,
-                    rescale_threshold=rescale_threshold)
+                    rescale_threshold=rescale_threshold, normaliser=normaliser)
     dev = mx.q_codes.device
     if out is None:
         out = torch.empty((mx.B, mx.Hq, mx.Sq, mx.d), dtype=out_dtype, device=dev)
@@ -264,7 +268,7 @@ def hifa4_attn_fwd_qraw(q: torch.Tensor, smooth: Optional[torch.Tensor], mx: MXQ
                         causal: bool, sm_scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                         lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                        rescale_threshold: float = 0.0, stream=None):
+                        rescale_threshold: float = 0.0, normaliser: int = 0, stream=None):
     """Prefill with Q as bf16 / fp16 activations [B,Hq,Sq,d], smoothed and quantised inside
     the kernel; mx holds the quantised K and V (its Q fields are not read).
     Returns (out, lse or None)."""
@@ -276,7 +280,8 @@ def hifa4_attn_fwd_qraw(q: torch.Tensor, smooth: Optional[torch.Tensor], mx: MXQ
     if smooth is not None and (smooth.dtype != torch.float32 or tuple(smooth.shape) != (mx.Hkv, d)):
         raise ValueError("smooth must be float32 [Hkv, d]")
     p = make_params(B, Hq, mx.Hkv, Sq, mx.Sk, d, causal=causal, sm_scale=sm_scale,
-                    kv_stride=mx.kv_stride, rescale_threshold=rescale_threshold)
+                    kv_stride=mx.kv_stride, rescale_threshold=rescale_threshold,
+                    normaliser=normaliser)
     if out is None:
         out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:

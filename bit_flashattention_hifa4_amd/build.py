@@ -41,6 +41,11 @@ def flags() -> list[str]:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # IEEE fp32 division (the key smoothing divides)
         "-fhip-fp32-correctly-rounded-divide-sqrt",
+        # Branch targets that are never fallen into start on a 16-byte boundary.
+        # Without it the prefill loop's speed depended on where the loop
+        # happened to start (measured: 69 or 81 us for the same instructions,
+        # alternating with each 4-byte shift of the code before the loop).
+        "-mllvm", "-align-all-nofallthru-blocks=4",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
     ]

@@ -79,6 +79,9 @@ hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
   if (!std::isfinite(p->rescale_threshold) || p->rescale_threshold < 0.0f)
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "rescale_threshold must be finite and >= 0");
+  if (p->normaliser != 0 && p->normaliser != 1)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "normaliser %d (0: P-Reordering, 1: direct)",
+                p->normaliser);
   *cap = p->kv_stride ? p->kv_stride : p->Sk;
   if (*cap < p->Sk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_stride %d < Sk %d", *cap, p->Sk);
   if (p->kv_lens && p->Sq != 1)
@@ -200,6 +203,7 @@ static hifa4_status attn_fwd_impl(const hifa4_attn_params* p, hifa4_mx_tensor q,
   a.chunk = chunk;
   a.dec_waves = hifa4::attn_decode_waves(d);
   a.tau = p->rescale_threshold;
+  a.direct_l = p->normaliser;
   hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
                             : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported)
@@ -363,6 +367,8 @@ hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void
   int cap, chunk;
   if (p && p->kv_lens) return fail(HIFA4_ERR_UNSUPPORTED, "bf16_attn_fwd takes no kv_lens");
   if (p && p->decode_chunk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "bf16_attn_fwd takes no decode_chunk");
+  if (p && p->normaliser)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "bf16_attn_fwd has no normaliser variant");
   hifa4_attn_params pp;
   if (p) {
     pp = *p;

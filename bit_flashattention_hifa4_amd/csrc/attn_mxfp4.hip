@@ -101,6 +101,22 @@ __device__ __forceinline__ float max_with_half_swap(float x) {
   return fmax_(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Non-reordered normaliser: the sum of the row's fp32 P over the 64 keys of a
+// step (the lane's 32 in the two accumulators after the exponentials, plus the
+// partner lane's 32), as a tree of adds.
+__device__ __forceinline__ float row_sum_p(const v16f& p0, const v16f& p1) {
+  float t[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) t[r] = p0[r] + p1[r];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int r = 0; r < w; r++) t[r] = t[r] + t[r + w];
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[0]), __float_as_uint(t[0]),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Softmax on the lane's 32 scores held in the two QK accumulators (tile t,
 // register r <-> key 32h + 16t + r), in place: the scores are replaced by P
 // before packing, so no copies of the accumulators are made.  Masked scores
@@ -575,7 +591,7 @@ __device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, 
   }
 }
 
-template <int D, bool kCausal>
+template <int D, bool kCausal, bool kDirect>
 __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_kernel(
     AttnArgs a, int ones_scale) {
   using T = PrefillTile<D>;
@@ -708,8 +724,10 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   auto pv_mfma = [&](const VOps<D>& vo, const uint4& p, int ps) {
 #pragma unroll
     for (int cc = 0; cc < NC; cc++) acc[cc] = mfma_fp4_32x32x64(vo.va[cc], p, acc[cc], vo.vs[cc], ps);
-    accl = mfma_fp4_32x32x64(ones, p, accl, ones_scale, ps);
+    if constexpr (!kDirect) accl = mfma_fp4_32x32x64(ones, p, accl, ones_scale, ps);
   };
+  // non-reordered normaliser (the sum of the fp32 P), in the running frame
+  float l_direct = 0.0f;
 
   // One pipeline step on tile kt, RP = kt mod 4 (ring slot, a compile-time
   // constant: every LDS address is a per-lane base plus an immediate).
@@ -755,8 +773,9 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     qk_mfma<D>(ko, qa, qsw, n0r, n1r);
     pv_mfma(vo, pend_p, pend_s);
     SoftmaxStep st = softmax_exp(c0, c1, sx, c, pk);
+    if constexpr (kDirect) l_direct = __builtin_fmaf(l_direct, st.alpha, row_sum_p(c0, c1));
 #pragma unroll
-    for (int i = 0; i < NJ * 2 + NC + 1; i++) {
+    for (int i = 0; i < NJ * 2 + NC + (kDirect ? 0 : 1); i++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // then ten VALU
     }
@@ -811,7 +830,7 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   HIFA4_WAIT_VMCNT(0);
 
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
-  const float lsum = __shfl(accl[0], n);
+  const float lsum = kDirect ? l_direct : __shfl(accl[0], n);
   if (q < a.Sq) {
     const int64_t row = bhq * a.Sq + q;
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
@@ -1024,9 +1043,8 @@ constexpr int kComputeUnits = 256;  // MI355X
 // Partial row of one query head: m (log2 units), l, two unused floats, acc[d].
 template <int D>
 __device__ __forceinline__ void dec_flush(const AttnArgs& a, int prow, int G, int n, int h,
-                                          float m_run, const v16f& accl, const v16f* acc) {
+                                          float m_run, float lsum, const v16f* acc) {
   constexpr int NC = D / 32;
-  const float lsum = __shfl(accl[0], n);
   if (n < G) {
     float* row = a.partials + ((int64_t)prow * G + n) * (D + 4);
     if (h == 0) {
@@ -1053,7 +1071,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int D>
+template <int D, bool kDirect>
 __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_kernel(AttnArgs a,
                                                                               int ones_scale) {
   using T = PrefillTile<D>;
@@ -1140,6 +1158,7 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
     shift_q();
 
     float m_run = -INFINITY;
+    float l_direct = 0.0f;  // non-reordered normaliser (sum of the fp32 P)
     v16f acc[NC];
 #pragma unroll
     for (int k = 0; k < NC; k++) acc[k] = v16f{};
@@ -1164,6 +1183,7 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
       const bool pair_end = cc.lt + 1 == cc.nt;
       if (pair_end && (cc.L & (kBN - 1))) mask_scores(s_lo, s_hi, cc.lt * kBN + 32 * h, cc.L);
       const SoftmaxStep sm = softmax_step(s_lo, s_hi, m_run, c, a.tau, pk);
+      if constexpr (kDirect) l_direct = __builtin_fmaf(l_direct, sm.alpha, row_sum_p(s_lo, s_hi));
       if (__any(sm.alpha != 1.0f)) {
 #pragma unroll
         for (int k = 0; k < NC; k++) acc[k] *= sm.alpha;
@@ -1172,11 +1192,14 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
 #pragma unroll
       for (int k = 0; k < NC; k++)
         acc[k] = mfma_fp4_32x32x64(vo.va[k], sm.p_codes, acc[k], vo.vs[k], sm.p_scale);
-      accl = mfma_fp4_32x32x64(ones, sm.p_codes, accl, ones_scale, sm.p_scale);
+      if constexpr (!kDirect)
+        accl = mfma_fp4_32x32x64(ones, sm.p_codes, accl, ones_scale, sm.p_scale);
 
       if (pair_end || t + 1 == t_end) {
-        dec_flush<D>(a, piece + cc.b * a.Hkv + cc.g, G, n, h, m_run, accl, acc);
+        dec_flush<D>(a, piece + cc.b * a.Hkv + cc.g, G, n, h, m_run,
+                     kDirect ? l_direct : __shfl(accl[0], n), acc);
         m_run = -INFINITY;
+        l_direct = 0.0f;
 #pragma unroll
         for (int k = 0; k < NC; k++) acc[k] = v16f{};
         accl = v16f{};
@@ -1283,12 +1306,15 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)n_qt * a.B * a.Hq;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (a.causal)
-    hipLaunchKernelGGL((attn_prefill_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       a, kScaleOne);
+  const dim3 g((unsigned)grid), b(256);
+  if (a.causal && !a.direct_l)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, true, false>), g, b, 0, stream, a, kScaleOne);
+  else if (!a.direct_l)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, false, false>), g, b, 0, stream, a, kScaleOne);
+  else if (a.causal)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, true, true>), g, b, 0, stream, a, kScaleOne);
   else
-    hipLaunchKernelGGL((attn_prefill_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       a, kScaleOne);
+    hipLaunchKernelGGL((attn_prefill_kernel<D, false, true>), g, b, 0, stream, a, kScaleOne);
   return hipGetLastError();
 }
 
@@ -1296,7 +1322,12 @@ template <int D>
 hipError_t launch_decode_d(const AttnArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   if (a.Hq / a.Hkv > 32) return hipErrorNotSupported;  // one MFMA column per query head
-  hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(a.dec_waves), dim3(64), 0, stream, a, kScaleOne);
+  if (a.direct_l)
+    hipLaunchKernelGGL((attn_decode_kernel<D, true>), dim3(a.dec_waves), dim3(64), 0, stream, a,
+                       kScaleOne);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<D, false>), dim3(a.dec_waves), dim3(64), 0, stream, a,
+                       kScaleOne);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.B * a.Hq;

@@ -49,6 +49,7 @@ struct AttnArgs {
   int chunk;               // decode: tokens per piece given by the caller, 0 = balanced
   int dec_waves;           // decode: waves of the persistent grid
   float tau;               // lazy-rescale threshold, log2 units (0 = every increase)
+  int direct_l;            // 1: l = sum of the fp32 P (vector ALU), 0: P-Reordering
 };
 
 // Key tile width of the online-softmax frame for a head dim.

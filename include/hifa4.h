@@ -89,6 +89,13 @@ typedef struct hifa4_attn_params {
                                2^threshold; 0 = move on every increase (P <= 1, the
                                FlashAttention-2 frame).  Exact attention is the same for any
                                value; P_hat (and so the MXFP4 result) depends on it. */
+  int32_t normaliser;       /* 0: P-Reordering, the method (Abstract, P-Reordering): the
+                               normaliser l = sum(P_hat) of the same 4-bit P_hat as the
+                               numerator, from the P V MFMA through an all-ones value
+                               column.  1: the non-reordered form the pages compare it
+                               with: l = sum(P) of the fp32 P before quantisation, summed
+                               on the vector ALU, numerator still P_hat V.  Must be 0 for
+                               bf16_attn_fwd. */
 } hifa4_attn_params;
 
 /*

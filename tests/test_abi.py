@@ -72,12 +72,12 @@ def test_quantize_rejects_bad_arguments(lib, kw, status, msg):
 
 def _params(**kw):
     p = dict(B=2, Hq=8, Hkv=2, Sq=128, Sk=128, d=128, causal=True, sm_scale=None, kv_stride=0,
-             kv_lens=None, decode_chunk=0)
+             kv_lens=None, decode_chunk=0, normaliser=0)
     p.update(kw)
     lens = p.pop("kv_lens")
     params = hb.make_params(**{k: p[k] for k in ("B", "Hq", "Hkv", "Sq", "Sk", "d")},
                             causal=p["causal"], sm_scale=p["sm_scale"], kv_stride=p["kv_stride"],
-                            decode_chunk=p["decode_chunk"])
+                            decode_chunk=p["decode_chunk"], normaliser=p["normaliser"])
     if lens is not None:
         params.kv_lens = lens
     return params
@@ -129,6 +129,7 @@ def test_schedule_and_workspace_are_host_queries(lib):
     (dict(Sq=1, B=1 << 20, Hq=64, Hkv=64, Sk=1 << 20), hb.HIFA4_ERR_UNSUPPORTED, "too large"),
     (dict(kv_stride=64), hb.HIFA4_ERR_INVALID_ARGUMENT, "kv_stride"),
     (dict(sm_scale=float("nan")), hb.HIFA4_ERR_INVALID_ARGUMENT, "sm_scale"),
+    (dict(normaliser=2), hb.HIFA4_ERR_INVALID_ARGUMENT, "normaliser"),
 ])
 def test_attn_rejects_bad_params(lib, kw, status, msg):
     assert _attn(lib, _params(**kw)) == status
@@ -173,6 +174,10 @@ def test_bf16_path_rejects_bad_arguments(lib):
     p = _params(d=48)
     assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x3000000, None,
                              None, 0, None) == hb.HIFA4_ERR_UNSUPPORTED
+    p = _params(normaliser=1)
+    assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x3000000, None,
+                             None, 0, None) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "normaliser" in hb.hifa4_last_error()
 
 
 def test_status_strings(lib):

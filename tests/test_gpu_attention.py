@@ -311,3 +311,91 @@ def test_prefill_with_q_from_activations_full_size():
     o, l = hb.hifa4_attn_fwd_qraw(q, s, mkv, causal=True, rescale_threshold=FAST)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
+
+
+def _check_rows_direct(o_gpu, lse_gpu, ref, vmax, what):
+    """The non-reordered variant against the oracle's o_naive / l_naive."""
+    fin = np.isfinite(ref["lse"])
+    lse_naive = np.where(fin, ref["lse"] - np.log(np.where(fin, ref["l"], 1.0))
+                         + np.log(np.where(fin, ref["l_naive"], 1.0)), -np.inf)
+    _check_rows(o_gpu, lse_gpu, dict(o=ref["o_naive"], lse=lse_naive), vmax, what + " (direct l)")
+
+
+@pytest.mark.parametrize("tau", [0.0, FAST])
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[2], SMALL[4], SMALL[5]],
+                         ids=lambda c: "x".join(str(v) for v in c))
+def test_prefill_direct_normaliser_matches_oracle(case, tau):
+    """normaliser = 1: l is the sum of the fp32 P (the pages' non-reordered form), the
+    numerator still P_hat V; the oracle's o_naive is that quantity."""
+    B, Hq, Hkv, Sq, Sk, d, causal, dt, sm, stride = case
+    print("direct-normaliser prefill parity:", case, "tau", tau, flush=True)
+    inp = W.random_case(B, Hq, Hkv, Sq, Sk, d, dtype=dt, seed=sum(case[:6]), rope_theta=1e4,
+                        n_outliers=2, smooth_alpha=0.5 if sm else None)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    s = torch.from_numpy(inp["smooth"]).cuda() if inp["smooth"] is not None else None
+    out_dt = torch.float16 if dt == "fp16" else torch.bfloat16
+    mx = hb.hifa4_quantize_qkv(q, k, v, s, kv_stride=stride)
+    out, lse = hb.hifa4_attn_fwd(mx, causal=causal, out_dtype=out_dt, rescale_threshold=tau,
+                                 normaliser=hb.NORMALISER_DIRECT)
+    torch.cuda.synchronize()
+    qq = _oracle_quant(inp)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=64,
+                           quant_p=True, tau=tau)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    _check_rows_direct(out.float().cpu().numpy(), lse.cpu().numpy(), ref, vmax, "case %s" % (case,))
+
+
+@pytest.mark.parametrize("chunk", [0, 192])
+def test_decode_direct_normaliser_matches_oracle(chunk):
+    cfg = W.DecodeConfig("small_decode", 5, 8, 2, 128, 1, 700)
+    lens = [700, 1, 64, 65, 333]
+    B, Hq, Hkv, d, cap = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, 704
+    print("direct-normaliser decode parity: chunk", chunk, flush=True)
+    mx = hb.alloc_mx(B, Hq, Hkv, 1, cap, d)
+    q = W.decode_q(cfg)
+    hb.hifa4_quantize_qkv(q.cuda(), None, None, None, out=mx)
+    for b, L in enumerate(lens):
+        kk, vv = W.decode_kv(cfg, b, int(L))
+        sl = hb.MXQKV(None, None, mx.k_codes[b:b + 1], mx.k_scales[b:b + 1], mx.v_codes[b:b + 1],
+                      mx.v_scales[b:b + 1], 1, Hq, Hkv, 0, int(L), d, cap)
+        hb.hifa4_quantize_qkv(None, kk.cuda(), vv.cuda(), None, kv_stride=cap, out=sl)
+    mx.Sq, mx.Sk, mx.kv_stride = 1, cap, cap
+    lens_t = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    out, lse = hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, decode_chunk=chunk,
+                                 rescale_threshold=FAST, normaliser=hb.NORMALISER_DIRECT)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    p = hb.make_params(B, Hq, Hkv, 1, cap, d, causal=True, kv_stride=cap, decode_chunk=chunk)
+    split = _decode_split(p, lens, Hkv)
+    for b, L in enumerate(lens):
+        ref, vmax = _decode_oracle(cfg, q, b, L, 64, split, tau=FAST)
+        _check_rows_direct(o[b:b + 1], l[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L))
+
+
+def test_normaliser_ab_accuracy_full_size():
+    """The pages' ablation on the Qwen3-8B-shaped layer: P-Reordering and the direct
+    normaliser against exact attention on sampled rows (printed), each against its own
+    oracle quantity (asserted)."""
+    cfg = W.QWEN3_8B
+    inp = W.prefill_inputs(cfg)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    s = torch.from_numpy(inp["smooth"]).cuda()
+    mx = hb.hifa4_quantize_qkv(q, k, v, s)
+    res = {}
+    for norm in (hb.NORMALISER_P_REORDERING, hb.NORMALISER_DIRECT):
+        o, l = hb.hifa4_attn_fwd(mx, causal=True, rescale_threshold=FAST, normaliser=norm)
+        torch.cuda.synchronize()
+        res[norm] = (o.float().cpu().numpy().reshape(-1, cfg.d), l.cpu().numpy().reshape(-1))
+    rows = np.sort(np.random.default_rng(11).choice(cfg.B * cfg.Hq * cfg.S, 128, replace=False))
+    qq = _oracle_quant(inp)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=64,
+                           quant_p=True, rows=rows, tau=FAST)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    _check_rows(res[0][0][rows], res[0][1][rows], ref, vmax, "P-Reordering")
+    _check_rows_direct(res[1][0][rows], res[1][1][rows], ref, vmax, "direct")
+    exact = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
+                             causal=True, bc=64, quant_p=False, rows=rows)
+    for norm, name in ((0, "P-Reordering"), (1, "direct l")):
+        e = res[norm][0][rows] - exact["o"]
+        print("%s vs exact attention: max %.4g rms %.4g" % (name, np.abs(e).max(),
+                                                           np.sqrt(np.mean(e ** 2))))
