@@ -96,6 +96,12 @@ def _open(path: str):
     lib.oracle_quantize_v.restype = None
     lib.oracle_quantize_v.argtypes = [_F, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, _U8, _U8, _D]
+    lib.oracle_rope_rows.restype = None
+    lib.oracle_rope_rows.argtypes = [_F, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     _F, _F, _F]
+    lib.oracle_smooth_calibrate.restype = None
+    lib.oracle_smooth_calibrate.argtypes = [_D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_double, _F]
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_attention.argtypes = [ctypes.POINTER(_AttnCfg), _D, _D, _D, _I32, _I32, _I64,
                                      ctypes.c_long, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
@@ -195,6 +201,39 @@ def quantize_v(x, *, cap: int | None = None, quantise: bool = True):
     _load().oracle_quantize_v(_ptr(x, _F), B, H, S, d, cap, int(quantise), _ptr(codes, _U8),
                               _ptr(scales, _U8), _ptr(deq, _D))
     return codes, scales, deq
+
+
+# --------------------------------------------------------------------------
+# RoPE and the offline Smooth-QK calibration (the steps before the path)
+# --------------------------------------------------------------------------
+
+def rope_rows(x, cos, sin, pos0: int = 0):
+    """Rotate-half RoPE of x [..., S, d] (fp32) with caller tables cos / sin [n_pos, d/2]
+    (fp32); token t of every row group sits at position pos0 + t.  Returns fp32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    cos = np.ascontiguousarray(cos, dtype=np.float32)
+    sin = np.ascontiguousarray(sin, dtype=np.float32)
+    S, d = x.shape[-2], x.shape[-1]
+    assert d % 2 == 0 and cos.shape == sin.shape and cos.shape[1] == d // 2
+    assert 0 <= pos0 and pos0 + S <= cos.shape[0]
+    out = np.empty_like(x)
+    rows = x.size // d
+    _load().oracle_rope_rows(_ptr(x, _F), rows, S, d, int(pos0), _ptr(cos, _F), _ptr(sin, _F),
+                             _ptr(out, _F))
+    return out
+
+
+def smooth_calibrate(q, k, alpha: float):
+    """s [Hkv, d] float32 from calibration activations q [B,Hq,S,d], k [B,Hkv,S,d]."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, S, d) and Hq % Hkv == 0
+    s = np.empty((Hkv, d), dtype=np.float32)
+    _load().oracle_smooth_calibrate(_ptr(q, _D), _ptr(k, _D), B, Hq, Hkv, S, d, float(alpha),
+                                    _ptr(s, _F))
+    return s
 
 
 # --------------------------------------------------------------------------

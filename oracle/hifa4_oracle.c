@@ -174,6 +174,65 @@ void oracle_quantize_rows(const float* x, int B, int H, int S, int d, const floa
   free(row);
 }
 
+/* ------------------------------------------------------------------------- */
+/* The steps just before the path: RoPE and the offline Smooth-QK calibration  */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Rotate-half rotary position embedding of rows x [rows][d] (fp32), the row r
+ * being token t = r % S at position pos0 + t.  Channel pair (j, j + d/2),
+ * j < d/2, is rotated by the angle whose cosine and sine are the tables'
+ * entries [pos][j] (tables [n_pos][d/2], fp32, given by the caller):
+ *   out[j]       = x[j] * cos - x[j + d/2] * sin
+ *   out[j + d/2] = x[j + d/2] * cos + x[j] * sin
+ * each product rounded to fp32, then the sum (no contraction).  The abstract
+ * places Smooth-QK after RoPE; this is the rotation that precedes it.
+ */
+void oracle_rope_rows(const float* x, long rows, int S, int d, int pos0, const float* cosv,
+                      const float* sinv, float* out) {
+  const int half = d / 2;
+  for (long r = 0; r < rows; r++) {
+    const long pos = pos0 + r % S;
+    const float* xr = x + (size_t)r * d;
+    float* o = out + (size_t)r * d;
+    for (int j = 0; j < half; j++) {
+      const float c = cosv[(size_t)pos * half + j];
+      const float sn = sinv[(size_t)pos * half + j];
+      const float a = xr[j], b = xr[j + half];
+      const float ac = a * c, bs = b * sn, bc = b * c, as = a * sn;
+      o[j] = ac - bs;
+      o[j + half] = bc + as;
+    }
+  }
+}
+
+/*
+ * Offline Smooth-QK calibration (Abstract, Smooth-QK: calibration-static s):
+ * per KV head g and channel j, s[g][j] = (max|K[., g, ., j]| / max|Q[., h, ., j]|)^alpha
+ * with the Q maximum over every query head h of g's group (h / (Hq / Hkv) == g),
+ * every batch entry and token; computed in fp64 and rounded to fp32 once.  A
+ * zero maximum on either side gives s = 1.  q [B][Hq][S][d], k [B][Hkv][S][d].
+ */
+void oracle_smooth_calibrate(const double* q, const double* k, int B, int Hq, int Hkv, int S,
+                             int d, double alpha, float* s_out) {
+  const int G = Hq / Hkv;
+  for (int g = 0; g < Hkv; g++)
+    for (int j = 0; j < d; j++) {
+      double qm = 0.0, km = 0.0;
+      for (int b = 0; b < B; b++) {
+        for (int t = 0; t < S; t++) {
+          const double kv = fabs(k[(((size_t)b * Hkv + g) * S + t) * d + j]);
+          if (kv > km) km = kv;
+          for (int h = g * G; h < (g + 1) * G; h++) {
+            const double qv = fabs(q[(((size_t)b * Hq + h) * S + t) * d + j]);
+            if (qv > qm) qm = qv;
+          }
+        }
+      }
+      s_out[(size_t)g * d + j] = (qm > 0.0 && km > 0.0) ? (float)pow(km / qm, alpha) : 1.0f;
+    }
+}
+
 /*
  * V quantisation: blocks of 32 consecutive tokens of one channel, aligned to
  * token 0; a partial tail block is padded with zeros (code 0) and its scale is

@@ -14,6 +14,7 @@ import pytest
 import oracle
 from tests import test_oracle_attention as TA
 from tests import test_oracle_quant as TQ
+from tests import test_oracle_prologue as TP
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "hifa4_oracle.c")
 
@@ -54,6 +55,12 @@ MUTANTS = [
      "cend = ((c0 + phase) / chunk + 1) * chunk + phase;", 0),
     ("split_phase_ignored", "cend = ((c0 + phase) / chunk + 1) * chunk - phase;",
      "cend = (c0 / chunk + 1) * chunk;", 0),
+    ("rope_first_half_sign_flipped", "o[j] = ac - bs;", "o[j] = ac + bs;", 0),
+    ("rope_second_half_sign_flipped", "o[j + half] = bc + as;", "o[j + half] = bc - as;", 0),
+    ("rope_position_offset_ignored", "const long pos = pos0 + r % S;", "const long pos = r % S;", 0),
+    ("calibration_over_all_query_heads", "for (int h = g * G; h < (g + 1) * G; h++) {",
+     "for (int h = 0; h < Hq; h++) {", 0),
+    ("calibration_ratio_inverted", "(float)pow(km / qm, alpha)", "(float)pow(qm / km, alpha)", 0),
     ("dot_product_drops_last_channel", "for (int j = 0; j < d; j++) s += qr[j] * kr[j];",
      "for (int j = 0; j < d - 1; j++) s += qr[j] * kr[j];", 0),
 ]
@@ -82,6 +89,11 @@ def _pin_checks():
         lambda: TA.test_split_k_mxfp4_equals_merge_of_chunk_runs(64),
         lambda: TA.test_split_k_exact_equals_unsplit(128),
         lambda: TA.test_split_phase_mxfp4_equals_merge_of_runs(128, [[0, 64], [64, 0]]),
+        TP.test_rope_identity_and_quarter_turn_are_exact,
+        TP.test_rope_uses_the_tokens_position_row,
+        TP.test_rope_preserves_pair_norms_and_inverts,
+        TP.test_calibration_hand_worked,
+        lambda: TP.test_calibration_balances_the_smoothed_maxima(0.25),
     ]
     return checks
 
