@@ -7,7 +7,8 @@ current HIP stream.  There is no CPU fallback: if the library is missing or
 the tensors are not on the GPU, the calls raise.
 
 The Python names match the C entry points: ``hifa4_quantize_qkv``,
-``hifa4_attn_fwd``, ``hifa4_attn_fwd_qraw``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
+``hifa4_quantize_qkv_rope``, ``hifa4_smooth_calibrate``,
+``hifa4_smooth_calibrate_workspace_size``, ``hifa4_attn_fwd``, ``hifa4_attn_fwd_qraw``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
 ``hifa4_attn_decode_piece_tiles``, ``hifa4_attn_workspace_size``,
 ``hifa4_status_string``, ``hifa4_last_error``.
 """
@@ -59,6 +60,11 @@ class AttnParamsC(ctypes.Structure):
         ("normaliser", ctypes.c_int32),
     ]
 
+class RopeC(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int32),
+                ("q_pos0", ctypes.c_int32), ("k_pos0", ctypes.c_int32)]
+
+
 NORMALISER_P_REORDERING = 0   # l = sum(P_hat) through the ones column (the method)
 NORMALISER_DIRECT = 1         # l = sum(P) in fp32 on the vector ALU (the pages' comparison)
 
@@ -82,6 +88,16 @@ def load_library(path: str = LIB_PATH):
     lib.hifa4_quantize_qkv.restype = st
     lib.hifa4_quantize_qkv.argtypes = [vp, vp, vp, st, i32, i32, i32, i32, i32, i32, i32, vp,
                                        MxTensorC, MxTensorC, MxTensorC, vp]
+    lib.hifa4_quantize_qkv_rope.restype = st
+    lib.hifa4_quantize_qkv_rope.argtypes = [vp, vp, vp, st, i32, i32, i32, i32, i32, i32, i32, vp,
+                                            ctypes.POINTER(RopeC), MxTensorC, MxTensorC,
+                                            MxTensorC, vp]
+    lib.hifa4_smooth_calibrate_workspace_size.restype = ctypes.c_size_t
+    lib.hifa4_smooth_calibrate_workspace_size.argtypes = [i32, i32]
+    lib.hifa4_smooth_calibrate.restype = st
+    lib.hifa4_smooth_calibrate.argtypes = [vp, vp, st, i32, i32, i32, i32, i32,
+                                           ctypes.POINTER(RopeC), ctypes.c_double, vp, vp,
+                                           ctypes.c_size_t, vp]
     lib.hifa4_attn_workspace_size.restype = ctypes.c_size_t
     lib.hifa4_attn_workspace_size.argtypes = [ctypes.POINTER(AttnParamsC)]
     lib.hifa4_attn_fwd.restype = st
@@ -171,6 +187,13 @@ def alloc_mx(B, Hq, Hkv, Sq, kv_stride, d, device="cuda") -> MXQKV:
                  B, Hq, Hkv, Sq, 0, d, kv_stride)
 
 
+def _rope_struct(cos: torch.Tensor, sin: torch.Tensor, q_pos0: int, k_pos0: int) -> RopeC:
+    if (cos.dtype != torch.float32 or sin.dtype != torch.float32 or cos.dim() != 2
+            or cos.shape != sin.shape or not cos.is_contiguous() or not sin.is_contiguous()):
+        raise ValueError("rope tables must be contiguous float32 [n_pos, d/2] of one shape")
+    return RopeC(_ptr(cos), _ptr(sin), int(cos.shape[0]), int(q_pos0), int(k_pos0))
+
+
 def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
                        v: Optional[torch.Tensor], smooth: Optional[torch.Tensor] = None, *,
                        kv_stride: int = 0, out: Optional[MXQKV] = None, Hkv: Optional[int] = None,
@@ -179,6 +202,24 @@ def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
 
     With k and v both None, pass Hkv (the smoothing rows are per KV head).
     """
+    return _quantize(q, k, v, smooth, None, kv_stride=kv_stride, out=out, Hkv=Hkv, stream=stream)
+
+
+def hifa4_quantize_qkv_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
+                            v: Optional[torch.Tensor], cos: torch.Tensor, sin: torch.Tensor, *,
+                            q_pos0: int = 0, k_pos0: int = 0,
+                            smooth: Optional[torch.Tensor] = None, kv_stride: int = 0,
+                            out: Optional[MXQKV] = None, Hkv: Optional[int] = None,
+                            stream=None) -> MXQKV:
+    """hifa4_quantize_qkv after rotate-half RoPE of Q and K with the tables cos / sin
+    (float32 [n_pos, d/2] on the GPU); query token t sits at position q_pos0 + t, key
+    token t at k_pos0 + t."""
+    rope = _rope_struct(cos, sin, q_pos0, k_pos0)
+    return _quantize(q, k, v, smooth, rope, kv_stride=kv_stride, out=out, Hkv=Hkv,
+                     stream=stream)
+
+
+def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, stream) -> MXQKV:
     ref = next(t for t in (q, k, v) if t is not None)
     B, d = ref.shape[0], ref.shape[3]
     Hq, Sq = (q.shape[1], q.shape[2]) if q is not None else (1, 0)
@@ -205,9 +246,49 @@ def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
                    _ptr(out.k_scales) if k is not None else None)
     mv = MxTensorC(_ptr(out.v_codes) if v is not None else None,
                    _ptr(out.v_scales) if v is not None else None)
-    _check(lib.hifa4_quantize_qkv(_ptr(q), _ptr(k), _ptr(v), _dtype_code(ref.dtype), B, Hq, Hkv,
-                                  Sq, Sk, kv_stride, d, _ptr(smooth), mq, mk, mv,
-                                  _stream(stream)))
+    if rope is None:
+        _check(lib.hifa4_quantize_qkv(_ptr(q), _ptr(k), _ptr(v), _dtype_code(ref.dtype), B, Hq,
+                                      Hkv, Sq, Sk, kv_stride, d, _ptr(smooth), mq, mk, mv,
+                                      _stream(stream)))
+    else:
+        _check(lib.hifa4_quantize_qkv_rope(_ptr(q), _ptr(k), _ptr(v), _dtype_code(ref.dtype), B,
+                                           Hq, Hkv, Sq, Sk, kv_stride, d, _ptr(smooth),
+                                           ctypes.byref(rope), mq, mk, mv, _stream(stream)))
+    return out
+
+
+def hifa4_smooth_calibrate_workspace_size(Hkv: int, d: int) -> int:
+    return int(load_library().hifa4_smooth_calibrate_workspace_size(int(Hkv), int(d)))
+
+
+def hifa4_smooth_calibrate(q: torch.Tensor, k: torch.Tensor, alpha: float, *,
+                           cos: Optional[torch.Tensor] = None, sin: Optional[torch.Tensor] = None,
+                           q_pos0: int = 0, k_pos0: int = 0, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Smooth-QK factors s [Hkv, d] float32 from calibration activations q [B,Hq,S,d] and
+    k [B,Hkv,S,d] (bf16 or fp16 on the GPU), rotated first by cos / sin when given."""
+    if q.dim() != 4 or k.dim() != 4 or q.dtype != k.dtype:
+        raise ValueError("q and k must be 4-d tensors of one dtype")
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, S, d):
+        raise ValueError("k must be [B, Hkv, S, d] with q's B, S and d")
+    if out is None:
+        out = torch.empty((Hkv, d), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (Hkv, d) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [Hkv, d]")
+    need = hifa4_smooth_calibrate_workspace_size(Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rope = None
+    if cos is not None or sin is not None:
+        if cos is None or sin is None:
+            raise ValueError("give both rope tables or neither")
+        rope = ctypes.byref(_rope_struct(cos, sin, q_pos0, k_pos0))
+    _check(load_library().hifa4_smooth_calibrate(
+        _ptr(q), _ptr(k), _dtype_code(q.dtype), B, Hq, Hkv, S, d, rope, float(alpha), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

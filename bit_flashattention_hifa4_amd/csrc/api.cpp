@@ -228,12 +228,34 @@ const char* hifa4_status_string(hifa4_status s) {
 
 const char* hifa4_last_error(void) { return g_last_error.c_str(); }
 
-hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const void* v, hifa4_dtype in_dtype,
-                                int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Sk,
-                                int32_t kv_stride, int32_t d, const float* smooth,
-                                hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
-                                hifa4_mx_tensor v_out, void* stream) {
-  g_last_error.clear();
+namespace {
+
+// Validation of the RoPE tables for tokens [q_pos0, q_pos0 + nq) and
+// [k_pos0, k_pos0 + nk) (n = 0: that tensor is not rotated).
+hifa4_status check_rope(const hifa4_rope* r, int d, int64_t nq, int64_t nk, Span* spans) {
+  if (!r) return fail(HIFA4_ERR_INVALID_ARGUMENT, "rope is NULL");
+  if (!r->cos || !r->sin) return fail(HIFA4_ERR_INVALID_ARGUMENT, "rope table is NULL");
+  if (!aligned16(r->cos) || !aligned16(r->sin))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "rope table is not 16-byte aligned");
+  if (r->n_pos < 0 || r->q_pos0 < 0 || r->k_pos0 < 0)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "negative rope position or table size");
+  if (nq > 0 && (int64_t)r->q_pos0 + nq > r->n_pos)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "query positions %d + %lld exceed the table (%d rows)",
+                r->q_pos0, (long long)nq, r->n_pos);
+  if (nk > 0 && (int64_t)r->k_pos0 + nk > r->n_pos)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "key positions %d + %lld exceed the table (%d rows)",
+                r->k_pos0, (long long)nk, r->n_pos);
+  const int64_t bytes = (int64_t)r->n_pos * (d / 2) * 4;
+  spans[0] = {"rope.cos", r->cos, bytes};
+  spans[1] = {"rope.sin", r->sin, bytes};
+  return HIFA4_OK;
+}
+
+hifa4_status quantize_impl(const void* q, const void* k, const void* v, hifa4_dtype in_dtype,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Sk,
+                           int32_t kv_stride, int32_t d, const float* smooth,
+                           const hifa4_rope* rope, bool with_rope, hifa4_mx_tensor q_out,
+                           hifa4_mx_tensor k_out, hifa4_mx_tensor v_out, void* stream) {
   if (in_dtype != HIFA4_BF16 && in_dtype != HIFA4_FP16)
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "in_dtype %d", (int)in_dtype);
   if (B < 0 || Sq < 0 || Sk < 0 || kv_stride < 0)
@@ -267,8 +289,13 @@ hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const void* v, hif
 
   const int64_t rq = (int64_t)B * Hq * Sq, rk = (int64_t)B * Hkv * Sk;
   const int64_t rcap = (int64_t)B * Hkv * cap;
-  const Span in[] = {{"q", q, rq * d * 2}, {"k", k, rk * d * 2}, {"v", v, rk * d * 2},
-                     {"smooth", smooth, smooth ? (int64_t)Hkv * d * 4 : 0}};
+  Span in[] = {{"q", q, rq * d * 2}, {"k", k, rk * d * 2}, {"v", v, rk * d * 2},
+               {"smooth", smooth, smooth ? (int64_t)Hkv * d * 4 : 0}, {"", nullptr, 0},
+               {"", nullptr, 0}};
+  if (with_rope) {
+    hifa4_status rs = check_rope(rope, d, q ? Sq : 0, k ? Sk : 0, in + 4);
+    if (rs != HIFA4_OK) return rs;
+  }
   const Span out[] = {
       {"q_out.codes", q ? q_out.codes : nullptr, row_codes_bytes(rq, d)},
       {"q_out.scales", q ? q_out.scales : nullptr, row_scales_bytes(rq, d)},
@@ -276,10 +303,16 @@ hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const void* v, hif
       {"k_out.scales", k ? k_out.scales : nullptr, row_scales_bytes(rcap, d)},
       {"v_out.codes", v ? v_out.codes : nullptr, col_blocks((int64_t)B * Hkv, cap) * d * 16},
       {"v_out.scales", v ? v_out.scales : nullptr, col_blocks((int64_t)B * Hkv, cap) * d}};
-  hifa4_status st = check_disjoint(in, 4, out, 6);
+  hifa4_status st = check_disjoint(in, 6, out, 6);
   if (st != HIFA4_OK) return st;
 
   hifa4::QuantizeArgs a = {};
+  if (with_rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.q_pos0 = rope->q_pos0;
+    a.k_pos0 = rope->k_pos0;
+  }
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -304,6 +337,93 @@ hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const void* v, hif
   if (!v || rk == 0) a.v = nullptr;
   return hip_status(hifa4::launch_quantize_qkv(a, in_dtype == HIFA4_BF16, (hipStream_t)stream),
                     "quantize launch");
+}
+
+}  // namespace
+
+hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const void* v, hifa4_dtype in_dtype,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Sk,
+                                int32_t kv_stride, int32_t d, const float* smooth,
+                                hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
+                                hifa4_mx_tensor v_out, void* stream) {
+  g_last_error.clear();
+  return quantize_impl(q, k, v, in_dtype, B, Hq, Hkv, Sq, Sk, kv_stride, d, smooth, nullptr,
+                       false, q_out, k_out, v_out, stream);
+}
+
+hifa4_status hifa4_quantize_qkv_rope(const void* q, const void* k, const void* v,
+                                     hifa4_dtype in_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t Sq, int32_t Sk, int32_t kv_stride, int32_t d,
+                                     const float* smooth, const hifa4_rope* rope,
+                                     hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
+                                     hifa4_mx_tensor v_out, void* stream) {
+  g_last_error.clear();
+  return quantize_impl(q, k, v, in_dtype, B, Hq, Hkv, Sq, Sk, kv_stride, d, smooth, rope, true,
+                       q_out, k_out, v_out, stream);
+}
+
+size_t hifa4_smooth_calibrate_workspace_size(int32_t Hkv, int32_t d) {
+  if (Hkv <= 0 || !supported_d(d)) return 0;
+  return (size_t)2 * Hkv * d * 4;
+}
+
+hifa4_status hifa4_smooth_calibrate(const void* q, const void* k, hifa4_dtype in_dtype,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                                    const hifa4_rope* rope, double alpha, float* smooth_out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (in_dtype != HIFA4_BF16 && in_dtype != HIFA4_FP16)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "in_dtype %d", (int)in_dtype);
+  if (B < 0 || S < 0) return fail(HIFA4_ERR_INVALID_ARGUMENT, "negative size");
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
+  if (!supported_d(d)) return fail(HIFA4_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128, 256)", d);
+  if (!std::isfinite(alpha)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "alpha is not finite");
+  const int64_t rows_q = (int64_t)B * Hq * S, rows_k = (int64_t)B * Hkv * S;
+  const bool any = rows_q > 0;
+  if (any && (!q || !k)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "q or k is NULL");
+  if ((q && !aligned16(q)) || (k && !aligned16(k)))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "q or k is not 16-byte aligned");
+  if (!smooth_out || !aligned16(smooth_out))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "smooth_out is NULL or not 16-byte aligned");
+  const size_t need = hifa4_smooth_calibrate_workspace_size(Hkv, d);
+  if (!workspace || !aligned16(workspace))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(HIFA4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                need);
+  Span in[] = {{"q", any ? q : nullptr, rows_q * d * 2},
+               {"k", any ? k : nullptr, rows_k * d * 2},
+               {"", nullptr, 0},
+               {"", nullptr, 0}};
+  if (rope) {
+    hifa4_status rs = check_rope(rope, d, S, S, in + 2);
+    if (rs != HIFA4_OK) return rs;
+  }
+  const Span out[] = {{"smooth_out", smooth_out, (int64_t)Hkv * d * 4},
+                      {"workspace", workspace, (int64_t)need}};
+  hifa4_status st = check_disjoint(in, 4, out, 2);
+  if (st != HIFA4_OK) return st;
+
+  hifa4::CalibrateArgs a = {};
+  a.q = any ? static_cast<const uint16_t*>(q) : nullptr;
+  a.k = any ? static_cast<const uint16_t*>(k) : nullptr;
+  a.smooth = smooth_out;
+  a.workspace = static_cast<uint32_t*>(workspace);
+  if (rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.q_pos0 = rope->q_pos0;
+    a.k_pos0 = rope->k_pos0;
+  }
+  a.B = any ? B : 0;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.d = d;
+  a.alpha = alpha;
+  return hip_status(hifa4::launch_smooth_calibrate(a, in_dtype == HIFA4_BF16, (hipStream_t)stream),
+                    "calibrate launch");
 }
 
 size_t hifa4_attn_workspace_size(const hifa4_attn_params* p) {

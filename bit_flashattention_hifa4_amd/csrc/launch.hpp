@@ -22,9 +22,26 @@ struct QuantizeArgs {
   int64_t blocks_q, blocks_k;  // 32-element row blocks
   int64_t wg_q, wg_k;          // filled by the launcher
   int64_t items_v;             // (channel pair, 32-token block) items; filled by the launcher
+  const float* rope_cos;       // rotate-half RoPE tables [n_pos][d/2] for Q and K, or null
+  const float* rope_sin;
+  int q_pos0, k_pos0;          // position of token 0 of Q / K in the tables
 };
 
 hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream);
+
+struct CalibrateArgs {
+  const uint16_t* q;     // [B][Hq][S][d]
+  const uint16_t* k;     // [B][Hkv][S][d]
+  float* smooth;         // [Hkv][d]
+  uint32_t* workspace;   // 2 * Hkv * d words: max|K| then max|Q| bit patterns
+  const float* rope_cos; // rotate-half RoPE tables [n_pos][d/2], or null
+  const float* rope_sin;
+  int q_pos0, k_pos0;
+  int B, Hq, Hkv, S, d;
+  double alpha;
+};
+
+hipError_t launch_smooth_calibrate(const CalibrateArgs& a, bool bf16, hipStream_t stream);
 
 // Attention problem after validation; pointers are device pointers.
 struct AttnArgs {

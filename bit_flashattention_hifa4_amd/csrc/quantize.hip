@@ -52,19 +52,55 @@ constexpr int kRowParts = 4;
 struct RowPart {
   uint32_t orow;  // output row (b, h, t) with the token capacity applied
   uint32_t j0;    // first element of this lane's 8
+  uint32_t t;     // token of the row
   bool ok;
 };
+
+// Rotate-half RoPE of the lane's 8 elements j0 .. j0+7: the partner elements
+// (j +- d/2) belong to the lane 2*NB parts away in the same row (a row's
+// 4*NB parts are consecutive lanes of one wave), exchanged as raw words.
+template <bool kBf16, int D>
+__device__ __forceinline__ void rope8(float (&v)[8], const uint4& w, uint32_t j0, uint32_t pos,
+                                      const float* __restrict__ cosv,
+                                      const float* __restrict__ sinv) {
+  constexpr int NB = D / 32;
+  constexpr uint32_t HALF = D / 2;
+  const uint32_t pw[4] = {(uint32_t)__shfl_xor((int)w.x, 2 * NB), (uint32_t)__shfl_xor((int)w.y, 2 * NB),
+                          (uint32_t)__shfl_xor((int)w.z, 2 * NB), (uint32_t)__shfl_xor((int)w.w, 2 * NB)};
+  float u[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    u[2 * i] = elem<kBf16>(pw[i] & 0xFFFFu);
+    u[2 * i + 1] = elem<kBf16>(pw[i] >> 16);
+  }
+  const uint32_t jj = j0 % HALF;
+  const float4* cp = reinterpret_cast<const float4*>(cosv + (size_t)pos * HALF + jj);
+  const float4* sp = reinterpret_cast<const float4*>(sinv + (size_t)pos * HALF + jj);
+  const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const bool first = j0 < HALF;  // own element is x[j] (partner x[j + d/2]) or the reverse
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float own = v[i] * c[i];
+    const float other = u[i] * sn[i];
+    v[i] = first ? own - other : own + other;
+  }
+}
 
 // Index arithmetic is 32-bit (the launcher checks the sizes fit), with the
 // head dim a compile-time constant, so the per-part decode is a handful of
 // integer ops rather than 64-bit divisions.
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kRope>
 __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
                                               const float* __restrict__ s, bool divide,
                                               uint32_t part0, uint32_t n_parts, uint32_t H,
                                               uint32_t S, uint32_t group, uint32_t cap,
                                               uint8_t* __restrict__ codes,
-                                              uint8_t* __restrict__ scales) {
+                                              uint8_t* __restrict__ scales,
+                                              const float* __restrict__ rope_cos,
+                                              const float* __restrict__ rope_sin,
+                                              uint32_t pos0) {
   constexpr uint32_t NB = D / 32;
   uint4 w[kRowParts];
   float4 f0[kRowParts], f1[kRowParts];
@@ -79,6 +115,7 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
     const uint32_t bh = row / S;
     const uint32_t t = row - bh * S;
     rp[r].orow = bh * cap + t;
+    rp[r].t = t;
     w[r] = rp[r].ok ? *reinterpret_cast<const uint4*>(x + (size_t)row * D + rp[r].j0)
                     : make_uint4(0, 0, 0, 0);
     if (s != nullptr) {
@@ -97,6 +134,8 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
       v[2 * i] = elem<kBf16>(ws[i] & 0xFFFFu);
       v[2 * i + 1] = elem<kBf16>(ws[i] >> 16);
     }
+    // RoPE first (every lane takes part in the partner exchange), then Smooth-QK
+    if constexpr (kRope) rope8<kBf16, D>(v, w[r], rp[r].j0, pos0 + rp[r].t, rope_cos, rope_sin);
     if (s != nullptr) {
       const float ff[8] = {f0[r].x, f0[r].y, f0[r].z, f0[r].w, f1[r].x, f1[r].y, f1[r].z, f1[r].w};
 #pragma unroll
@@ -166,7 +205,7 @@ __device__ __forceinline__ void quantise_v_pair(const uint16_t* __restrict__ x, 
   *reinterpret_cast<uint16_t*>(scales + ob * D + 2 * c) = (uint16_t)(sa | (sbb << 8));
 }
 
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kRope>
 __global__ __launch_bounds__(kThreads) void quantize_qkv_kernel(QuantizeArgs a) {
   // Grid order: V token blocks (the longest work items) first, then K, then
   // Q, so that the long items do not form the tail of the launch.
@@ -179,25 +218,152 @@ __global__ __launch_bounds__(kThreads) void quantize_qkv_kernel(QuantizeArgs a) 
       quantise_v_pair<kBf16, D>(a.v, item, a.Sk, a.cap, a.v_codes, a.v_scales);
   } else if (wg < wg_v + wg_k) {
     const uint32_t part0 = (wg - wg_v) * kThreads * kRowParts + threadIdx.x;
-    quantise_rows<kBf16, D>(a.k, a.smooth, true, part0, (uint32_t)(4 * a.blocks_k), a.Hkv, a.Sk,
-                            1, a.cap, a.k_codes, a.k_scales);
+    quantise_rows<kBf16, D, kRope>(a.k, a.smooth, true, part0, (uint32_t)(4 * a.blocks_k), a.Hkv,
+                                   a.Sk, 1, a.cap, a.k_codes, a.k_scales, a.rope_cos,
+                                   a.rope_sin, (uint32_t)a.k_pos0);
   } else {
     const uint32_t part0 = (wg - wg_v - wg_k) * kThreads * kRowParts + threadIdx.x;  // 4 parts per block
-    quantise_rows<kBf16, D>(a.q, a.smooth, false, part0, (uint32_t)(4 * a.blocks_q), a.Hq, a.Sq,
-                            a.Hq / a.Hkv, a.Sq, a.q_codes, a.q_scales);
+    quantise_rows<kBf16, D, kRope>(a.q, a.smooth, false, part0, (uint32_t)(4 * a.blocks_q), a.Hq,
+                                   a.Sq, a.Hq / a.Hkv, a.Sq, a.q_codes, a.q_scales, a.rope_cos,
+                                   a.rope_sin, (uint32_t)a.q_pos0);
   }
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kRope>
 void launch_d(const QuantizeArgs& a, unsigned grid, hipStream_t stream) {
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 64>), dim3(grid), dim3(kThreads), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 128>), dim3(grid), dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 256>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 64, kRope>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 128, kRope>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((quantize_qkv_kernel<kBf16, 256, kRope>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Offline Smooth-QK calibration (Abstract, Smooth-QK: s is static, taken from
+// calibration activations): per KV head g and channel j, the maxima of |K| and
+// of |Q| over the heads of g's query group, every batch entry and token, then
+// s = (max|K| / max|Q|)^alpha in fp64, rounded to fp32; s = 1 where either
+// maximum is zero.  Optionally the same rotate-half RoPE as the quantiser is
+// applied first, since s is defined on post-RoPE activations.
+//
+// Pass 1 (calib_max_kernel): one workgroup per (tensor, b, h, 256-token
+// chunk) with the quantiser's row layout (d/8 lanes per row, 16 bytes each);
+// per-lane maxima, an LDS reduction over the workgroup's rows, then one
+// unsigned atomic max per channel into the workspace (|x| is non-negative, so
+// its bit pattern orders like its value; NaN never enters since fmaxf drops
+// it).  Pass 2 (calib_finish_kernel) forms s.  The workspace is cleared by a
+// fill kernel first.
+constexpr int kCalibTokens = 256;
+
+__global__ __launch_bounds__(kThreads) void calib_clear_kernel(uint32_t* ws, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) ws[i] = 0u;
+}
+
+template <bool kBf16, int D, bool kRope>
+__global__ __launch_bounds__(kThreads) void calib_max_kernel(CalibrateArgs a, uint32_t* ws) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPI = kThreads / LPR;  // rows per pass of the workgroup
+  constexpr int U = 4;                 // passes with loads in flight
+  __shared__ float red[RPI][D];
+  const uint32_t nch = (uint32_t)(a.S + kCalibTokens - 1) / kCalibTokens;
+  const uint32_t items_k = (uint32_t)a.B * a.Hkv * nch;
+  uint32_t item = blockIdx.x;
+  const bool is_q = item >= items_k;
+  if (is_q) item -= items_k;
+  const uint32_t H = is_q ? a.Hq : a.Hkv;
+  const uint32_t bh = item / nch;
+  const uint32_t t0 = (item - bh * nch) * kCalibTokens;
+  const uint32_t g = is_q ? (bh % H) / (a.Hq / a.Hkv) : bh % H;
+  const uint16_t* x = (is_q ? a.q : a.k) + (size_t)bh * a.S * D;
+  const int pos0 = is_q ? a.q_pos0 : a.k_pos0;
+  const uint32_t r0 = threadIdx.x / LPR;
+  const uint32_t j0 = (threadIdx.x % LPR) * 8;
+  const uint32_t t_end = min((uint32_t)a.S, t0 + kCalibTokens);
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (uint32_t tb = t0; tb < t_end; tb += RPI * U) {
+    uint4 w[U];
+    uint32_t tt[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      tt[u] = tb + u * RPI + r0;
+      // every lane of a row shares its token, so a row is valid or not as a whole
+      w[u] = tt[u] < t_end ? *reinterpret_cast<const uint4*>(x + (size_t)tt[u] * D + j0)
+                           : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const uint32_t ws4[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[2 * i] = elem<kBf16>(ws4[i] & 0xFFFFu);
+        v[2 * i + 1] = elem<kBf16>(ws4[i] >> 16);
+      }
+      if constexpr (kRope)  // zeros rotate to zeros; invalid rows use position pos0
+        rope8<kBf16, D>(v, w[u], j0, pos0 + (tt[u] < t_end ? tt[u] : 0u), a.rope_cos, a.rope_sin);
+#pragma unroll
+      for (int i = 0; i < 8; i++) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) red[r0][j0 + i] = m[i];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int r = 0; r < RPI; r++) mx = fmaxf(mx, red[r][threadIdx.x]);
+    if (mx > 0.0f)
+      atomicMax(ws + (is_q ? (size_t)a.Hkv * D : 0) + (size_t)g * D + threadIdx.x,
+                __float_as_uint(mx));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void calib_finish_kernel(const uint32_t* ws, float* s,
+                                                                int n, double alpha) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const double km = (double)__uint_as_float(ws[i]);
+  const double qm = (double)__uint_as_float(ws[n + i]);
+  s[i] = (qm > 0.0 && km > 0.0) ? (float)pow(km / qm, alpha) : 1.0f;
+}
+
+template <bool kBf16, bool kRope>
+void launch_calib_d(const CalibrateArgs& a, unsigned grid, uint32_t* ws, hipStream_t stream) {
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((calib_max_kernel<kBf16, 64, kRope>), dim3(grid), dim3(kThreads), 0, stream, a, ws); break;
+    case 128: hipLaunchKernelGGL((calib_max_kernel<kBf16, 128, kRope>), dim3(grid), dim3(kThreads), 0, stream, a, ws); break;
+    default: hipLaunchKernelGGL((calib_max_kernel<kBf16, 256, kRope>), dim3(grid), dim3(kThreads), 0, stream, a, ws); break;
   }
 }
 
 }  // namespace
+
+hipError_t launch_smooth_calibrate(const CalibrateArgs& a, bool bf16, hipStream_t stream) {
+  const int n = a.Hkv * a.d;
+  uint32_t* ws = a.workspace;
+  const int64_t nch = (a.S + kCalibTokens - 1) / kCalibTokens;
+  const int64_t items = (int64_t)a.B * (a.Hq + a.Hkv) * nch;
+  // 32-bit item and token arithmetic inside the kernel
+  if (items > 0x7FFFFFFF || (int64_t)a.S + kCalibTokens > 0x7FFFFFFF)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(calib_clear_kernel, dim3((2 * n + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, ws, 2 * n);
+  if (items > 0) {
+    const bool rope = a.rope_cos != nullptr;
+    if (bf16 && !rope)
+      launch_calib_d<true, false>(a, (unsigned)items, ws, stream);
+    else if (!rope)
+      launch_calib_d<false, false>(a, (unsigned)items, ws, stream);
+    else if (bf16)
+      launch_calib_d<true, true>(a, (unsigned)items, ws, stream);
+    else
+      launch_calib_d<false, true>(a, (unsigned)items, ws, stream);
+  }
+  hipLaunchKernelGGL(calib_finish_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, ws, a.smooth, n, a.alpha);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream) {
   const int64_t per_wg = (int64_t)kThreads * kRowParts;
@@ -212,10 +378,15 @@ hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream) {
   if (total > lim / (kThreads * kRowParts) || 4 * a.blocks_q > lim || 4 * a.blocks_k > lim ||
       a.items_v > lim || (int64_t)a.B * a.Hkv * a.cap > lim || (int64_t)a.B * a.Hq * a.Sq > lim)
     return hipErrorInvalidConfiguration;
-  if (bf16)
-    launch_d<true>(a, (unsigned)total, stream);
+  const bool rope = a.rope_cos != nullptr;
+  if (bf16 && !rope)
+    launch_d<true, false>(a, (unsigned)total, stream);
+  else if (!rope)
+    launch_d<false, false>(a, (unsigned)total, stream);
+  else if (bf16)
+    launch_d<true, true>(a, (unsigned)total, stream);
   else
-    launch_d<false>(a, (unsigned)total, stream);
+    launch_d<false, true>(a, (unsigned)total, stream);
   return hipGetLastError();
 }
 

@@ -110,6 +110,15 @@ def _torch_dtype(name: str) -> torch.dtype:
     return {"bf16": torch.bfloat16, "fp16": torch.float16}[name]
 
 
+def rope_tables(n_pos: int, d: int, theta: float):
+    """cos / sin tables float32 [n_pos, d/2] of the standard rotary frequencies
+    theta^(-2j/d), angles computed in fp64 and rounded once."""
+    half = d // 2
+    inv = theta ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def apply_rope(x: np.ndarray, theta: float) -> np.ndarray:
     """Rotate-half RoPE on [..., S, d] float32, positions 0..S-1."""
     S, d = x.shape[-2], x.shape[-1]

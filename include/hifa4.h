@@ -118,6 +118,66 @@ HIFA4_API hifa4_status hifa4_quantize_qkv(const void* q, const void* k, const vo
                                 hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
                                 hifa4_mx_tensor v_out, void* stream);
 
+/*
+ * Rotate-half rotary position embedding, the step Smooth-QK follows (the
+ * Abstract places the smoothing after RoPE).  Channel pair (j, j + d/2),
+ * j < d/2, of a token at position pos is rotated by the table entries
+ * c = cos[pos][j], s = sin[pos][j]:
+ *   x'[j] = x[j] * c - x[j + d/2] * s,   x'[j + d/2] = x[j + d/2] * c + x[j] * s
+ * in fp32, each product rounded, then the sum (no fused multiply-add).  The
+ * caller owns the tables (any base frequency or scaling), so the library does
+ * not evaluate trigonometric functions.
+ */
+typedef struct hifa4_rope {
+  const float* cos;  /* device fp32 [n_pos][d/2], 16-byte aligned */
+  const float* sin;  /* device fp32 [n_pos][d/2], 16-byte aligned */
+  int32_t n_pos;     /* rows of the tables */
+  int32_t q_pos0;    /* position of query token 0 (the same for every batch entry) */
+  int32_t k_pos0;    /* position of key token 0 (the same for every batch entry) */
+} hifa4_rope;
+
+/*
+ * hifa4_quantize_qkv with RoPE: Q and K are rotated (rope, positions
+ * q_pos0 + t and k_pos0 + t) in fp32, then smoothed and quantised exactly as
+ * hifa4_quantize_qkv does; V is not rotated.  rope must not be NULL; the
+ * positions of every token given (q_pos0 + Sq and k_pos0 + Sk, for the tensors
+ * passed) must lie within [0, n_pos].  The tables are inputs (read only, not
+ * overlapping the outputs).  Other arguments and errors as for
+ * hifa4_quantize_qkv.
+ */
+HIFA4_API hifa4_status hifa4_quantize_qkv_rope(const void* q, const void* k, const void* v,
+                                     hifa4_dtype in_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t Sq, int32_t Sk, int32_t kv_stride, int32_t d,
+                                     const float* smooth, const hifa4_rope* rope,
+                                     hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
+                                     hifa4_mx_tensor v_out, void* stream);
+
+/* Bytes of device workspace hifa4_smooth_calibrate needs: 2 * Hkv * d * 4
+ * (0 for Hkv <= 0 or an unsupported d). */
+HIFA4_API size_t hifa4_smooth_calibrate_workspace_size(int32_t Hkv, int32_t d);
+
+/*
+ * Offline Smooth-QK calibration (Abstract, Smooth-QK: s is calibration-static):
+ * from calibration activations q [B][Hq][S][d] and k [B][Hkv][S][d] (device,
+ * in_dtype, contiguous, 16-byte aligned), optionally rotated first by rope
+ * (NULL: the activations are already post-RoPE), writes smooth_out (device
+ * fp32 [Hkv][d], the row layout hifa4_quantize_qkv takes):
+ *   s[g][j] = (max |K[., g, ., j]| / max |Q[., h, ., j]|)^alpha
+ * with the Q maximum over every query head h of g's group (h / (Hq / Hkv) ==
+ * g), every batch entry and token; the ratio and the power in fp64, rounded
+ * once to fp32 (the power is the device's fp64 pow, within an ulp of the
+ * correctly rounded value, so s is within one fp32 ulp of the exact result).
+ * s = 1 where either maximum is zero (including B * S == 0, when q and k may
+ * be NULL).  alpha must be finite.  workspace: device, 16-byte aligned, at
+ * least hifa4_smooth_calibrate_workspace_size(Hkv, d) bytes, not overlapping
+ * q, k, the tables or smooth_out; its contents are overwritten.  Three
+ * launches on stream (clear, maxima, finish).
+ */
+HIFA4_API hifa4_status hifa4_smooth_calibrate(const void* q, const void* k, hifa4_dtype in_dtype,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                                    const hifa4_rope* rope, double alpha, float* smooth_out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace hifa4_attn_fwd / bf16_attn_fwd need for p
  * (0 when none); returns 0 as well for invalid parameters. */
 HIFA4_API size_t hifa4_attn_workspace_size(const hifa4_attn_params* p);

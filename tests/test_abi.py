@@ -70,6 +70,96 @@ def test_quantize_rejects_bad_arguments(lib, kw, status, msg):
     assert msg in hb.hifa4_last_error()
 
 
+def _quant_rope(lib, rope, **kw):
+    args = dict(q=A, k=A + 0x4000000, v=A + 0x8000000, dt=hb.HIFA4_BF16, B=1, Hq=4, Hkv=2, Sq=64,
+                Sk=64, stride=0, d=128, smooth=None, qo=_mx(0x20000000), ko=_mx(0x40000000),
+                vo=_mx(0x60000000))
+    args.update(kw)
+    return lib.hifa4_quantize_qkv_rope(args["q"], args["k"], args["v"], args["dt"], args["B"],
+                                       args["Hq"], args["Hkv"], args["Sq"], args["Sk"],
+                                       args["stride"], args["d"], args["smooth"],
+                                       ctypes.byref(rope) if rope is not None else None,
+                                       args["qo"], args["ko"], args["vo"], None)
+
+
+T = 0x7000000  # fake table address, clear of every buffer above
+
+
+def _rope(**kw):
+    r = dict(cos=T, sin=T + 0x100000, n_pos=128, q_pos0=0, k_pos0=0)
+    r.update(kw)
+    return hb.RopeC(r["cos"], r["sin"], r["n_pos"], r["q_pos0"], r["k_pos0"])
+
+
+@pytest.mark.parametrize("rope,kw,status,msg", [
+    (None, {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "rope is NULL"),
+    (dict(sin=None), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "table is NULL"),
+    (dict(cos=T + 4), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(n_pos=-1), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "negative"),
+    (dict(q_pos0=-2), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "negative"),
+    (dict(q_pos0=65), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "query positions"),
+    (dict(k_pos0=100), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "key positions"),
+    (dict(n_pos=63), dict(k=None, v=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "query positions"),
+    (dict(cos=0x20000000), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "overlaps input rope.cos"),
+    (dict(d_bad=True), dict(d=96), hb.HIFA4_ERR_UNSUPPORTED, "head dim"),
+])
+def test_quantize_rope_rejects_bad_arguments(lib, rope, kw, status, msg):
+    if rope is not None:
+        rope.pop("d_bad", None)
+    assert _quant_rope(lib, _rope(**rope) if rope is not None else None, **kw) == status
+    assert msg in hb.hifa4_last_error()
+
+
+def test_quantize_rope_positions_only_checked_for_given_tensors(lib):
+    # Key positions past the table are an error only when K is given.  Each call still
+    # fails validation (q_out overlaps q), so nothing is enqueued.
+    r = _rope(k_pos0=1000)
+    assert _quant_rope(lib, r, k=None, v=None, qo=_mx(A)) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "overlaps input q" in hb.hifa4_last_error()
+    assert _quant_rope(lib, r, qo=_mx(A)) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "key positions" in hb.hifa4_last_error()
+
+
+def _calib(lib, rope=None, **kw):
+    args = dict(q=A, k=A + 0x4000000, dt=hb.HIFA4_BF16, B=1, Hq=4, Hkv=2, S=64, d=128, alpha=0.5,
+                out=0x20000000, ws=0x30000000, ws_bytes=2 * 2 * 128 * 4)
+    args.update(kw)
+    return lib.hifa4_smooth_calibrate(args["q"], args["k"], args["dt"], args["B"], args["Hq"],
+                                      args["Hkv"], args["S"], args["d"],
+                                      ctypes.byref(rope) if rope is not None else None,
+                                      args["alpha"], args["out"], args["ws"], args["ws_bytes"],
+                                      None)
+
+
+@pytest.mark.parametrize("rope,kw,status,msg", [
+    (None, dict(d=96), hb.HIFA4_ERR_UNSUPPORTED, "head dim"),
+    (None, dict(Hq=3), hb.HIFA4_ERR_INVALID_ARGUMENT, "Hq % Hkv"),
+    (None, dict(S=-1), hb.HIFA4_ERR_INVALID_ARGUMENT, "negative"),
+    (None, dict(dt=5), hb.HIFA4_ERR_INVALID_ARGUMENT, "in_dtype"),
+    (None, dict(alpha=float("nan")), hb.HIFA4_ERR_INVALID_ARGUMENT, "alpha"),
+    (None, dict(alpha=float("inf")), hb.HIFA4_ERR_INVALID_ARGUMENT, "alpha"),
+    (None, dict(k=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "NULL"),
+    (None, dict(q=A + 2), hb.HIFA4_ERR_INVALID_ARGUMENT, "aligned"),
+    (None, dict(out=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "smooth_out"),
+    (None, dict(ws=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "workspace"),
+    (None, dict(ws_bytes=2047), hb.HIFA4_ERR_WORKSPACE_TOO_SMALL, "need 2048"),
+    (None, dict(out=A + 0x100), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlaps input q"),
+    (None, dict(ws=0x20000200), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(k_pos0=70), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "key positions"),
+    (dict(sin=0x30000000), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "workspace overlaps input rope.sin"),
+])
+def test_calibrate_rejects_bad_arguments(lib, rope, kw, status, msg):
+    assert _calib(lib, _rope(**rope) if rope is not None else None, **kw) == status
+    assert msg in hb.hifa4_last_error()
+
+
+def test_calibrate_workspace_size(lib):
+    assert lib.hifa4_smooth_calibrate_workspace_size(8, 128) == 2 * 8 * 128 * 4
+    assert lib.hifa4_smooth_calibrate_workspace_size(1, 64) == 512
+    assert lib.hifa4_smooth_calibrate_workspace_size(0, 128) == 0
+    assert lib.hifa4_smooth_calibrate_workspace_size(2, 96) == 0
+
+
 def _params(**kw):
     p = dict(B=2, Hq=8, Hkv=2, Sq=128, Sk=128, d=128, causal=True, sm_scale=None, kv_stride=0,
              kv_lens=None, decode_chunk=0, normaliser=0)
