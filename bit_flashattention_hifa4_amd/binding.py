@@ -7,7 +7,7 @@ current HIP stream.  There is no CPU fallback: if the library is missing or
 the tensors are not on the GPU, the calls raise.
 
 The Python names match the C entry points: ``hifa4_quantize_qkv``,
-``hifa4_quantize_qkv_rope``, ``hifa4_smooth_calibrate``,
+``hifa4_quantize_qkv_rope``, ``hifa4_kv_append``, ``hifa4_smooth_calibrate``,
 ``hifa4_smooth_calibrate_workspace_size``, ``hifa4_attn_fwd``, ``hifa4_attn_fwd_qraw``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
 ``hifa4_attn_decode_piece_tiles``, ``hifa4_attn_workspace_size``,
 ``hifa4_status_string``, ``hifa4_last_error``.
@@ -92,6 +92,10 @@ def load_library(path: str = LIB_PATH):
     lib.hifa4_quantize_qkv_rope.argtypes = [vp, vp, vp, st, i32, i32, i32, i32, i32, i32, i32, vp,
                                             ctypes.POINTER(RopeC), MxTensorC, MxTensorC,
                                             MxTensorC, vp]
+    lib.hifa4_kv_append.restype = st
+    lib.hifa4_kv_append.argtypes = [vp, vp, vp, st, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                    ctypes.POINTER(RopeC), vp, MxTensorC, MxTensorC, MxTensorC,
+                                    vp]
     lib.hifa4_smooth_calibrate_workspace_size.restype = ctypes.c_size_t
     lib.hifa4_smooth_calibrate_workspace_size.argtypes = [i32, i32]
     lib.hifa4_smooth_calibrate.restype = st
@@ -255,6 +259,51 @@ def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, st
                                            Hq, Hkv, Sq, Sk, kv_stride, d, _ptr(smooth),
                                            ctypes.byref(rope), mq, mk, mv, _stream(stream)))
     return out
+
+
+def alloc_v_tail(B, Hkv, d, dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
+    """Zeroed raw-value tail buffer [B, Hkv, 32, d] of hifa4_kv_append."""
+    return torch.zeros((B, Hkv, 32, d), dtype=dtype, device=device)
+
+
+def hifa4_kv_append(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
+                    kv_lens: torch.Tensor, cache: MXQKV, v_tail: torch.Tensor, *,
+                    kv_lens_out: Optional[torch.Tensor] = None,
+                    smooth: Optional[torch.Tensor] = None, cos: Optional[torch.Tensor] = None,
+                    sin: Optional[torch.Tensor] = None, q_pos0: int = 0, k_pos0: int = 0,
+                    stream=None) -> MXQKV:
+    """Append k / v [B,Hkv,n,d] to the MXFP4 cache at each sequence's length kv_lens
+    (int32 [B] on the GPU) after RoPE (cos / sin, optional) and Smooth-QK; q [B,Hq,n,d]
+    (optional) is quantised into cache.q_codes / q_scales at the same positions.
+    kv_lens_out (int32 [B]) receives the new lengths.  Returns cache with Sq = n and
+    Sk = its capacity (the upper bound the decode attention takes with kv_lens)."""
+    if k.dim() != 4 or v.shape != k.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must be 4-d tensors of one shape and dtype")
+    B, Hkv, n, d = k.shape
+    Hq = q.shape[1] if q is not None else cache.Hq
+    if q is not None and (tuple(q.shape) != (B, Hq, n, d) or q.dtype != k.dtype):
+        raise ValueError("q must be [B, Hq, n, d] in k's dtype")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    if kv_lens_out is not None and (kv_lens_out.dtype != torch.int32 or kv_lens_out.numel() != B):
+        raise ValueError("kv_lens_out must be int32 [B]")
+    if tuple(v_tail.shape) != (B, Hkv, 32, d) or v_tail.dtype != k.dtype:
+        raise ValueError("v_tail must be [B, Hkv, 32, d] in k's dtype")
+    if q is not None and tuple(cache.q_codes.shape) != (B, Hq, n, d // 2):
+        raise ValueError("cache.q_codes must be [B, Hq, n, d/2]")
+    rope = None
+    if cos is not None or sin is not None:
+        if cos is None or sin is None:
+            raise ValueError("give both rope tables or neither")
+        rope = ctypes.byref(_rope_struct(cos, sin, q_pos0, k_pos0))
+    mq = MxTensorC(_ptr(cache.q_codes), _ptr(cache.q_scales)) if q is not None else MxTensorC()
+    _check(load_library().hifa4_kv_append(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(k.dtype), B, Hq, Hkv, n, cache.kv_stride, d,
+        _ptr(kv_lens), _ptr(kv_lens_out), _ptr(smooth), rope, _ptr(v_tail), mq,
+        MxTensorC(_ptr(cache.k_codes), _ptr(cache.k_scales)),
+        MxTensorC(_ptr(cache.v_codes), _ptr(cache.v_scales)), _stream(stream)))
+    cache.Sq, cache.Sk = n, cache.kv_stride
+    return cache
 
 
 def hifa4_smooth_calibrate_workspace_size(Hkv: int, d: int) -> int:

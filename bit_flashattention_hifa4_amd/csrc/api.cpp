@@ -362,6 +362,108 @@ hifa4_status hifa4_quantize_qkv_rope(const void* q, const void* k, const void* v
                        q_out, k_out, v_out, stream);
 }
 
+hifa4_status hifa4_kv_append(const void* q, const void* k, const void* v, hifa4_dtype in_dtype,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t n_new, int32_t kv_stride,
+                             int32_t d, const int32_t* kv_lens, int32_t* kv_lens_out,
+                             const float* smooth, const hifa4_rope* rope, void* v_tail,
+                             hifa4_mx_tensor q_out, hifa4_mx_tensor k_cache,
+                             hifa4_mx_tensor v_cache, void* stream) {
+  g_last_error.clear();
+  if (in_dtype != HIFA4_BF16 && in_dtype != HIFA4_FP16)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "in_dtype %d", (int)in_dtype);
+  if (B < 0 || n_new < 0) return fail(HIFA4_ERR_INVALID_ARGUMENT, "negative size");
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
+  if (!supported_d(d)) return fail(HIFA4_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128, 256)", d);
+  if (kv_stride <= 0) return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_stride (cache capacity) must be > 0");
+  struct Req {
+    const char* name;
+    const void* p;
+    bool needed;
+  };
+  const bool any_new = (int64_t)B * n_new > 0;
+  const Req req[] = {{"k", k, any_new},
+                     {"v", v, any_new},
+                     {"kv_lens", kv_lens, true},
+                     {"v_tail", v_tail, true},
+                     {"k_cache.codes", k_cache.codes, true},
+                     {"k_cache.scales", k_cache.scales, true},
+                     {"v_cache.codes", v_cache.codes, true},
+                     {"v_cache.scales", v_cache.scales, true},
+                     {"q", q, false},
+                     {"q_out.codes", q ? q_out.codes : nullptr, q != nullptr},
+                     {"q_out.scales", q ? q_out.scales : nullptr, q != nullptr},
+                     {"kv_lens_out", kv_lens_out, false},
+                     {"smooth", smooth, false}};
+  for (const Req& r : req) {
+    if (r.needed && !r.p) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is NULL", r.name);
+    if (r.p && !aligned16(r.p))
+      return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", r.name);
+  }
+  Span in[] = {{"q", q, (int64_t)B * Hq * n_new * d * 2},
+               {"k", k, (int64_t)B * Hkv * n_new * d * 2},
+               {"v", v, (int64_t)B * Hkv * n_new * d * 2},
+               {"smooth", smooth, smooth ? (int64_t)Hkv * d * 4 : 0},
+               {"kv_lens", kv_lens, (int64_t)B * 4},
+               {"", nullptr, 0},
+               {"", nullptr, 0}};
+  if (rope) {
+    if (!rope->cos || !rope->sin) return fail(HIFA4_ERR_INVALID_ARGUMENT, "rope table is NULL");
+    if (!aligned16(rope->cos) || !aligned16(rope->sin))
+      return fail(HIFA4_ERR_INVALID_ARGUMENT, "rope table is not 16-byte aligned");
+    if (rope->n_pos < 1 || rope->q_pos0 < 0 || rope->k_pos0 < 0)
+      return fail(HIFA4_ERR_INVALID_ARGUMENT, "rope needs n_pos >= 1 and positions >= 0");
+    const int64_t top = (int64_t)(rope->q_pos0 > rope->k_pos0 ? rope->q_pos0 : rope->k_pos0) +
+                        kv_stride + n_new;
+    if (top > 0x7FFFFFFF) return fail(HIFA4_ERR_INVALID_ARGUMENT, "rope positions overflow");
+    const int64_t bytes = (int64_t)rope->n_pos * (d / 2) * 4;
+    in[5] = {"rope.cos", rope->cos, bytes};
+    in[6] = {"rope.sin", rope->sin, bytes};
+  }
+  const int64_t rq = (int64_t)B * Hq * n_new, rcap = (int64_t)B * Hkv * kv_stride;
+  const int64_t vblk = col_blocks((int64_t)B * Hkv, kv_stride);
+  const Span out[] = {{"q_out.codes", q ? q_out.codes : nullptr, row_codes_bytes(rq, d)},
+                      {"q_out.scales", q ? q_out.scales : nullptr, row_scales_bytes(rq, d)},
+                      {"k_cache.codes", k_cache.codes, row_codes_bytes(rcap, d)},
+                      {"k_cache.scales", k_cache.scales, row_scales_bytes(rcap, d)},
+                      {"v_cache.codes", v_cache.codes, vblk * d * 16},
+                      {"v_cache.scales", v_cache.scales, vblk * d},
+                      {"kv_lens_out", kv_lens_out, (int64_t)B * 4},
+                      {"v_tail", v_tail, (int64_t)B * Hkv * 32 * d * 2}};
+  hifa4_status st = check_disjoint(in, 7, out, 8);
+  if (st != HIFA4_OK) return st;
+
+  hifa4::AppendArgs a = {};
+  a.q = (q && rq > 0) ? static_cast<const uint16_t*>(q) : nullptr;
+  a.k = any_new ? static_cast<const uint16_t*>(k) : nullptr;
+  a.v = any_new ? static_cast<const uint16_t*>(v) : nullptr;
+  a.smooth = smooth;
+  if (rope) {
+    a.rope_cos = rope->cos;
+    a.rope_sin = rope->sin;
+    a.n_pos = rope->n_pos;
+    a.q_pos0 = rope->q_pos0;
+    a.k_pos0 = rope->k_pos0;
+  }
+  a.lens = kv_lens;
+  a.lens_out = kv_lens_out;
+  a.v_tail = static_cast<uint16_t*>(v_tail);
+  a.q_codes = q_out.codes;
+  a.q_scales = q_out.scales;
+  a.k_codes = k_cache.codes;
+  a.k_scales = k_cache.scales;
+  a.v_codes = v_cache.codes;
+  a.v_scales = v_cache.scales;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_new = n_new;
+  a.d = d;
+  a.cap = kv_stride;
+  return hip_status(hifa4::launch_kv_append(a, in_dtype == HIFA4_BF16, (hipStream_t)stream),
+                    "kv append launch");
+}
+
 size_t hifa4_smooth_calibrate_workspace_size(int32_t Hkv, int32_t d) {
   if (Hkv <= 0 || !supported_d(d)) return 0;
   return (size_t)2 * Hkv * d * 4;

@@ -29,6 +29,30 @@ struct QuantizeArgs {
 
 hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream);
 
+// KV-cache append: n_new tokens per sequence at positions lens[b] ...
+struct AppendArgs {
+  const uint16_t* q;      // [B][Hq][n_new][d] or null
+  const uint16_t* k;      // [B][Hkv][n_new][d]
+  const uint16_t* v;      // [B][Hkv][n_new][d]
+  const float* smooth;    // [Hkv][d] or null
+  const float* rope_cos;  // [n_pos][d/2] or null
+  const float* rope_sin;
+  const int32_t* lens;    // [B] current lengths
+  int32_t* lens_out;      // [B] lengths after the append, or null
+  uint16_t* v_tail;       // [B][Hkv][32][d] raw values of each open value block (in/out)
+  uint8_t* q_codes;
+  uint8_t* q_scales;
+  uint8_t* k_codes;       // cache, row layout with capacity cap
+  uint8_t* k_scales;
+  uint8_t* v_codes;       // cache, column layout with capacity cap
+  uint8_t* v_scales;
+  int B, Hq, Hkv, n_new, d, cap;
+  int n_pos, q_pos0, k_pos0;
+  int64_t blocks_q, blocks_k, wg_q, wg_k, items_v;  // filled by the launcher
+};
+
+hipError_t launch_kv_append(AppendArgs a, bool bf16, hipStream_t stream);
+
 struct CalibrateArgs {
   const uint16_t* q;     // [B][Hq][S][d]
   const uint16_t* k;     // [B][Hkv][S][d]

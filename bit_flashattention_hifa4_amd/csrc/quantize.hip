@@ -91,7 +91,19 @@ __device__ __forceinline__ void rope8(float (&v)[8], const uint4& w, uint32_t j0
 // Index arithmetic is 32-bit (the launcher checks the sizes fit), with the
 // head dim a compile-time constant, so the per-part decode is a handful of
 // integer ops rather than 64-bit divisions.
-template <bool kBf16, int D, bool kRope>
+// Cache append (kAppend): token t of sequence b sits at L_b + t, with L_b the
+// sequence's current length from `lens` (clamped to [0, kv_cap]); with
+// offset_rows the output is cache row L_b + t and rows past the capacity are
+// not written, else row t.  Table rows are clamped to max_pos, so a length
+// past the tables reads no memory outside them.
+struct AppendRows {
+  const int32_t* lens;
+  uint32_t kv_cap;
+  bool offset_rows;
+  uint32_t max_pos;
+};
+
+template <bool kBf16, int D, bool kRope, bool kAppend = false>
 __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
                                               const float* __restrict__ s, bool divide,
                                               uint32_t part0, uint32_t n_parts, uint32_t H,
@@ -100,7 +112,7 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
                                               uint8_t* __restrict__ scales,
                                               const float* __restrict__ rope_cos,
                                               const float* __restrict__ rope_sin,
-                                              uint32_t pos0) {
+                                              uint32_t pos0, AppendRows ap = {}) {
   constexpr uint32_t NB = D / 32;
   uint4 w[kRowParts];
   float4 f0[kRowParts], f1[kRowParts];
@@ -118,6 +130,16 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
     rp[r].t = t;
     w[r] = rp[r].ok ? *reinterpret_cast<const uint4*>(x + (size_t)row * D + rp[r].j0)
                     : make_uint4(0, 0, 0, 0);
+    if constexpr (kAppend) {
+      const int32_t l = ap.lens[bh / H];
+      const uint32_t L = l < 0 ? 0u : min((uint32_t)l, ap.kv_cap);
+      rp[r].t = L + t;
+      if (ap.offset_rows) {
+        rp[r].orow += L;
+        // a row is written only inside the cache (uniform over the row's lanes)
+        rp[r].ok = rp[r].ok && L + t < ap.kv_cap;
+      }
+    }
     if (s != nullptr) {
       const uint32_t hs = (bh % H) / group;
       const float4* sp = reinterpret_cast<const float4*>(s + hs * D + rp[r].j0);
@@ -135,7 +157,10 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
       v[2 * i + 1] = elem<kBf16>(ws[i] >> 16);
     }
     // RoPE first (every lane takes part in the partner exchange), then Smooth-QK
-    if constexpr (kRope) rope8<kBf16, D>(v, w[r], rp[r].j0, pos0 + rp[r].t, rope_cos, rope_sin);
+    if constexpr (kRope) {
+      const uint32_t pos = kAppend ? min(pos0 + rp[r].t, ap.max_pos) : pos0 + rp[r].t;
+      rope8<kBf16, D>(v, w[r], rp[r].j0, pos, rope_cos, rope_sin);
+    }
     if (s != nullptr) {
       const float ff[8] = {f0[r].x, f0[r].y, f0[r].z, f0[r].w, f1[r].x, f1[r].y, f1[r].z, f1[r].w};
 #pragma unroll
@@ -239,6 +264,112 @@ void launch_d(const QuantizeArgs& a, unsigned grid, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// KV-cache append for decode.  New K rows are rotated, smoothed and quantised
+// into cache rows L_b .. L_b + n - 1 (the row layout needs nothing else).  A
+// value block holds 32 consecutive tokens of one channel under one scale, so
+// a new token in a partly filled block changes that block's scale: the block
+// is quantised again from the raw values of its earlier tokens, which the
+// caller's tail buffer keeps ([B][Hkv][32][d], slot = token % 32).  One lane
+// owns a (b, g, channel pair) for every block the append touches; it reads the
+// old tail slots before it writes new ones, and no other lane touches them, so
+// the buffer is updated in place.  The cache then equals a one-shot
+// quantisation of the whole sequence.
+template <bool kBf16, int D>
+__device__ __forceinline__ void append_v_pair(const AppendArgs& a, uint32_t item) {
+  constexpr uint32_t HALF = D / 2;
+  const uint32_t c = item % HALF;
+  const uint32_t bh = item / HALF;
+  const uint32_t b = bh / (uint32_t)a.Hkv;
+  const uint32_t cap = (uint32_t)a.cap;
+  const int32_t l = a.lens[b];
+  const uint32_t L = l < 0 ? 0u : min((uint32_t)l, cap);
+  const uint32_t end = min(L + (uint32_t)a.n_new, cap);
+  if (bh % (uint32_t)a.Hkv == 0 && c == 0 && a.lens_out) a.lens_out[b] = (int32_t)end;
+  if (end <= L) return;
+  const uint16_t* src = a.v + (size_t)bh * a.n_new * D + 2 * c;
+  uint32_t* tail = reinterpret_cast<uint32_t*>(a.v_tail + (size_t)bh * 32 * D + 2 * c);
+  const uint32_t nblk_cap = (cap + 31) / 32;
+  for (uint32_t blk = L / 32; blk <= (end - 1) / 32; blk++) {
+    const uint32_t t0 = blk * 32;
+    uint32_t w[32];
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      const uint32_t tok = t0 + k;
+      w[k] = 0;
+      if (tok < L)
+        w[k] = tail[(size_t)k * HALF];  // earlier token of this block
+      else if (tok < end)
+        w[k] = *reinterpret_cast<const uint32_t*>(src + (size_t)(tok - L) * D);
+    }
+    float va[32], vb[32];
+    float ma = 0.0f, mb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      va[k] = elem<kBf16>(w[k] & 0xFFFFu);
+      vb[k] = elem<kBf16>(w[k] >> 16);
+      ma = fmaxf(ma, fabsf(va[k]));
+      mb = fmaxf(mb, fabsf(vb[k]));
+    }
+    const uint32_t sa = e8m0_from_amax(ma), sbb = e8m0_from_amax(mb);
+    const float fa = e8m0_to_float(sa), fb = e8m0_to_float(sbb);
+    uint32_t ca[4], cb[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float xa[8] = {va[8 * q], va[8 * q + 1], va[8 * q + 2], va[8 * q + 3],
+                           va[8 * q + 4], va[8 * q + 5], va[8 * q + 6], va[8 * q + 7]};
+      const float xb[8] = {vb[8 * q], vb[8 * q + 1], vb[8 * q + 2], vb[8 * q + 3],
+                           vb[8 * q + 4], vb[8 * q + 5], vb[8 * q + 6], vb[8 * q + 7]};
+      ca[q] = encode8(xa, fa);
+      cb[q] = encode8(xb, fb);
+    }
+    const size_t ob = (size_t)bh * nblk_cap + blk;
+    uint4* dst = reinterpret_cast<uint4*>(a.v_codes + (ob * D + 2 * c) * 16);
+    dst[0] = make_uint4(ca[0], ca[1], ca[2], ca[3]);
+    dst[1] = make_uint4(cb[0], cb[1], cb[2], cb[3]);
+    *reinterpret_cast<uint16_t*>(a.v_scales + ob * D + 2 * c) = (uint16_t)(sa | (sbb << 8));
+    // the block still open after the append keeps its new tokens' raw values
+    if (end % 32 != 0 && blk == end / 32) {
+#pragma unroll
+      for (int k = 0; k < 32; k++)
+        if (t0 + k >= L && t0 + k < end) tail[(size_t)k * HALF] = w[k];
+    }
+  }
+}
+
+template <bool kBf16, int D, bool kRope>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
+  const uint32_t wg = blockIdx.x;
+  const uint32_t wg_v = (uint32_t)((a.items_v + kThreads - 1) / kThreads);
+  const uint32_t wg_k = (uint32_t)a.wg_k;
+  const uint32_t max_pos = (uint32_t)(a.n_pos > 0 ? a.n_pos - 1 : 0);
+  if (wg < wg_v) {
+    const uint32_t item = wg * kThreads + threadIdx.x;
+    if (item < (uint32_t)a.items_v) append_v_pair<kBf16, D>(a, item);
+  } else if (wg < wg_v + wg_k) {
+    const uint32_t part0 = (wg - wg_v) * kThreads * kRowParts + threadIdx.x;
+    quantise_rows<kBf16, D, kRope, true>(
+        a.k, a.smooth, true, part0, (uint32_t)(4 * a.blocks_k), a.Hkv, a.n_new, 1, a.cap,
+        a.k_codes, a.k_scales, a.rope_cos, a.rope_sin, (uint32_t)a.k_pos0,
+        AppendRows{a.lens, (uint32_t)a.cap, true, max_pos});
+  } else {
+    const uint32_t part0 = (wg - wg_v - wg_k) * kThreads * kRowParts + threadIdx.x;
+    quantise_rows<kBf16, D, kRope, true>(
+        a.q, a.smooth, false, part0, (uint32_t)(4 * a.blocks_q), a.Hq, a.n_new, a.Hq / a.Hkv,
+        a.n_new, a.q_codes, a.q_scales, a.rope_cos, a.rope_sin, (uint32_t)a.q_pos0,
+        AppendRows{a.lens, (uint32_t)a.cap, false, max_pos});
+  }
+}
+
+template <bool kBf16, bool kRope>
+void launch_append_d(const AppendArgs& a, unsigned grid, hipStream_t stream) {
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((kv_append_kernel<kBf16, 64, kRope>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((kv_append_kernel<kBf16, 128, kRope>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((kv_append_kernel<kBf16, 256, kRope>), dim3(grid), dim3(kThreads), 0, stream, a); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Offline Smooth-QK calibration (Abstract, Smooth-QK: s is static, taken from
 // calibration activations): per KV head g and channel j, the maxima of |K| and
 // of |Q| over the heads of g's query group, every batch entry and token, then
@@ -338,6 +469,35 @@ void launch_calib_d(const CalibrateArgs& a, unsigned grid, uint32_t* ws, hipStre
 }
 
 }  // namespace
+
+hipError_t launch_kv_append(AppendArgs a, bool bf16, hipStream_t stream) {
+  const int64_t per_wg = (int64_t)kThreads * kRowParts;
+  const int64_t NB = a.d / 32;
+  a.blocks_k = (int64_t)a.B * a.Hkv * a.n_new * NB;
+  a.blocks_q = a.q ? (int64_t)a.B * a.Hq * a.n_new * NB : 0;
+  a.wg_k = (4 * a.blocks_k + per_wg - 1) / per_wg;
+  a.wg_q = (4 * a.blocks_q + per_wg - 1) / per_wg;
+  a.items_v = (int64_t)a.B * a.Hkv * (a.d / 2);
+  const int64_t wg_v = (a.items_v + kThreads - 1) / kThreads;
+  const int64_t total = wg_v + a.wg_k + a.wg_q;
+  if (a.B == 0) return hipSuccess;
+  // 32-bit index arithmetic inside the kernel
+  const int64_t lim = 0x7FFFFFFF;
+  if (total > lim / (kThreads * kRowParts) || 4 * a.blocks_q > lim || 4 * a.blocks_k > lim ||
+      (int64_t)a.B * a.Hkv * a.cap > lim || (int64_t)a.cap + a.n_new > lim ||
+      (int64_t)a.B * a.Hq * a.n_new > lim)
+    return hipErrorInvalidConfiguration;
+  const bool rope = a.rope_cos != nullptr;
+  if (bf16 && !rope)
+    launch_append_d<true, false>(a, (unsigned)total, stream);
+  else if (!rope)
+    launch_append_d<false, false>(a, (unsigned)total, stream);
+  else if (bf16)
+    launch_append_d<true, true>(a, (unsigned)total, stream);
+  else
+    launch_append_d<false, true>(a, (unsigned)total, stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_smooth_calibrate(const CalibrateArgs& a, bool bf16, hipStream_t stream) {
   const int n = a.Hkv * a.d;

@@ -152,6 +152,48 @@ HIFA4_API hifa4_status hifa4_quantize_qkv_rope(const void* q, const void* k, con
                                      hifa4_mx_tensor q_out, hifa4_mx_tensor k_out,
                                      hifa4_mx_tensor v_out, void* stream);
 
+/*
+ * KV-cache append for decode: n_new tokens per sequence are added to an MXFP4
+ * cache after RoPE and Smooth-QK, the steps the Abstract places before the
+ * 4-bit attention (Smooth-QK after RoPE), at each sequence's own position.
+ * Sequence b currently holds L_b = kv_lens[b] tokens; its new token i sits at
+ * position L_b + i (RoPE table row q_pos0 / k_pos0 + L_b + i).
+ *   q     [B][Hq][n_new][d] new queries, or NULL: rotated, smoothed (x s) and
+ *         quantised to q_out, row layout with T = n_new (the decode Q of
+ *         hifa4_attn_fwd when n_new == 1);
+ *   k, v  [B][Hkv][n_new][d] new keys / values (NULL allowed when B * n_new == 0),
+ *         k rotated, smoothed (/ s) and
+ *         quantised into k_cache rows L_b .. L_b + n_new - 1; v into v_cache,
+ *         where every value block the append touches is quantised again from
+ *         the raw values of all its tokens, so after any sequence of appends
+ *         the cache holds exactly what hifa4_quantize_qkv(_rope) of each whole
+ *         sequence writes;
+ *   v_tail  device, in_dtype [B][Hkv][32][d], IN/OUT: slot t % 32 holds the raw
+ *         value of token t for the tokens of the last, partly filled value
+ *         block (t >= 32 * floor(L_b / 32)); the call reads the slots below
+ *         L_b % 32 and writes those of its new tokens in the block left open.
+ *         Zero-initialise it with the cache (L_b == 0 reads nothing);
+ *   kv_lens      device int32 [B], read only;
+ *   kv_lens_out  device int32 [B] or NULL: receives min(L_b + n_new, kv_stride),
+ *         ready for the next hifa4_attn_fwd decode call (must not be kv_lens);
+ *   kv_stride    the cache capacity in tokens (> 0); k_cache / v_cache use the
+ *         layouts of hifa4_mx_tensor with T = kv_stride;
+ *   smooth, dtype as for hifa4_quantize_qkv; rope may be NULL (no rotation),
+ *         else n_pos >= 1.
+ * Lengths live on the device, so the host cannot check them: the caller
+ * guarantees 0 <= L_b and L_b + n_new <= kv_stride (and within the tables).
+ * The kernel clamps L_b to [0, kv_stride], writes no row past the capacity
+ * and clamps table rows to n_pos - 1, so no access leaves the buffers, but the
+ * result for such a sequence is unspecified.  One launch.
+ */
+HIFA4_API hifa4_status hifa4_kv_append(const void* q, const void* k, const void* v,
+                             hifa4_dtype in_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t n_new, int32_t kv_stride, int32_t d,
+                             const int32_t* kv_lens, int32_t* kv_lens_out,
+                             const float* smooth, const hifa4_rope* rope, void* v_tail,
+                             hifa4_mx_tensor q_out, hifa4_mx_tensor k_cache,
+                             hifa4_mx_tensor v_cache, void* stream);
+
 /* Bytes of device workspace hifa4_smooth_calibrate needs: 2 * Hkv * d * 4
  * (0 for Hkv <= 0 or an unsupported d). */
 HIFA4_API size_t hifa4_smooth_calibrate_workspace_size(int32_t Hkv, int32_t d);

@@ -120,6 +120,49 @@ def test_quantize_rope_positions_only_checked_for_given_tensors(lib):
     assert "key positions" in hb.hifa4_last_error()
 
 
+def _append(lib, rope=None, **kw):
+    args = dict(q=A, k=A + 0x4000000, v=A + 0x8000000, dt=hb.HIFA4_BF16, B=2, Hq=4, Hkv=2, n=1,
+                cap=256, d=128, lens=0x9000000, lens_out=0x9001000, smooth=None,
+                tail=0x9100000, qo=_mx(0x20000000), kc=_mx(0x40000000), vc=_mx(0x60000000))
+    args.update(kw)
+    return lib.hifa4_kv_append(args["q"], args["k"], args["v"], args["dt"], args["B"], args["Hq"],
+                               args["Hkv"], args["n"], args["cap"], args["d"], args["lens"],
+                               args["lens_out"], args["smooth"],
+                               ctypes.byref(rope) if rope is not None else None, args["tail"],
+                               args["qo"], args["kc"], args["vc"], None)
+
+
+@pytest.mark.parametrize("rope,kw,status,msg", [
+    (None, dict(d=96), hb.HIFA4_ERR_UNSUPPORTED, "head dim"),
+    (None, dict(cap=0), hb.HIFA4_ERR_INVALID_ARGUMENT, "capacity"),
+    (None, dict(n=-1), hb.HIFA4_ERR_INVALID_ARGUMENT, "negative"),
+    (None, dict(Hq=5), hb.HIFA4_ERR_INVALID_ARGUMENT, "Hq % Hkv"),
+    (None, dict(lens=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "kv_lens is NULL"),
+    (None, dict(tail=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "v_tail is NULL"),
+    (None, dict(k=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "k is NULL"),
+    (None, dict(qo=hb.MxTensorC(None, 0x20000000)), hb.HIFA4_ERR_INVALID_ARGUMENT, "q_out.codes"),
+    (None, dict(lens_out=0x9000004), hb.HIFA4_ERR_INVALID_ARGUMENT, "aligned"),
+    (None, dict(lens_out=0x9000000), hb.HIFA4_ERR_INVALID_ARGUMENT, "kv_lens_out overlaps input kv_lens"),
+    (None, dict(tail=0x40000100), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlap"),
+    (None, dict(kc=_mx(A + 0x40)), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlaps input q"),
+    (dict(n_pos=0), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "n_pos >= 1"),
+    (dict(cos=None), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "table is NULL"),
+    (dict(q_pos0=0x7FFFFF00), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "overflow"),
+    (dict(sin=0x9100000), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "v_tail overlaps input rope.sin"),
+])
+def test_kv_append_rejects_bad_arguments(lib, rope, kw, status, msg):
+    assert _append(lib, _rope(**rope) if rope is not None else None, **kw) == status
+    assert msg in hb.hifa4_last_error()
+
+
+def test_kv_append_allows_null_kv_only_when_empty(lib):
+    # n = 0: k and v may be NULL; the call still validates the rest (here: an overlap)
+    assert _append(lib, k=None, v=None, n=0, tail=0x40000100) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "overlap" in hb.hifa4_last_error()
+    assert _append(lib, k=None, n=1) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "k is NULL" in hb.hifa4_last_error()
+
+
 def _calib(lib, rope=None, **kw):
     args = dict(q=A, k=A + 0x4000000, dt=hb.HIFA4_BF16, B=1, Hq=4, Hkv=2, S=64, d=128, alpha=0.5,
                 out=0x20000000, ws=0x30000000, ws_bytes=2 * 2 * 128 * 4)
