@@ -271,6 +271,28 @@ def main():
         "kernel_source_sha256_16": kernel_source_sha(),
     }
 
+    # ---- the step with RoPE of K in the quantise launch (the headline step takes
+    #      post-RoPE activations; this one rotates pre-RoPE K in the same pass),
+    #      timed back to back like the headline
+    cos, sin = (torch.from_numpy(t).to(dev) for t in W.rope_tables(cfg.S, cfg.d, cfg.rope_theta))
+
+    def step_rope():
+        hb.hifa4_quantize_qkv_rope(None, k, v, cos, sin, smooth=smooth, out=mx, Hkv=cfg.Hkv)
+        attend()
+
+    settle(step_rope, torch, 50.0)
+    n_r = max(5, args.steps // 2)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(n_r):
+        step_rope()
+    r1.record()
+    torch.cuda.synchronize()
+    extra["step_rope_kv_ms"] = r0.elapsed_time(r1) / n_r
+    log("step with RoPE of K in the quantise launch: %.3f ms (headline step %.3f ms GPU)"
+        % (extra["step_rope_kv_ms"], gpu_ms_per_step))
+    quantise()   # restore the codes of the step's inputs
+
     # ---- the same attention in the FlashAttention-2 frame (rescale threshold 0)
     f0 = lambda: hb.hifa4_attn_fwd_qraw(q, smooth, mx, causal=cfg.causal, out=out, lse=lse,
                                         rescale_threshold=0.0)
@@ -349,7 +371,7 @@ def main():
 def decode_leg(W, hb, torch, np, dev, args):
     cfg = W.DECODE
     lens = W.decode_lengths(cfg)
-    cap = int(-(-int(lens.max()) // 64) * 64)
+    cap = int(-(-(int(lens.max()) + 1) // 64) * 64)   # room for the decode step's new token
     log("building the decode cache: %d sequences, %d tokens" % (cfg.B, int(lens.sum())))
     mx = hb.alloc_mx(cfg.B, cfg.Hq, cfg.Hkv, 1, cap, cfg.d, device=dev)
     hb.hifa4_quantize_qkv(W.decode_q(cfg).to(dev), None, None, None, out=mx)
@@ -378,9 +400,51 @@ def decode_leg(W, hb, torch, np, dev, args):
     total = float(kv_bytes + qo)
     gbs = total / (d_ms.mean() * 1e-3) / 1e9
     log("decode %.3f ms: %.1f GB/s (%.1f%% of HBM peak)" % (d_ms.mean(), gbs, gbs / HBM_PEAK_GBS * 100))
-    return {"decode_workload": cfg.name, "decode_tokens": int(lens.sum()),
-            "decode_ms_avg": float(d_ms.mean()), "decode_bytes": total, "decode_gbs": gbs,
-            "decode_fraction_of_hbm_peak": gbs / HBM_PEAK_GBS}
+    res = {"decode_workload": cfg.name, "decode_tokens": int(lens.sum()),
+           "decode_ms_avg": float(d_ms.mean()), "decode_bytes": total, "decode_gbs": gbs,
+           "decode_fraction_of_hbm_peak": gbs / HBM_PEAK_GBS}
+
+    # the whole decode step: append one token per sequence (RoPE at its position,
+    # K row, value-block requantisation, new Q) then attention over L + 1 keys.
+    # Repeating it rewrites the same rows from the same lengths, so every
+    # repetition does the same work.
+    rng = np.random.default_rng(cfg.seed + 5)
+    new = [torch.from_numpy(rng.standard_normal((cfg.B, h, 1, cfg.d), dtype=np.float32))
+           .to(torch.bfloat16).to(dev) for h in (cfg.Hq, cfg.Hkv, cfg.Hkv)]
+    cos, sin = (torch.from_numpy(t).to(dev) for t in W.rope_tables(cap, cfg.d, 1.0e6))
+    tail = hb.alloc_v_tail(cfg.B, cfg.Hkv, cfg.d, device=dev)
+    lens_new = torch.empty_like(lens_t)
+
+    def append():
+        hb.hifa4_kv_append(new[0], new[1], new[2], lens_t, mx, tail, kv_lens_out=lens_new,
+                           cos=cos, sin=sin)
+
+    def attend_new():
+        hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_new, out=out, lse=lse, workspace=ws,
+                          rescale_threshold=hb.RESCALE_THRESHOLD_FAST)
+
+    def dstep():
+        append()
+        attend_new()
+
+    settle(dstep, torch)
+    n = max(10, args.steps)
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n)]
+    for e0, e1, e2 in evs:
+        e0.record()
+        append()
+        e1.record()
+        attend_new()
+        e2.record()
+    torch.cuda.synchronize()
+    ap_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    st_ms = np.array([a.elapsed_time(c) for a, _, c in evs])
+    log("decode step %.3f ms (append %.3f ms + attention over L + 1)" % (st_ms.mean(), ap_ms.mean()))
+    res.update({"decode_step_definition": "hifa4_kv_append (1 token: RoPE, K row, V block "
+                                          "requantisation, Q) + hifa4_attn_fwd over L + 1 keys",
+                "decode_step_ms_avg": float(st_ms.mean()),
+                "decode_append_ms_avg": float(ap_ms.mean())})
+    return res
 
 
 if __name__ == "__main__":

@@ -240,7 +240,11 @@ def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, st
     cap = kv_stride or Sk
     if out is None:
         out = alloc_mx(B, Hq, Hkv, Sq, cap, d, device=ref.device)
-    out.Sk, out.Sq, out.kv_stride = Sk, Sq, cap
+    # only the shapes of the tensors given change (a K/V-only call keeps out's Q shape)
+    if q is not None:
+        out.Sq = Sq
+    if kk is not None:
+        out.Sk, out.kv_stride = Sk, cap
     if smooth is not None and (smooth.dtype != torch.float32 or tuple(smooth.shape) != (Hkv, d)):
         raise ValueError("smooth must be float32 [Hkv, d]")
     lib = load_library()

@@ -58,11 +58,26 @@ struct RowPart {
 
 // Rotate-half RoPE of the lane's 8 elements j0 .. j0+7: the partner elements
 // (j +- d/2) belong to the lane 2*NB parts away in the same row (a row's
-// 4*NB parts are consecutive lanes of one wave), exchanged as raw words.
+// 4*NB parts are consecutive lanes of one wave), exchanged as raw words.  The
+// table entries are loaded first (rope_load, issued with the row loads).
+struct RopeCS {
+  float4 c0, c1, s0, s1;
+};
+
+template <int D>
+__device__ __forceinline__ RopeCS rope_load(uint32_t j0, uint32_t pos,
+                                            const float* __restrict__ cosv,
+                                            const float* __restrict__ sinv) {
+  constexpr uint32_t HALF = D / 2;
+  const uint32_t jj = j0 % HALF;
+  const float4* cp = reinterpret_cast<const float4*>(cosv + (size_t)pos * HALF + jj);
+  const float4* sp = reinterpret_cast<const float4*>(sinv + (size_t)pos * HALF + jj);
+  return RopeCS{cp[0], cp[1], sp[0], sp[1]};
+}
+
 template <bool kBf16, int D>
-__device__ __forceinline__ void rope8(float (&v)[8], const uint4& w, uint32_t j0, uint32_t pos,
-                                      const float* __restrict__ cosv,
-                                      const float* __restrict__ sinv) {
+__device__ __forceinline__ void rope8(float (&v)[8], const uint4& w, uint32_t j0,
+                                      const RopeCS& cs) {
   constexpr int NB = D / 32;
   constexpr uint32_t HALF = D / 2;
   const uint32_t pw[4] = {(uint32_t)__shfl_xor((int)w.x, 2 * NB), (uint32_t)__shfl_xor((int)w.y, 2 * NB),
@@ -73,10 +88,7 @@ __device__ __forceinline__ void rope8(float (&v)[8], const uint4& w, uint32_t j0
     u[2 * i] = elem<kBf16>(pw[i] & 0xFFFFu);
     u[2 * i + 1] = elem<kBf16>(pw[i] >> 16);
   }
-  const uint32_t jj = j0 % HALF;
-  const float4* cp = reinterpret_cast<const float4*>(cosv + (size_t)pos * HALF + jj);
-  const float4* sp = reinterpret_cast<const float4*>(sinv + (size_t)pos * HALF + jj);
-  const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  const float4 c0 = cs.c0, c1 = cs.c1, s0 = cs.s0, s1 = cs.s1;
   const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
   const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
   const bool first = j0 < HALF;  // own element is x[j] (partner x[j + d/2]) or the reverse
@@ -117,6 +129,7 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
   uint4 w[kRowParts];
   float4 f0[kRowParts], f1[kRowParts];
   RowPart rp[kRowParts];
+  RopeCS cs[kRowParts];
 #pragma unroll
   for (int r = 0; r < kRowParts; r++) {
     const uint32_t part = part0 + (uint32_t)r * kThreads;
@@ -140,6 +153,10 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
         rp[r].ok = rp[r].ok && L + t < ap.kv_cap;
       }
     }
+    if constexpr (kRope) {
+      const uint32_t pos = kAppend ? min(pos0 + rp[r].t, ap.max_pos) : pos0 + rp[r].t;
+      cs[r] = rope_load<D>(rp[r].j0, pos, rope_cos, rope_sin);
+    }
     if (s != nullptr) {
       const uint32_t hs = (bh % H) / group;
       const float4* sp = reinterpret_cast<const float4*>(s + hs * D + rp[r].j0);
@@ -157,10 +174,7 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
       v[2 * i + 1] = elem<kBf16>(ws[i] >> 16);
     }
     // RoPE first (every lane takes part in the partner exchange), then Smooth-QK
-    if constexpr (kRope) {
-      const uint32_t pos = kAppend ? min(pos0 + rp[r].t, ap.max_pos) : pos0 + rp[r].t;
-      rope8<kBf16, D>(v, w[r], rp[r].j0, pos, rope_cos, rope_sin);
-    }
+    if constexpr (kRope) rope8<kBf16, D>(v, w[r], rp[r].j0, cs[r]);
     if (s != nullptr) {
       const float ff[8] = {f0[r].x, f0[r].y, f0[r].z, f0[r].w, f1[r].x, f1[r].y, f1[r].z, f1[r].w};
 #pragma unroll
@@ -432,7 +446,9 @@ __global__ __launch_bounds__(kThreads) void calib_max_kernel(CalibrateArgs a, ui
         v[2 * i + 1] = elem<kBf16>(ws4[i] >> 16);
       }
       if constexpr (kRope)  // zeros rotate to zeros; invalid rows use position pos0
-        rope8<kBf16, D>(v, w[u], j0, pos0 + (tt[u] < t_end ? tt[u] : 0u), a.rope_cos, a.rope_sin);
+        rope8<kBf16, D>(v, w[u], j0,
+                        rope_load<D>(j0, pos0 + (tt[u] < t_end ? tt[u] : 0u), a.rope_cos,
+                                     a.rope_sin));
 #pragma unroll
       for (int i = 0; i < 8; i++) m[i] = fmaxf(m[i], fabsf(v[i]));
     }
