@@ -337,6 +337,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, dev)
 
+    if not args.no_decode:
+        extra.update(read_ceiling(torch, dev))
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a sample")
@@ -366,6 +369,35 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def read_ceiling(torch, dev, nbytes=2 << 30):
+    """HBM read rate of a plain streaming kernel (the probe library's) over a
+    buffer 8x the last-level cache: the practical ceiling next to the decode's
+    rate, which the 8 TB/s peak is not."""
+    import ctypes
+    from bit_flashattention_hifa4_amd import build
+    lib = ctypes.CDLL(build.PROBES_LIB)
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    best = 0.0
+    for blocks in (1024, 2048, 8192):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        s = torch.cuda.current_stream().cuda_stream
+        f = lambda: lib.probe_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, s)
+        for _ in range(3):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9)
+    del buf
+    log("plain streaming read over 2 GiB: %.1f GB/s" % best)
+    return {"stream_read_ceiling_gbs": best}
 
 
 def decode_leg(W, hb, torch, np, dev, args):

@@ -1,8 +1,9 @@
 // probes.hip -- diagnostic kernels that pin down gfx950 instruction behaviour
 // the attention kernels rely on: the operand / scale / accumulator lane
 // layouts of the scaled-FP4 and bf16 MFMAs, the rounding of the packed FP4
-// convert, the lane placement of memory -> LDS buffer loads, and the issue
-// rates of v_exp_f32 and the FP4 MFMA.
+// convert, the lane placement of memory -> LDS buffer loads, the issue
+// rates of v_exp_f32 and the FP4 MFMA, and the HBM read rate of a plain
+// streaming kernel.
 //
 // Built into its own library (libhifa4_probes.so); the tests call it to check
 // those facts against independent host-side expectations.  Every kernel reads
@@ -15,6 +16,23 @@
 
 namespace hifa4 {
 namespace {
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, size_t n16,
+                                                         uint32_t* __restrict__ out) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
+           d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
 
 template <int kOpsel>
 __global__ __launch_bounds__(64) void mfma_fp4_32_kernel(const uint4* a, const uint4* b,
@@ -244,6 +262,13 @@ int probe_cvt_pk_fp4(const float* x, const float* scale, uint32_t* out, int n, i
 int probe_half_swap(const float* x, float* out, int n_waves, void* stream) {
   if (n_waves <= 0) return -1;
   hipLaunchKernelGGL(half_swap_kernel, dim3(n_waves), dim3(64), 0, (hipStream_t)stream, x, out);
+  return status(hipGetLastError());
+}
+
+int probe_stream_read(const void* src, size_t bytes, uint32_t* out, int n_blocks, void* stream) {
+  if (!src || !out || n_blocks <= 0 || (bytes & 15)) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const uint4*>(src), bytes / 16, out);
   return status(hipGetLastError());
 }
 

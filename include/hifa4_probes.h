@@ -71,6 +71,14 @@ HIFA4_PROBE_API int probe_lds_dma(const uint8_t* src, uint8_t* out, int size, vo
 HIFA4_PROBE_API int probe_buffer_range(const uint32_t* src, uint32_t* out, int soffset,
                                        int num_records, void* stream);
 
+/* Streaming read: n_blocks x 256 threads read `bytes` (a multiple of 16) of
+ * src in 16-byte words, grid-stride, four words in flight per thread, and
+ * write the xor of every word each thread read to out[n_blocks * 256]
+ * (which keeps the loads alive).  Timed over a buffer larger than the
+ * last-level cache, it gives the HBM read rate a plain kernel reaches. */
+HIFA4_PROBE_API int probe_stream_read(const void* src, size_t bytes, uint32_t* out, int n_blocks,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

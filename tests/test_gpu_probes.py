@@ -51,6 +51,8 @@ def lib():
     l.probe_lds_dma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_buffer_range.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p]
+    l.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
     return l
 
 
@@ -321,3 +323,22 @@ def test_buffer_range_check_with_sgpr_offset(lib, soffset, num_records):
         print("%s soffset=%d num_records=%d: counts soffset %s, ignores it %s" % (
             name, soffset, num_records, (part == with_so).all(), (part == without_so).all()))
         assert (part == with_so).all()
+
+
+def test_stream_read_covers_every_word_once(lib):
+    """Each thread's xor covers exactly the words i, i + stride, ... below the end
+    (a ragged tail past the unrolled part included), checked on the host."""
+    rng = np.random.default_rng(8)
+    n_blocks = 3
+    n16 = 3 * 256 * 4 * 2 + 3 * 256 + 37        # two unrolled rounds, a tail, a ragged end
+    words = rng.integers(0, 2**32, size=n16 * 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    out = torch.empty(n_blocks * 256, dtype=torch.int32, device="cuda")
+    assert lib.probe_stream_read(src.data_ptr(), n16 * 16, out.data_ptr(), n_blocks, _stream()) == 0
+    torch.cuda.synchronize()
+    w4 = np.bitwise_xor.reduce(words.reshape(n16, 4), axis=1)
+    stride = n_blocks * 256
+    exp = np.array([np.bitwise_xor.reduce(w4[t::stride]) if t < n16 else 0
+                    for t in range(stride)], dtype=np.uint32)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), exp)
+    assert lib.probe_stream_read(src.data_ptr(), 8, out.data_ptr(), n_blocks, _stream()) == -1
