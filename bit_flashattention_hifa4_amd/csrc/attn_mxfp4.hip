@@ -776,8 +776,10 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     if constexpr (kDirect) l_direct = __builtin_fmaf(l_direct, st.alpha, row_sum_p(c0, c1));
 #pragma unroll
     for (int i = 0; i < NJ * 2 + NC + (kDirect ? 0 : 1); i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // then ten VALU
+      // one MFMA, then a few VALU: ten for d <= 128 (9 MFMAs a step), three for
+      // d = 256 (17 MFMAs; measured 365 -> 356 us on the Gemma2 shape)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, D == 256 ? 3 : 10, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ... and the Q K^T products may not sink past this step's barrier into
