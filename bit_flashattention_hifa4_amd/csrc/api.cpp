@@ -146,7 +146,9 @@ static hifa4_status attn_fwd_impl(const hifa4_attn_params* p, hifa4_mx_tensor q,
   const char* names[] = {q_raw ? "q" : "q.codes", q_raw ? "q" : "q.scales", "k.codes", "k.scales",
                          "v.codes", "v.scales", "out"};
   for (int i = 0; i < 7; i++) {
-    if (!ptrs[i]) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    // with no key capacity (Sk == 0) the K / V buffers are empty and may be NULL
+    const bool kv = i >= 2 && i < 6;
+    if (!ptrs[i] && !(kv && rcap == 0)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
     if (!aligned16(ptrs[i])) return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
   }
   if (lse && !aligned16(lse)) return fail(HIFA4_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");

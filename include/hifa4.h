@@ -240,9 +240,10 @@ HIFA4_API size_t hifa4_attn_workspace_size(const hifa4_attn_params* p);
  * from a fresh softmax state and restarts where it crosses into the next pair.
  * So a fresh state starts at key t of pair s whenever t == 0 or
  * (first_tile(s) * 64 + t) is a multiple of 64 * piece_tiles.
- * q, k, v: MX tensors from hifa4_quantize_qkv (T = Sq for q, kv_stride for k, v).
+ * q, k, v: MX tensors from hifa4_quantize_qkv (T = Sq for q, kv_stride for k, v;
+ *      with a key capacity of 0 the k and v buffers are empty and may be NULL).
  * out: device [B][Hq][Sq][d] in out_dtype, O = acc / l (rows without any
- *      visible key are 0).
+ *      visible key are 0).  B * Hq * Sq == 0 enqueues nothing.
  * lse: device fp32 [B][Hq][Sq] natural-log sum-exp of the scaled scores
  *      (m + ln l; -inf for rows without a visible key), or NULL.
  * workspace: device scratch of hifa4_attn_workspace_size(p) bytes (may be NULL if 0).

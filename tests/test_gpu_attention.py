@@ -399,3 +399,28 @@ def test_normaliser_ab_accuracy_full_size():
         e = res[norm][0][rows] - exact["o"]
         print("%s vs exact attention: max %.4g rms %.4g" % (name, np.abs(e).max(),
                                                            np.sqrt(np.mean(e ** 2))))
+
+
+@pytest.mark.parametrize("Sq", [1, 70])
+def test_no_keys_gives_zero_rows_and_empty_problems_enqueue_nothing(Sq):
+    """Sk == 0 (K / V buffers empty, passed as NULL): every row sees no key, so O = 0 and
+    LSE = -inf, prefill and decode alike.  B == 0 and Sq == 0 are no-ops."""
+    B, Hq, Hkv, d = 2, 4, 2, 128
+    rng = np.random.default_rng(3)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, Sq, d), dtype=np.float32)).to(torch.bfloat16)
+    mx = hb.hifa4_quantize_qkv(q.cuda(), None, None, None, Hkv=Hkv)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    mx = hb.MXQKV(mx.q_codes, mx.q_scales, torch.empty((B, Hkv, 0, d // 2), **u8),
+                  torch.empty((B, Hkv, 0, d // 32), **u8), torch.empty((B, Hkv, 0, d, 16), **u8),
+                  torch.empty((B, Hkv, 0, d), **u8), B, Hq, Hkv, Sq, 0, d, 0)
+    out = torch.full((B, Hq, Sq, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    hb.hifa4_attn_fwd(mx, causal=Sq > 1, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    assert torch.all(torch.isneginf(lse))
+    # nothing to compute: success, outputs untouched
+    e = hb.MXQKV(mx.q_codes[:0], mx.q_scales[:0], mx.k_codes[:0], mx.k_scales[:0],
+                 mx.v_codes[:0], mx.v_scales[:0], 0, Hq, Hkv, Sq, 0, d, 0)
+    hb.hifa4_attn_fwd(e, causal=True, out=out[:0], lse=lse[:0])
+    torch.cuda.synchronize()
