@@ -155,8 +155,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the attention path has no "
-              "multi-GPU leg); got --gpus %d, WORLD_SIZE %d" % (args.gpus, world), file=sys.stderr)
+        print("bench.py: the attention path runs on one GPU only (it has no multi-GPU "
+              "leg); got --gpus %d, WORLD_SIZE %d" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
