@@ -1,16 +1,19 @@
 """Seeded synthetic workloads for the attention path.
 
-This module only draws numbers: it holds none of the method's arithmetic
-(no quantisation, no softmax, no attention).  Both the HIP path and the CPU
-oracle receive exactly the tensors made here.
+This module only makes inputs: it holds none of the attention path's
+arithmetic (no quantisation, no softmax, no attention).  Both the HIP path and
+the CPU oracle receive exactly the tensors made here.  Its RoPE and its
+calibration of s are part of the input recipe (they make synthetic post-RoPE
+activations and a static smoothing vector); the library's own RoPE and
+calibration are checked against the oracle's, never against these.
 
 The pages measure HiFA4 on activation traces of real LLMs (Qwen3-8B, Gemma2-9B,
 Llama-3.1-8B, Mistral-7B, Phi-4B; "HiFA4: Training-Free 4-bit FlashAttention on
 Ascend HIF4 NPUs for LLM Inference", Abstract).  Those weights and traces are
 not available, so the workloads below stand in for them with the same head
 counts, head dims and sequence lengths, N(0, 1) activations, a synthetic RoPE,
-and seeded outlier key channels (the situation Smooth-QK is meant for: the
-abstract says it moves quantisation difficulty from K to Q).
+and seeded outlier key channels (the situation Smooth-QK is meant for: it
+moves quantisation difficulty from K to Q, Abstract, Smooth-QK).
 
 Recipe (per config):
   * numpy ``default_rng`` (PCG64), float32 standard normals;
