@@ -215,23 +215,37 @@ __device__ __forceinline__ void mask_scores(v16f& s0, v16f& s1, int kb, int lim)
   }
 }
 
+// Output rows: each half-wave holds 4 of every 8 consecutive channels of its
+// query's row; one lane swap per dword (lane n with lane n + 32) gives every
+// lane 8 consecutive channels of one group, stored as 16 bytes (8 stores per
+// 32 output channels' worth of 4 groups instead of 16 8-byte ones; measured
+// 4 % faster on a 4096-item launch, 0.7 % on the Qwen3 shape, same bits).
 template <int NC>
 __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row, int h, const v16f (&acc)[NC],
                                           float inv) {
   constexpr int D = NC * 32;
+  auto cvt2 = [&](float x, float y) -> uint32_t {
+    const uint32_t u = a.out_fp16 ? float_to_half_bits(x) : float_to_bf16_bits(x);
+    const uint32_t v = a.out_fp16 ? float_to_half_bits(y) : float_to_bf16_bits(y);
+    return u | (v << 16);
+  };
 #pragma unroll
   for (int c = 0; c < NC; c++) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; g4++) {
-      const int ch = 32 * c + 8 * g4 + 4 * h;
-      uint32_t u[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float v = acc[c][4 * g4 + i] * inv;
-        u[i] = a.out_fp16 ? float_to_half_bits(v) : float_to_bf16_bits(v);
-      }
-      uint2 w = make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16));
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + ch) = w;
+    for (int gp = 0; gp < 2; gp++) {
+      // groups ga (stored by the lower half-wave) and gb (upper): lane (n, h)
+      // holds channels 8 g + 4 h .. + 3 of both
+      const int ga = 2 * gp, gb = 2 * gp + 1;
+      const uint32_t a0 = cvt2(acc[c][4 * ga] * inv, acc[c][4 * ga + 1] * inv);
+      const uint32_t a1 = cvt2(acc[c][4 * ga + 2] * inv, acc[c][4 * ga + 3] * inv);
+      const uint32_t b0 = cvt2(acc[c][4 * gb] * inv, acc[c][4 * gb + 1] * inv);
+      const uint32_t b1 = cvt2(acc[c][4 * gb + 2] * inv, acc[c][4 * gb + 3] * inv);
+      // the upper half's group-ga words go down, the lower half's group-gb words up
+      const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+      const int ch = 32 * c + 8 * (h ? gb : ga);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + row * D + ch) =
+          make_uint4(s0[0], s1[0], s0[1], s1[1]);
     }
   }
 }
