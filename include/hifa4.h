@@ -21,12 +21,14 @@
  *   - `stream` is a hipStream_t (NULL = the default stream); every call only
  *     enqueues work on it and never synchronises;
  *   - the library never allocates device memory; scratch memory comes from the
- *     caller's `workspace` (size from hifa4_attn_workspace_size);
+ *     caller's `workspace` (sizes from hifa4_attn_workspace_size and
+ *     hifa4_smooth_calibrate_workspace_size);
  *   - arguments are validated before anything is enqueued: on a negative
  *     status nothing was enqueued and hifa4_last_error() describes why;
  *   - a launch failure returns HIFA4_ERR_HIP; faults during execution surface
  *     at the caller's next synchronisation;
- *   - outputs must not overlap inputs; inputs are read only;
+ *   - outputs must not overlap inputs or each other; inputs are read only (the
+ *     one in/out buffer is hifa4_kv_append's v_tail, documented there);
  *   - NaN / Inf inputs are unsupported (results unspecified);
  *   - calls are reentrant; the only global state is the per-thread error text.
  */
