@@ -8,7 +8,10 @@
 // with the K rows loaded in a permuted order so that each lane's accumulator
 // registers already hold the keys of its P V operand (K = 16 keys per MFMA:
 // lane (q, h) needs keys 16u + 8h .. + 7 of MFMA u).  V is staged in LDS
-// transposed (channel-major) so its A operand is one 16-byte LDS read.
+// transposed (channel-major) so its A operand is one 16-byte LDS read.  Tiles
+// are double-buffered: the next tile is loaded into registers while the
+// current one is computed, then written to the other LDS buffer (V transposed
+// four keys at a time, one 8-byte LDS write per channel).
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -21,6 +24,15 @@ constexpr int kBN = 64;
 constexpr int kBR = 128;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Two fp32 to a packed bf16 pair with the hardware's round-to-nearest-even
+// convert (one gfx950 instruction for both).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
 // Key (within the 64-key step) loaded as A row m of 32-key tile t.
 __device__ __forceinline__ int perm_row_bf16(int t, int m) {
   const int j = m >> 3, hh = (m >> 2) & 1, i = m & 3;
@@ -32,8 +44,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
   constexpr int NJ = D / 16;     // QK MFMAs per 32-key tile
   constexpr int NC = D / 32;     // channel tiles
   constexpr int VT = kBN + 8;    // padded key stride of the transposed V tile (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[D * VT];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[2][D * VT];
+  // per thread and tile: KL 16-byte K chunks, VL groups of (4 keys, 8 channels)
+  constexpr int KL = kBN * D / 8 / 256;
+  constexpr int VITEMS = (kBN / 4) * (D / 8);
+  constexpr int VL = (VITEMS + 255) / 256;
+  static_assert(KL >= 1 && KL * 256 == kBN * D / 8, "K tile must split evenly over the workgroup");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -84,40 +101,80 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
 
-  for (int kt = 0; kt < n_tiles; kt++) {
-    const int n0 = kt * kBN;
-    __syncthreads();
-    // K tile, row-major [key][D]
-    for (int ci = tid; ci < kBN * D / 8; ci += 256) {
-      const int row = ci / (D / 8), off = (ci % (D / 8)) * 8;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (n0 + row < L)
-        w = *reinterpret_cast<const uint4*>(a.k + (bkv * a.cap + n0 + row) * D + off);
-      *reinterpret_cast<uint4*>(lds_k + row * D + off) = w;
-    }
-    // V tile transposed: thread -> (key = ci % 64, 8 channels)
-    for (int ci = tid; ci < kBN * D / 8; ci += 256) {
-      const int key = ci % kBN, cg = (ci / kBN) * 8;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (n0 + key < L)
-        w = *reinterpret_cast<const uint4*>(a.v + (bkv * a.cap + n0 + key) * D + cg);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // tile loads into registers (keys past L read as zeros) and their LDS stores
+  uint4 kr[KL], vr[VL][4];
+  auto load_tile = [&](int n0) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        lds_vt[(cg + 2 * i) * VT + key] = (uint16_t)(ws[i] & 0xFFFFu);
-        lds_vt[(cg + 2 * i + 1) * VT + key] = (uint16_t)(ws[i] >> 16);
+    for (int i = 0; i < KL; i++) {
+      const int ci = tid + 256 * i;
+      const int row = ci / (D / 8), off = (ci % (D / 8)) * 8;
+      kr[i] = n0 + row < L
+                  ? *reinterpret_cast<const uint4*>(a.k + (bkv * a.cap + n0 + row) * D + off)
+                  : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VL; i++) {
+      const int ci = tid + 256 * i;
+      const int k4 = ci % (kBN / 4), cg = (ci / (kBN / 4)) * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++) {
+        const int key = 4 * k4 + kk;
+        vr[i][kk] = ci < VITEMS && n0 + key < L
+                        ? *reinterpret_cast<const uint4*>(a.v + (bkv * a.cap + n0 + key) * D + cg)
+                        : make_uint4(0, 0, 0, 0);
       }
     }
-    __syncthreads();
-    if (n0 >= wave_end) continue;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KL; i++) {
+      const int ci = tid + 256 * i;
+      const int row = ci / (D / 8), off = (ci % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(lds_k[buf] + row * D + off) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VL; i++) {
+      const int ci = tid + 256 * i;
+      if (ci >= VITEMS) break;
+      const int k4 = ci % (kBN / 4), cg = (ci / (kBN / 4)) * 8;
+      const uint32_t wk[4][4] = {{vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w},
+                                 {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w},
+                                 {vr[i][2].x, vr[i][2].y, vr[i][2].z, vr[i][2].w},
+                                 {vr[i][3].x, vr[i][3].y, vr[i][3].z, vr[i][3].w}};
+      // channel c of keys 4 k4 .. 4 k4 + 3: one 8-byte write
+#pragma unroll
+      for (int c2 = 0; c2 < 4; c2++) {
+        const uint32_t w0 = wk[0][c2], w1 = wk[1][c2], w2 = wk[2][c2], w3 = wk[3][c2];
+        // low halves: channel cg + 2 c2, high halves: channel cg + 2 c2 + 1
+        const uint2 lo = make_uint2((w0 & 0xFFFFu) | (w1 << 16), (w2 & 0xFFFFu) | (w3 << 16));
+        const uint2 hi = make_uint2((w0 >> 16) | (w1 & 0xFFFF0000u), (w2 >> 16) | (w3 & 0xFFFF0000u));
+        *reinterpret_cast<uint2*>(lds_vt[buf] + (cg + 2 * c2) * VT + 4 * k4) = lo;
+        *reinterpret_cast<uint2*>(lds_vt[buf] + (cg + 2 * c2 + 1) * VT + 4 * k4) = hi;
+      }
+    }
+  };
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; kt++) {
+    const int n0 = kt * kBN;
+    const int buf = kt & 1;
+    const bool more = kt + 1 < n_tiles;  // uniform
+    if (more) load_tile(n0 + kBN);
+    const uint16_t* lk = lds_k[buf];
+    const uint16_t* lv = lds_vt[buf];
+    if (n0 < wave_end) {
 
     v16f s0 = v16f{}, s1 = v16f{};
     const int r0 = perm_row_bf16(0, n), r1 = perm_row_bf16(1, n);
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
       v8s k0, k1;
-      uint4 w0 = *reinterpret_cast<const uint4*>(lds_k + r0 * D + 16 * j + 8 * h);
-      uint4 w1 = *reinterpret_cast<const uint4*>(lds_k + r1 * D + 16 * j + 8 * h);
+      uint4 w0 = *reinterpret_cast<const uint4*>(lk + r0 * D + 16 * j + 8 * h);
+      uint4 w1 = *reinterpret_cast<const uint4*>(lk + r1 * D + 16 * j + 8 * h);
       __builtin_memcpy(&k0, &w0, 16);
       __builtin_memcpy(&k1, &w1, 16);
       s0 = mfma_bf16_32x32x16(k0, qa[j], s0);
@@ -172,18 +229,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int k = 16 * (u >> 1) + 8 * (u & 1) + 2 * i;
-        pw[i] = float_to_bf16_bits(p[k]) | (float_to_bf16_bits(p[k + 1]) << 16);
+        pw[i] = pack_bf16x2(p[k], p[k + 1]);
       }
       v8s pb;
       __builtin_memcpy(&pb, pw, 16);
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
         v8s va;
-        uint4 w = *reinterpret_cast<const uint4*>(lds_vt + (32 * cc + n) * VT + 16 * u + 8 * h);
+        uint4 w = *reinterpret_cast<const uint4*>(lv + (32 * cc + n) * VT + 16 * u + 8 * h);
         __builtin_memcpy(&va, &w, 16);
         acc[cc] = mfma_bf16_32x32x16(va, pb, acc[cc]);
       }
     }
+    }  // n0 < wave_end
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   if (q < a.Sq) {
@@ -194,11 +254,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; g4++) {
         const int ch = 32 * cc + 8 * g4 + 4 * h;
-        uint32_t u[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) u[i] = float_to_bf16_bits(acc[cc][4 * g4 + i] * inv);
         *reinterpret_cast<uint2*>(a.out + row * D + ch) =
-            make_uint2(u[0] | (u[1] << 16), u[2] | (u[3] << 16));
+            make_uint2(pack_bf16x2(acc[cc][4 * g4] * inv, acc[cc][4 * g4 + 1] * inv),
+                       pack_bf16x2(acc[cc][4 * g4 + 2] * inv, acc[cc][4 * g4 + 3] * inv));
       }
     if (a.lse && h == 0) a.lse[row] = l_run > 0.0f ? m_run * kLn2 + logf(l_run) : -INFINITY;
   }
