@@ -44,6 +44,7 @@ class _AttnCfg(ctypes.Structure):
         ("causal", ctypes.c_int), ("sm_scale", ctypes.c_double),
         ("bc", ctypes.c_int), ("chunk", ctypes.c_int), ("quant_p", ctypes.c_int),
         ("br", ctypes.c_int), ("nthreads", ctypes.c_int), ("tau", ctypes.c_double),
+        ("p_rule", ctypes.c_int),
     ]
 
 
@@ -88,14 +89,16 @@ def _open(path: str):
     lib.oracle_e2m1_encode_array.restype = None
     lib.oracle_e2m1_encode_array.argtypes = [_D, ctypes.c_long, _U8]
     lib.oracle_mx_block.restype = ctypes.c_uint
-    lib.oracle_mx_block.argtypes = [_D, ctypes.c_int, ctypes.c_long, _U8, _D, ctypes.c_long]
+    lib.oracle_mx_block.argtypes = [_D, ctypes.c_int, ctypes.c_long, _U8, _D, ctypes.c_long,
+                                    ctypes.c_int]
     lib.oracle_quantize_rows.restype = None
     lib.oracle_quantize_rows.argtypes = [_F, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, _F, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_int, ctypes.c_int, _U8, _U8, _D]
+                                         ctypes.c_int, ctypes.c_int, _U8, _U8, _D, ctypes.c_int]
     lib.oracle_quantize_v.restype = None
     lib.oracle_quantize_v.argtypes = [_F, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, _U8, _U8, _D]
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, _U8, _U8, _D,
+                                      ctypes.c_int]
     lib.oracle_rope_rows.restype = None
     lib.oracle_rope_rows.argtypes = [_F, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      _F, _F, _F]
@@ -145,13 +148,16 @@ def e2m1_encode_array(y) -> np.ndarray:
     return out.reshape(y.shape)
 
 
-def mx_block(x) -> tuple[np.ndarray, int, np.ndarray]:
-    """Quantise one block of <= 32 values: (codes 0..15 per element, E8M0 byte, dequantised)."""
+def mx_block(x, rule: int = 0) -> tuple[np.ndarray, int, np.ndarray]:
+    """Quantise one block of <= 32 values: (codes 0..15 per element, E8M0 byte, dequantised).
+
+    rule 0: OCP MX shared exponent; rule 1: no-clip (one higher when amax > 6 * 2^e)."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
     n = x.size
     codes = np.zeros(n, dtype=np.uint8)
     deq = np.zeros(n, dtype=np.float64)
-    sc = _load().oracle_mx_block(_ptr(x, _D), n, 1, _ptr(codes, _U8), _ptr(deq, _D), 1)
+    sc = _load().oracle_mx_block(_ptr(x, _D), n, 1, _ptr(codes, _U8), _ptr(deq, _D), 1,
+                                 int(rule))
     return codes, int(sc), deq
 
 
@@ -160,7 +166,7 @@ def mx_block(x) -> tuple[np.ndarray, int, np.ndarray]:
 # --------------------------------------------------------------------------
 
 def quantize_rows(x, smooth=None, *, divide: bool, cap: int | None = None,
-                  quantise: bool = True):
+                  quantise: bool = True, rule: int = 0):
     """Q (divide=False) or K (divide=True) rows: x fp32 [B,H,S,d]; smooth [Hs,d] or None.
 
     Returns (codes [B,H,cap,d/2] u8, scales [B,H,cap,d/32] u8, deq [B,H,S,d] f64).
@@ -183,11 +189,11 @@ def quantize_rows(x, smooth=None, *, divide: bool, cap: int | None = None,
         scales = np.zeros((B, H, cap, d // 32), dtype=np.uint8)
     _load().oracle_quantize_rows(_ptr(x, _F), B, H, S, d, _ptr(sm, _F), group, int(divide),
                                  cap, int(quantise), _ptr(codes, _U8), _ptr(scales, _U8),
-                                 _ptr(deq, _D))
+                                 _ptr(deq, _D), int(rule))
     return codes, scales, deq
 
 
-def quantize_v(x, *, cap: int | None = None, quantise: bool = True):
+def quantize_v(x, *, cap: int | None = None, quantise: bool = True, rule: int = 0):
     """V: x fp32 [B,H,S,d] -> (codes [B,H,nblk,d,16], scales [B,H,nblk,d], deq [B,H,S,d])."""
     x = _f32(x)
     B, H, S, d = x.shape
@@ -199,7 +205,7 @@ def quantize_v(x, *, cap: int | None = None, quantise: bool = True):
         codes = np.zeros((B, H, nblk, d, 16), dtype=np.uint8)
         scales = np.zeros((B, H, nblk, d), dtype=np.uint8)
     _load().oracle_quantize_v(_ptr(x, _F), B, H, S, d, cap, int(quantise), _ptr(codes, _U8),
-                              _ptr(scales, _U8), _ptr(deq, _D))
+                              _ptr(scales, _U8), _ptr(deq, _D), int(rule))
     return codes, scales, deq
 
 
@@ -244,11 +250,12 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
               chunk: int = 0, quant_p: bool = True, br: int = 128, kv_lens=None, rows=None,
               chunk_phase=None,
               want_weights: bool = False, want_eps: bool = False, nthreads: int | None = None,
-              tau: float = 0.0):
+              tau: float = 0.0, p_rule: int = 0):
     """Online-softmax attention over dequantised (or exact) operands, fp64.
 
     q [B,Hq,Sq,d]; k, v [B,Hkv,Sk,d] (float64).  tau: lazy-rescale threshold
-    (log2 units, 0 = FlashAttention-2 frame).  chunk > 0 splits each row's keys
+    (log2 units, 0 = FlashAttention-2 frame).  p_rule: block-scale rule of
+    P_hat (0 OCP, 1 no-clip).  chunk > 0 splits each row's keys
     into runs that start from a fresh softmax state and are merged with the
     log-sum-exp rule; chunk_phase [B,Hkv] (keys, multiples of bc below chunk)
     shifts that grid: a run starts at every key t > 0 with (t + phase) % chunk
@@ -264,7 +271,7 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
     cfg = _AttnCfg(B, Hq, Hkv, Sq, Sk, d, int(causal),
                    float(sm_scale if sm_scale is not None else 1.0 / np.sqrt(d)),
                    int(bc), int(chunk), int(quant_p), int(br),
-                   int(nthreads or default_threads()), float(tau))
+                   int(nthreads or default_threads()), float(tau), int(p_rule))
     lens = None
     if kv_lens is not None:
         lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
@@ -312,7 +319,7 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
     return out
 
 
-def quantize_qkv(q, k, v, smooth=None, *, kv_cap: int | None = None):
+def quantize_qkv(q, k, v, smooth=None, *, kv_cap: int | None = None, rule: int = 0):
     """Smooth-QK + MXFP4 of all three operands, in the library's layouts.
 
     q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] fp32 (exact values of the bf16/fp16 inputs).
@@ -321,10 +328,11 @@ def quantize_qkv(q, k, v, smooth=None, *, kv_cap: int | None = None):
     """
     out = {}
     if q is not None:
-        out["q_codes"], out["q_scales"], out["q_deq"] = quantize_rows(q, smooth, divide=False)
+        out["q_codes"], out["q_scales"], out["q_deq"] = quantize_rows(q, smooth, divide=False,
+                                                                      rule=rule)
     if k is not None:
         out["k_codes"], out["k_scales"], out["k_deq"] = quantize_rows(k, smooth, divide=True,
-                                                                      cap=kv_cap)
+                                                                      cap=kv_cap, rule=rule)
     if v is not None:
-        out["v_codes"], out["v_scales"], out["v_deq"] = quantize_v(v, cap=kv_cap)
+        out["v_codes"], out["v_scales"], out["v_deq"] = quantize_v(v, cap=kv_cap, rule=rule)
     return out

@@ -101,10 +101,14 @@ void oracle_e2m1_encode_array(const double* y, long n, unsigned char* codes) {
 /* MX block quantisation of n <= 32 values x[k*stride].  Writes one 4-bit code
  * per element into codes[k] (value 0..15) and the dequantised value into
  * deq[k*deq_stride] when deq != NULL.  Returns the E8M0 scale byte.
- * Shared exponent: floor(log2(amax)) - 2, clamped to [-127, 127]; a block of
- * zeros gets exponent -127 (byte 0). */
+ * Shared exponent, rule 0 (OCP MX v1.0): floor(log2(amax)) - 2, clamped to
+ * [-127, 127]; a block of zeros gets exponent -127 (byte 0).  Elements above
+ * 6 * 2^e then saturate to +-6 (amax in (6, 8) * 2^e).
+ * Rule 1 (no-clip): the OCP exponent plus one whenever amax > 6 * 2^e, so that
+ * amax / 2^e <= 6 and no element saturates; every block whose amax / 2^e is at
+ * most 6 under the OCP rule keeps the OCP exponent and codes. */
 unsigned oracle_mx_block(const double* x, int n, long stride, unsigned char* codes,
-                         double* deq, long deq_stride) {
+                         double* deq, long deq_stride, int rule) {
   double amax = 0.0;
   for (int k = 0; k < n; k++) {
     double a = fabs(x[k * stride]);
@@ -118,6 +122,7 @@ unsigned oracle_mx_block(const double* x, int n, long stride, unsigned char* cod
     (void)frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
     e = ex - 1 - 2;
     if (e < -127) e = -127;
+    if (rule == 1 && amax > ldexp(6.0, e)) e += 1;
     if (e > 127) e = 127;
   }
   for (int k = 0; k < n; k++) {
@@ -145,7 +150,7 @@ unsigned oracle_mx_block(const double* x, int n, long stride, unsigned char* cod
  */
 void oracle_quantize_rows(const float* x, int B, int H, int S, int d, const float* smooth,
                           int group, int divide, int cap, int quantise, unsigned char* codes,
-                          unsigned char* scales, double* deq) {
+                          unsigned char* scales, double* deq, int rule) {
   double* row = (double*)malloc(sizeof(double) * (size_t)d);
   unsigned char blk[32];
   for (int b = 0; b < B; b++)
@@ -165,7 +170,7 @@ void oracle_quantize_rows(const float* x, int B, int H, int S, int d, const floa
         }
         size_t orow = ((size_t)b * H + h) * cap + t;
         for (int j0 = 0; j0 < d; j0 += 32) {
-          unsigned sc = oracle_mx_block(row + j0, 32, 1, blk, dq ? dq + j0 : NULL, 1);
+          unsigned sc = oracle_mx_block(row + j0, 32, 1, blk, dq ? dq + j0 : NULL, 1, rule);
           scales[orow * (d / 32) + j0 / 32] = (unsigned char)sc;
           for (int k = 0; k < 32; k += 2)
             codes[orow * (d / 2) + (j0 + k) / 2] = (unsigned char)(blk[k] | (blk[k + 1] << 4));
@@ -245,7 +250,7 @@ void oracle_smooth_calibrate(const double* q, const double* k, int B, int Hq, in
  * deq:    double [B][H][S][d] or NULL (with quantise == 0: the fp32 values)
  */
 void oracle_quantize_v(const float* x, int B, int H, int S, int d, int cap, int quantise,
-                       unsigned char* codes, unsigned char* scales, double* deq) {
+                       unsigned char* codes, unsigned char* scales, double* deq, int rule) {
   int nblk = (cap + 31) / 32;
   double col[32];
   double dqc[32];
@@ -264,7 +269,7 @@ void oracle_quantize_v(const float* x, int B, int H, int S, int d, int cap, int 
               for (int k = 0; k < n; k++) dh[(size_t)(t0 + k) * d + c] = col[k];
             continue;
           }
-          unsigned sc = oracle_mx_block(col, 32, 1, blk, dqc, 1);
+          unsigned sc = oracle_mx_block(col, 32, 1, blk, dqc, 1, rule);
           scales[blkrow * d + c] = (unsigned char)sc;
           for (int k = 0; k < 32; k += 2)
             codes[(blkrow * d + c) * 16 + k / 2] = (unsigned char)(blk[k] | (blk[k + 1] << 4));
@@ -291,6 +296,7 @@ typedef struct {
   double tau;      /* lazy-rescale threshold in log2 units: the running max moves to a
                       tile's row max only if that exceeds it by more than tau; 0 gives the
                       FlashAttention-2 frame (P <= 1) */
+  int p_rule;      /* block-scale rule of P_hat: 0 OCP, 1 no-clip (see oracle_mx_block) */
 } oracle_attn_cfg;
 
 typedef struct {
@@ -366,7 +372,7 @@ static void attn_row(attn_job* J, int b, int h, int i, size_t out, double* S, do
             long t = a0 + k;
             blk[k] = (t >= t0 && t < t1) ? P[t - t0] : 0.0;
           }
-          (void)oracle_mx_block(blk, 32, 1, codes, dq, 1);
+          (void)oracle_mx_block(blk, 32, 1, codes, dq, 1, c->p_rule);
           for (int k = 0; k < 32; k++) {
             long t = a0 + k;
             if (t >= t0 && t < t1) Ph[t - t0] = dq[k];

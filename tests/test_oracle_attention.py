@@ -54,8 +54,9 @@ def brute_attention(q, k, v, causal, sm_scale, kv_lens=None):
     return o, lse
 
 
-def mx_quantize_rows_np(p):
-    """Block quantiser written for the test: 32 columns per block, aligned to 0."""
+def mx_quantize_rows_np(p, rule=0):
+    """Block quantiser written for the test: 32 columns per block, aligned to 0.
+    rule 1 raises the exponent by one where the block maximum exceeds 6 * 2^e."""
     n, S = p.shape
     nb = -(-S // 32)
     pad = np.zeros((n, nb * 32))
@@ -64,6 +65,8 @@ def mx_quantize_rows_np(p):
     amax = np.abs(blk).max(axis=-1, keepdims=True)
     _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
     e = np.where(amax > 0, np.clip(ex - 1 - 2, -127, 127), -127)
+    if rule == 1:
+        e = np.where(amax > 6.0 * np.exp2(e), e + 1, e)
     y = np.minimum(np.abs(blk) / np.exp2(e), 6.0)
     dist = np.abs(y[..., None] - MAG)
     best = dist.min(axis=-1, keepdims=True)
@@ -123,18 +126,24 @@ def test_lazy_rescale_frame_hand_worked(tau, bc, rise):
     np.testing.assert_allclose(r["lse"][0, 0, 0], np.log(n + n * np.exp(rise)), rtol=1e-14)
 
 
+@pytest.mark.parametrize("p_rule", [0, 1])
 @pytest.mark.parametrize("Sk", [32, 75, 160])
-def test_single_tile_mxfp4_p_closed_form(Sk):
+def test_single_tile_mxfp4_p_closed_form(Sk, p_rule):
     rng = np.random.default_rng(Sk)
     Sq, d = 9, 64
     q = rng.standard_normal((1, 1, Sq, d)) * 2
     k = rng.standard_normal((1, 1, Sk, d))
     v = rng.standard_normal((1, 1, Sk, d))
     sm = 1.0 / np.sqrt(d)
-    r = oracle.attention(q, k, v, causal=False, sm_scale=sm, bc=4096, quant_p=True)
+    r = oracle.attention(q, k, v, causal=False, sm_scale=sm, bc=4096, quant_p=True,
+                         p_rule=p_rule)
     s = q[0, 0] @ k[0, 0].T * sm
     p = np.exp(s - s.max(axis=1, keepdims=True))
-    ph = mx_quantize_rows_np(p)
+    ph = mx_quantize_rows_np(p, p_rule)
+    # the block holding a row's maximum has max P = 1 = 4 * 2^-2 under either rule; with
+    # more blocks, some has its maximum in (6, 8) * 2^e and the rules differ
+    if p_rule == 1 and Sk > 32:
+        assert np.abs(ph - mx_quantize_rows_np(p, 0)).max() > 1e-3
     o = ph @ v[0, 0] / ph.sum(axis=1, keepdims=True)
     np.testing.assert_allclose(r["o"][0, 0], o, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(r["l"][0, 0], ph.sum(axis=1), rtol=1e-13)

@@ -61,6 +61,11 @@ MUTANTS = [
     ("calibration_over_all_query_heads", "for (int h = g * G; h < (g + 1) * G; h++) {",
      "for (int h = 0; h < Hq; h++) {", 0),
     ("calibration_ratio_inverted", "(float)pow(km / qm, alpha)", "(float)pow(qm / km, alpha)", 0),
+    ("noclip_rule_ignored", "if (rule == 1 && amax > ldexp(6.0, e)) e += 1;", "", 0),
+    ("noclip_boundary_inclusive", "if (rule == 1 && amax > ldexp(6.0, e)) e += 1;",
+     "if (rule == 1 && amax >= ldexp(6.0, e)) e += 1;", 0),
+    ("p_rule_not_passed", "(void)oracle_mx_block(blk, 32, 1, codes, dq, 1, c->p_rule);",
+     "(void)oracle_mx_block(blk, 32, 1, codes, dq, 1, 0);", 0),
     ("dot_product_drops_last_channel", "for (int j = 0; j < d; j++) s += qr[j] * kr[j];",
      "for (int j = 0; j < d - 1; j++) s += qr[j] * kr[j];", 0),
 ]
@@ -77,10 +82,15 @@ def _pin_checks():
     ]
     for name, x, sc, codes in TQ._golden_blocks():
         checks.append(lambda x=x, sc=sc, codes=codes, name=name: TQ.test_mx_block_golden(name, x, sc, codes))
+    for name, x, sc, codes in TQ._golden_blocks("mx_blocks_noclip.txt"):
+        checks.append(lambda x=x, sc=sc, codes=codes, name=name:
+                      TQ.test_mx_block_noclip_golden(name, x, sc, codes))
+    checks.append(TQ.test_mx_block_noclip_is_the_smallest_unsaturated_exponent)
     for case in TA.CASES:
         checks.append(lambda case=case: TA.test_exact_mode_equals_textbook_softmax(case, 64, 0.0))
     checks += [
-        lambda: TA.test_single_tile_mxfp4_p_closed_form(75),
+        lambda: TA.test_single_tile_mxfp4_p_closed_form(75, 0),
+        lambda: TA.test_single_tile_mxfp4_p_closed_form(160, 1),
         lambda: TA.test_lazy_rescale_frame_hand_worked(8.0, 64, 1.0),
         lambda: TA.test_lazy_rescale_frame_hand_worked(2.0, 32, 1.7),
         lambda: TA.test_smooth_qk_invariance_exact(True),

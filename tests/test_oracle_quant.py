@@ -6,7 +6,9 @@ Pins:
   * hand-worked E2M1 roundings (tests/golden/e2m1_rounding.txt);
   * a sweep of fp32 inputs around every rounding boundary and across every
     exponent, against a brute-force nearest-value search written here;
-  * hand-worked MX blocks (tests/golden/mx_blocks.txt);
+  * hand-worked MX blocks (tests/golden/mx_blocks.txt), and under the
+    no-clip exponent rule (tests/golden/mx_blocks_noclip.txt) with its
+    characterisation as the smallest unsaturated exponent;
   * idempotence and exact round trip of on-grid blocks;
   * hand-worked Smooth-QK direction (Q * s, K / s) and byte layouts.
 """
@@ -85,9 +87,9 @@ def test_e2m1_sweep_against_brute_force():
     assert bad.size == 0, [(y[i], got[i], want[i]) for i in bad[:10]]
 
 
-def _golden_blocks():
+def _golden_blocks(fname="mx_blocks.txt"):
     out = []
-    with open(os.path.join(GOLDEN, "mx_blocks.txt")) as f:
+    with open(os.path.join(GOLDEN, fname)) as f:
         for line in f:
             if not line.strip() or line.startswith("#"):
                 continue
@@ -112,6 +114,47 @@ def test_mx_block_golden(name, x, scale, codes):
     # dequantised value = signed E2M1 value * 2^(scale - 127)
     want_deq = np.array([MAG[c & 7] * (-1 if c & 8 else 1) for c in codes]) * 2.0 ** (scale - 127)
     np.testing.assert_array_equal(deq, want_deq)
+
+
+@pytest.mark.parametrize("name,x,scale,codes", _golden_blocks("mx_blocks_noclip.txt"),
+                         ids=lambda v: v if isinstance(v, str) else "")
+def test_mx_block_noclip_golden(name, x, scale, codes):
+    got_codes, got_scale, deq = oracle.mx_block(x, rule=1)
+    assert got_scale == scale
+    np.testing.assert_array_equal(got_codes, codes)
+    want_deq = np.array([MAG[c & 7] * (-1 if c & 8 else 1) for c in codes]) * 2.0 ** (scale - 127)
+    np.testing.assert_array_equal(deq, want_deq)
+
+
+def test_mx_block_noclip_is_the_smallest_unsaturated_exponent():
+    """The no-clip exponent X1 is the smallest X >= the OCP exponent X0 with
+    max|x| <= 6 * 2^X; then no element saturates and every element lies within
+    2^X1 of its dequantised value (half the widest E2M1 gap, 4 -> 6).  Where
+    X1 == X0 the codes are the OCP codes."""
+    rng = np.random.default_rng(23)
+    moved = 0
+    for trial in range(3000):
+        x = rng.standard_normal(32) * np.exp2(rng.integers(-60, 60))
+        if trial % 3 == 0:  # put the block maximum near 6 * 2^k
+            i = rng.integers(0, 32)
+            x[i] = np.sign(x[i] or 1.0) * np.abs(x).max() * rng.uniform(1.0, 1.6)
+        c0, s0, d0 = oracle.mx_block(x, rule=0)
+        c1, s1, d1 = oracle.mx_block(x, rule=1)
+        amax = np.abs(x).max()
+        x1 = s1 - 127
+        assert s1 - s0 in (0, 1)
+        assert amax <= 6.0 * 2.0 ** x1
+        if s1 > s0:
+            moved += 1
+            assert amax > 6.0 * 2.0 ** (s0 - 127)
+        else:
+            np.testing.assert_array_equal(c1, c0)
+        assert np.all(np.abs(d1 - x) <= 2.0 ** x1)
+        np.testing.assert_array_equal(c1 & 7, brute_force_e2m1(x / 2.0 ** x1) & 7)
+    assert moved > 300
+    # the OCP rule does saturate such a block: 7.9 -> 6
+    _, s, d = oracle.mx_block(np.array([7.9]), rule=0)
+    assert s == 127 and d[0] == 6.0
 
 
 def test_mx_block_idempotent_and_on_grid_round_trip():
