@@ -31,6 +31,8 @@ HIFA4_ERR_WORKSPACE_TOO_SMALL = -3
 HIFA4_ERR_HIP = -4
 HIFA4_BF16 = 0
 HIFA4_FP16 = 1
+SCALE_OCP = 0     # hifa4_scale_rule: OCP MX shared exponent
+SCALE_NOCLIP = 1  # one higher wherever OCP would saturate an element
 
 # Lazy-rescale threshold (log2 units) the benchmark and the full-size tests run
 # with: a row's running max moves only when a key tile raises it by more than
@@ -47,7 +49,8 @@ class HiFA4Error(RuntimeError):
 
 
 class MxTensorC(ctypes.Structure):
-    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("scale_rule", ctypes.c_int32)]
 
 
 class AttnParamsC(ctypes.Structure):
@@ -58,6 +61,7 @@ class AttnParamsC(ctypes.Structure):
         ("kv_stride", ctypes.c_int32), ("kv_lens", ctypes.c_void_p),
         ("decode_chunk", ctypes.c_int32), ("rescale_threshold", ctypes.c_float),
         ("normaliser", ctypes.c_int32),
+        ("scale_rule", ctypes.c_int32),
     ]
 
 class RopeC(ctypes.Structure):
@@ -178,9 +182,10 @@ class MXQKV:
     Sk: int
     d: int
     kv_stride: int
+    scale_rule: int = SCALE_OCP  # block-scale rule the quantise / append calls write with
 
 
-def alloc_mx(B, Hq, Hkv, Sq, kv_stride, d, device="cuda") -> MXQKV:
+def alloc_mx(B, Hq, Hkv, Sq, kv_stride, d, device="cuda", scale_rule=0) -> MXQKV:
     """Output buffers of hifa4_quantize_qkv (uninitialised device memory)."""
     nblk = (kv_stride + 31) // 32
     u8 = dict(dtype=torch.uint8, device=device)
@@ -188,7 +193,7 @@ def alloc_mx(B, Hq, Hkv, Sq, kv_stride, d, device="cuda") -> MXQKV:
                  torch.empty((B, Hkv, kv_stride, d // 2), **u8),
                  torch.empty((B, Hkv, kv_stride, d // 32), **u8),
                  torch.empty((B, Hkv, nblk, d, 16), **u8), torch.empty((B, Hkv, nblk, d), **u8),
-                 B, Hq, Hkv, Sq, 0, d, kv_stride)
+                 B, Hq, Hkv, Sq, 0, d, kv_stride, int(scale_rule))
 
 
 def _rope_struct(cos: torch.Tensor, sin: torch.Tensor, q_pos0: int, k_pos0: int) -> RopeC:
@@ -201,12 +206,14 @@ def _rope_struct(cos: torch.Tensor, sin: torch.Tensor, q_pos0: int, k_pos0: int)
 def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
                        v: Optional[torch.Tensor], smooth: Optional[torch.Tensor] = None, *,
                        kv_stride: int = 0, out: Optional[MXQKV] = None, Hkv: Optional[int] = None,
-                       stream=None) -> MXQKV:
+                       scale_rule: int = SCALE_OCP, stream=None) -> MXQKV:
     """Smooth-QK + MXFP4 quantisation; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] bf16 or fp16 on the GPU.
 
-    With k and v both None, pass Hkv (the smoothing rows are per KV head).
+    With k and v both None, pass Hkv (the smoothing rows are per KV head).  scale_rule
+    (SCALE_OCP or SCALE_NOCLIP) is recorded in the returned tensors.
     """
-    return _quantize(q, k, v, smooth, None, kv_stride=kv_stride, out=out, Hkv=Hkv, stream=stream)
+    return _quantize(q, k, v, smooth, None, kv_stride=kv_stride, out=out, Hkv=Hkv,
+                     scale_rule=scale_rule, stream=stream)
 
 
 def hifa4_quantize_qkv_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
@@ -214,16 +221,17 @@ def hifa4_quantize_qkv_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor]
                             q_pos0: int = 0, k_pos0: int = 0,
                             smooth: Optional[torch.Tensor] = None, kv_stride: int = 0,
                             out: Optional[MXQKV] = None, Hkv: Optional[int] = None,
-                            stream=None) -> MXQKV:
+                            scale_rule: int = SCALE_OCP, stream=None) -> MXQKV:
     """hifa4_quantize_qkv after rotate-half RoPE of Q and K with the tables cos / sin
     (float32 [n_pos, d/2] on the GPU); query token t sits at position q_pos0 + t, key
     token t at k_pos0 + t."""
     rope = _rope_struct(cos, sin, q_pos0, k_pos0)
     return _quantize(q, k, v, smooth, rope, kv_stride=kv_stride, out=out, Hkv=Hkv,
-                     stream=stream)
+                     scale_rule=scale_rule, stream=stream)
 
 
-def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, stream) -> MXQKV:
+def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, scale_rule,
+              stream) -> MXQKV:
     ref = next(t for t in (q, k, v) if t is not None)
     B, d = ref.shape[0], ref.shape[3]
     Hq, Sq = (q.shape[1], q.shape[2]) if q is not None else (1, 0)
@@ -245,15 +253,17 @@ def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, st
         out.Sq = Sq
     if kk is not None:
         out.Sk, out.kv_stride = Sk, cap
+    out.scale_rule = int(scale_rule)
+    r = out.scale_rule
     if smooth is not None and (smooth.dtype != torch.float32 or tuple(smooth.shape) != (Hkv, d)):
         raise ValueError("smooth must be float32 [Hkv, d]")
     lib = load_library()
     mq = MxTensorC(_ptr(out.q_codes) if q is not None else None,
-                   _ptr(out.q_scales) if q is not None else None)
+                   _ptr(out.q_scales) if q is not None else None, r)
     mk = MxTensorC(_ptr(out.k_codes) if k is not None else None,
-                   _ptr(out.k_scales) if k is not None else None)
+                   _ptr(out.k_scales) if k is not None else None, r)
     mv = MxTensorC(_ptr(out.v_codes) if v is not None else None,
-                   _ptr(out.v_scales) if v is not None else None)
+                   _ptr(out.v_scales) if v is not None else None, r)
     if rope is None:
         _check(lib.hifa4_quantize_qkv(_ptr(q), _ptr(k), _ptr(v), _dtype_code(ref.dtype), B, Hq,
                                       Hkv, Sq, Sk, kv_stride, d, _ptr(smooth), mq, mk, mv,
@@ -280,7 +290,8 @@ def hifa4_kv_append(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
     (int32 [B] on the GPU) after RoPE (cos / sin, optional) and Smooth-QK; q [B,Hq,n,d]
     (optional) is quantised into cache.q_codes / q_scales at the same positions.
     kv_lens_out (int32 [B]) receives the new lengths.  Returns cache with Sq = n and
-    Sk = its capacity (the upper bound the decode attention takes with kv_lens)."""
+    Sk = its capacity (the upper bound the decode attention takes with kv_lens).  New blocks
+    take cache.scale_rule."""
     if k.dim() != 4 or v.shape != k.shape or k.dtype != v.dtype:
         raise ValueError("k and v must be 4-d tensors of one shape and dtype")
     B, Hkv, n, d = k.shape
@@ -300,12 +311,13 @@ def hifa4_kv_append(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
         if cos is None or sin is None:
             raise ValueError("give both rope tables or neither")
         rope = ctypes.byref(_rope_struct(cos, sin, q_pos0, k_pos0))
-    mq = MxTensorC(_ptr(cache.q_codes), _ptr(cache.q_scales)) if q is not None else MxTensorC()
+    r = cache.scale_rule
+    mq = MxTensorC(_ptr(cache.q_codes), _ptr(cache.q_scales), r) if q is not None else MxTensorC()
     _check(load_library().hifa4_kv_append(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(k.dtype), B, Hq, Hkv, n, cache.kv_stride, d,
         _ptr(kv_lens), _ptr(kv_lens_out), _ptr(smooth), rope, _ptr(v_tail), mq,
-        MxTensorC(_ptr(cache.k_codes), _ptr(cache.k_scales)),
-        MxTensorC(_ptr(cache.v_codes), _ptr(cache.v_scales)), _stream(stream)))
+        MxTensorC(_ptr(cache.k_codes), _ptr(cache.k_scales), r),
+        MxTensorC(_ptr(cache.v_codes), _ptr(cache.v_scales), r), _stream(stream)))
     cache.Sq, cache.Sk = n, cache.kv_stride
     return cache
 
@@ -346,11 +358,12 @@ def hifa4_smooth_calibrate(q: torch.Tensor, k: torch.Tensor, alpha: float, *,
 
 
 def make_params(B, Hq, Hkv, Sq, Sk, d, *, causal, sm_scale=None, kv_stride=0, kv_lens=None,
-                decode_chunk=0, rescale_threshold=0.0, normaliser=0) -> AttnParamsC:
+                decode_chunk=0, rescale_threshold=0.0, normaliser=0,
+                scale_rule=0) -> AttnParamsC:
     return AttnParamsC(B, Hq, Hkv, Sq, Sk, d, 1 if causal else 0,
                        float(sm_scale) if sm_scale else 0.0, kv_stride,
                        _ptr(kv_lens) if kv_lens is not None else None, decode_chunk,
-                       float(rescale_threshold), int(normaliser))
+                       float(rescale_threshold), int(normaliser), int(scale_rule))
 
 
 def hifa4_attn_workspace_size(params: AttnParamsC) -> int:
@@ -373,13 +386,15 @@ def hifa4_attn_fwd(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,
                    out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                    lse: Optional[torch.Tensor] = None, want_lse: bool = True,
                    workspace: Optional[torch.Tensor] = None, rescale_threshold: float = 0.0,
-                   normaliser: int = 0, stream=None):
-    """Fused MXFP4 attention on quantised operands; returns (out, lse or None)."""
+                   normaliser: int = 0, scale_rule: int = SCALE_OCP, stream=None):
+    """Fused MXFP4 attention on quantised operands; returns (out, lse or None).
+    scale_rule: block-scale rule of P_hat."""
     if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != mx.B):
         raise ValueError("kv_lens must be int32 [B]")
     p = make_params(mx.B, mx.Hq, mx.Hkv, mx.Sq, mx.Sk, mx.d, causal=causal, sm_scale=sm_scale,
                     kv_stride=mx.kv_stride, kv_lens=kv_lens, decode_chunk=decode_chunk,
-                    rescale_threshold=rescale_threshold, normaliser=normaliser)
+                    rescale_threshold=rescale_threshold, normaliser=normaliser,
+                    scale_rule=scale_rule)
     dev = mx.q_codes.device
     if out is None:
         out = torch.empty((mx.B, mx.Hq, mx.Sq, mx.d), dtype=out_dtype, device=dev)
@@ -402,9 +417,11 @@ def hifa4_attn_fwd_qraw(q: torch.Tensor, smooth: Optional[torch.Tensor], mx: MXQ
                         causal: bool, sm_scale: Optional[float] = None,
                         out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
                         lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                        rescale_threshold: float = 0.0, normaliser: int = 0, stream=None):
+                        rescale_threshold: float = 0.0, normaliser: int = 0,
+                        scale_rule: int = SCALE_OCP, stream=None):
     """Prefill with Q as bf16 / fp16 activations [B,Hq,Sq,d], smoothed and quantised inside
-    the kernel; mx holds the quantised K and V (its Q fields are not read).
+    the kernel; mx holds the quantised K and V (its Q fields are not read).  scale_rule
+    governs both P_hat and the in-kernel Q blocks.
     Returns (out, lse or None)."""
     B, Hq, Sq, d = q.shape
     if q.dtype not in (torch.bfloat16, torch.float16) or not q.is_contiguous():
@@ -415,7 +432,7 @@ def hifa4_attn_fwd_qraw(q: torch.Tensor, smooth: Optional[torch.Tensor], mx: MXQ
         raise ValueError("smooth must be float32 [Hkv, d]")
     p = make_params(B, Hq, mx.Hkv, Sq, mx.Sk, d, causal=causal, sm_scale=sm_scale,
                     kv_stride=mx.kv_stride, rescale_threshold=rescale_threshold,
-                    normaliser=normaliser)
+                    normaliser=normaliser, scale_rule=scale_rule)
     if out is None:
         out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:

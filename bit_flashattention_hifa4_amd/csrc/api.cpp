@@ -65,6 +65,14 @@ int64_t row_codes_bytes(int64_t rows, int d) { return rows * (d / 2); }
 int64_t row_scales_bytes(int64_t rows, int d) { return rows * (d / 32); }
 int64_t col_blocks(int64_t heads, int cap) { return heads * ((cap + 31) / 32); }
 
+// Kernel bias of a block-scale rule (hifa4_scale_rule); false for an unknown rule.
+bool scale_bias(int32_t rule, uint32_t* bias) {
+  if (rule == HIFA4_SCALE_OCP) *bias = hifa4::kScaleBiasOcp;
+  else if (rule == HIFA4_SCALE_NOCLIP) *bias = hifa4::kScaleBiasNoClip;
+  else return false;
+  return true;
+}
+
 // Shared validation of the attention parameter block.
 hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
   if (!p) return fail(HIFA4_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -82,6 +90,9 @@ hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
   if (p->normaliser != 0 && p->normaliser != 1)
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "normaliser %d (0: P-Reordering, 1: direct)",
                 p->normaliser);
+  uint32_t bias;
+  if (!scale_bias(p->scale_rule, &bias))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "scale_rule %d (0: OCP, 1: no-clip)", p->scale_rule);
   *cap = p->kv_stride ? p->kv_stride : p->Sk;
   if (*cap < p->Sk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_stride %d < Sk %d", *cap, p->Sk);
   if (p->kv_lens && p->Sq != 1)
@@ -206,6 +217,8 @@ static hifa4_status attn_fwd_impl(const hifa4_attn_params* p, hifa4_mx_tensor q,
   a.dec_waves = hifa4::attn_decode_waves(d);
   a.tau = p->rescale_threshold;
   a.direct_l = p->normaliser;
+  scale_bias(p->scale_rule, &a.p_bias);  // checked in check_params
+  a.q_bias = a.p_bias;
   hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
                             : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported)
@@ -288,6 +301,10 @@ hifa4_status quantize_impl(const void* q, const void* k, const void* v, hifa4_dt
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "k given but k_out has a NULL buffer");
   if (v && (!v_out.codes || !v_out.scales))
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "v given but v_out has a NULL buffer");
+  uint32_t qb = 0, kb = 0, vb = 0;
+  if ((q && !scale_bias(q_out.scale_rule, &qb)) || (k && !scale_bias(k_out.scale_rule, &kb)) ||
+      (v && !scale_bias(v_out.scale_rule, &vb)))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "unknown scale_rule in an output (0: OCP, 1: no-clip)");
 
   const int64_t rq = (int64_t)B * Hq * Sq, rk = (int64_t)B * Hkv * Sk;
   const int64_t rcap = (int64_t)B * Hkv * cap;
@@ -321,6 +338,9 @@ hifa4_status quantize_impl(const void* q, const void* k, const void* v, hifa4_dt
   a.smooth = smooth;
   a.q_codes = q_out.codes;
   a.q_scales = q_out.scales;
+  a.q_bias = qb;
+  a.k_bias = kb;
+  a.v_bias = vb;
   a.k_codes = k_out.codes;
   a.k_scales = k_out.scales;
   a.v_codes = v_out.codes;
@@ -402,6 +422,10 @@ hifa4_status hifa4_kv_append(const void* q, const void* k, const void* v, hifa4_
     if (r.p && !aligned16(r.p))
       return fail(HIFA4_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", r.name);
   }
+  uint32_t qb = 0, kb = 0, vb = 0;
+  if ((q && !scale_bias(q_out.scale_rule, &qb)) || !scale_bias(k_cache.scale_rule, &kb) ||
+      !scale_bias(v_cache.scale_rule, &vb))
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "unknown scale_rule in an output (0: OCP, 1: no-clip)");
   Span in[] = {{"q", q, (int64_t)B * Hq * n_new * d * 2},
                {"k", k, (int64_t)B * Hkv * n_new * d * 2},
                {"v", v, (int64_t)B * Hkv * n_new * d * 2},
@@ -456,6 +480,9 @@ hifa4_status hifa4_kv_append(const void* q, const void* k, const void* v, hifa4_
   a.k_scales = k_cache.scales;
   a.v_codes = v_cache.codes;
   a.v_scales = v_cache.scales;
+  a.q_bias = qb;
+  a.k_bias = kb;
+  a.v_bias = vb;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -593,6 +620,8 @@ hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void
   if (p && p->decode_chunk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "bf16_attn_fwd takes no decode_chunk");
   if (p && p->normaliser)
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "bf16_attn_fwd has no normaliser variant");
+  if (p && p->scale_rule)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "bf16_attn_fwd quantises nothing (scale_rule must be 0)");
   hifa4_attn_params pp;
   if (p) {
     pp = *p;

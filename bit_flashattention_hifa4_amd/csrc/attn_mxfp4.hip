@@ -161,14 +161,14 @@ __device__ __forceinline__ SoftmaxMax softmax_max(const v16f& s0, const v16f& s1
 // `pk` is the previous step's packed P: every byte of it is overwritten, it
 // only gives the partial-write converts a register to start from.
 __device__ __forceinline__ SoftmaxStep softmax_exp(v16f& s0, v16f& s1, const SoftmaxMax& x,
-                                                   float c, uint4& pk) {
+                                                   float c, uint32_t p_bias, uint4& pk) {
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -x.m_use));
     s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -x.m_use));
   }
   const float pmax = fast_exp2(x.bmc - x.m_use);
-  const uint32_t sb = e8m0_from_amax(pmax);
+  const uint32_t sb = e8m0_from_amax(pmax, p_bias);
   SoftmaxStep st;
   st.alpha = x.alpha;
   st.p_scale = (int)sb;
@@ -192,9 +192,9 @@ __device__ __forceinline__ SoftmaxStep softmax_exp(v16f& s0, v16f& s1, const Sof
 
 // Whole step (decode): max phase then exp phase.
 __device__ __forceinline__ SoftmaxStep softmax_step(v16f& s0, v16f& s1, float& m_run, float c,
-                                                    float tau, uint4& pk) {
+                                                    float tau, uint32_t p_bias, uint4& pk) {
   const SoftmaxMax x = softmax_max(s0, s1, m_run, c, tau);
-  return softmax_exp(s0, s1, x, c, pk);
+  return softmax_exp(s0, s1, x, c, p_bias, pk);
 }
 
 // Mask keys >= lim (key of element (t, r) is kb + 16t + r) with -inf.  The
@@ -560,7 +560,7 @@ constexpr int prefill_min_blocks() { return D >= 256 ? 1 : 2; }  // also used by
 // convert), so the codes are bit-identical.  The scale byte of block 2j + h
 // goes to byte h + 2 (j % 2) of word j / 2, the quantise kernel's row layout
 // as the lane reads it.
-template <int D, bool kBf16>
+template <int D, bool kBf16, uint32_t kQBias>
 __device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, int hs, int h,
                                                 uint4 (&qa)[D / 64],
                                                 uint32_t (&qsw_raw)[(D / 64 + 1) / 2]) {
@@ -598,7 +598,7 @@ __device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, 
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
-    const uint32_t sb = e8m0_from_amax(amax);
+    const uint32_t sb = e8m0_from_amax(amax, kQBias);
     const float scale = e8m0_to_float(sb);
     uint32_t wd[4];
 #pragma unroll
@@ -612,7 +612,10 @@ __device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, 
   }
 }
 
-template <int D, bool kCausal, bool kDirect>
+// kQNoClip: the block-scale rule of Q quantised in the prologue, a template
+// parameter rather than a kernel argument (reading the rule there at run time
+// cost about 3% of the whole kernel's time on the Qwen3-8B-shaped layer).
+template <int D, bool kCausal, bool kDirect, bool kQNoClip>
 __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_kernel(
     AttnArgs a, int ones_scale) {
   using T = PrefillTile<D>;
@@ -690,9 +693,11 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   if (q < a.Sq && a.q_raw) {
     // Q from the activations: smoothed and quantised here
     if (a.q_raw_bf16)
-      quantise_q_lane<D, true>(a, bhq * a.Sq + q, g, h, qa, qsw_raw);
+      quantise_q_lane<D, true, kQNoClip ? kScaleBiasNoClip : kScaleBiasOcp>(a, bhq * a.Sq + q, g,
+                                                                           h, qa, qsw_raw);
     else
-      quantise_q_lane<D, false>(a, bhq * a.Sq + q, g, h, qa, qsw_raw);
+      quantise_q_lane<D, false, kQNoClip ? kScaleBiasNoClip : kScaleBiasOcp>(a, bhq * a.Sq + q, g,
+                                                                            h, qa, qsw_raw);
   } else if (q < a.Sq) {
     const uint8_t* qc = a.q_codes + (bhq * a.Sq + q) * DB;
     const uint8_t* qsc = a.q_scales + (bhq * a.Sq + q) * DS;
@@ -793,7 +798,7 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
 
     qk_mfma<D>(ko, qa, qsw, n0r, n1r);
     pv_mfma(vo, pend_p, pend_s);
-    SoftmaxStep st = softmax_exp(c0, c1, sx, c, pk);
+    SoftmaxStep st = softmax_exp(c0, c1, sx, c, a.p_bias, pk);
     if constexpr (kDirect) l_direct = __builtin_fmaf(l_direct, st.alpha, row_sum_p(c0, c1));
 #pragma unroll
     for (int i = 0; i < NJ * 2 + NC + (kDirect ? 0 : 1); i++) {
@@ -1209,7 +1214,7 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
 
       const bool pair_end = cc.lt + 1 == cc.nt;
       if (pair_end && (cc.L & (kBN - 1))) mask_scores(s_lo, s_hi, cc.lt * kBN + 32 * h, cc.L);
-      const SoftmaxStep sm = softmax_step(s_lo, s_hi, m_run, c, a.tau, pk);
+      const SoftmaxStep sm = softmax_step(s_lo, s_hi, m_run, c, a.tau, a.p_bias, pk);
       if constexpr (kDirect) l_direct = __builtin_fmaf(l_direct, sm.alpha, row_sum_p(s_lo, s_hi));
       if (__any(sm.alpha != 1.0f)) {
 #pragma unroll
@@ -1327,6 +1332,22 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
 // see its scale operands as integer registers, not as a folded constant.
 constexpr int kScaleOne = 127;
 
+template <int D, bool kQNoClip>
+void launch_prefill_rule(const AttnArgs& a, dim3 g, dim3 b, hipStream_t stream) {
+  if (a.causal && !a.direct_l)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, true, false, kQNoClip>), g, b, 0, stream, a,
+                       kScaleOne);
+  else if (!a.direct_l)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, false, false, kQNoClip>), g, b, 0, stream, a,
+                       kScaleOne);
+  else if (a.causal)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, true, true, kQNoClip>), g, b, 0, stream, a,
+                       kScaleOne);
+  else
+    hipLaunchKernelGGL((attn_prefill_kernel<D, false, true, kQNoClip>), g, b, 0, stream, a,
+                       kScaleOne);
+}
+
 template <int D>
 hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
   const int n_qt = (a.Sq + kBR - 1) / kBR;
@@ -1334,14 +1355,11 @@ hipError_t launch_prefill_d(const AttnArgs& a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), b(256);
-  if (a.causal && !a.direct_l)
-    hipLaunchKernelGGL((attn_prefill_kernel<D, true, false>), g, b, 0, stream, a, kScaleOne);
-  else if (!a.direct_l)
-    hipLaunchKernelGGL((attn_prefill_kernel<D, false, false>), g, b, 0, stream, a, kScaleOne);
-  else if (a.causal)
-    hipLaunchKernelGGL((attn_prefill_kernel<D, true, true>), g, b, 0, stream, a, kScaleOne);
+  // the no-clip Q instances only matter when Q is quantised in the prologue
+  if (a.q_raw && a.q_bias == kScaleBiasNoClip)
+    launch_prefill_rule<D, true>(a, g, b, stream);
   else
-    hipLaunchKernelGGL((attn_prefill_kernel<D, false, true>), g, b, 0, stream, a, kScaleOne);
+    launch_prefill_rule<D, false>(a, g, b, stream);
   return hipGetLastError();
 }
 

@@ -36,11 +36,15 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(const v8s& a, const v8s& b, c
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// E8M0 byte of the OCP MX shared exponent floor(log2(amax)) - 2 for a
-// non-negative finite fp32 amax: the fp32 exponent field minus 2, floored at 0
-// (zero and tiny blocks get exponent -127).
-__device__ __forceinline__ uint32_t e8m0_from_amax(float amax) {
-  int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+// E8M0 byte of a block's shared exponent for a non-negative finite fp32 amax:
+// with bias 0 the OCP MX exponent floor(log2(amax)) - 2, i.e. the fp32
+// exponent field minus 2, floored at 0 (zero and tiny blocks get exponent
+// -127).  A bias of 2^22 - 1 (the no-clip rule) carries into the exponent
+// field exactly when the mantissa exceeds 1.5, i.e. when amax > 6 * 2^X for
+// that OCP exponent X, so the exponent rises by one precisely where an element
+// would otherwise saturate at 6.
+__device__ __forceinline__ uint32_t e8m0_from_amax(float amax, uint32_t bias) {
+  int ef = (int)((__float_as_uint(amax) + bias) >> 23);
   return (uint32_t)max(ef - 2, 0);
 }
 

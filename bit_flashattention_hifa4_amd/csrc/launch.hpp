@@ -7,6 +7,12 @@
 
 namespace hifa4 {
 
+// Block-scale rules, as the bias the kernels add to a block maximum's fp32 bit
+// pattern before taking its exponent field: the OCP MX shared exponent, or the
+// no-clip one (one higher wherever the OCP exponent would saturate an element).
+constexpr uint32_t kScaleBiasOcp = 0u;
+constexpr uint32_t kScaleBiasNoClip = 0x003FFFFFu;
+
 struct QuantizeArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -25,6 +31,7 @@ struct QuantizeArgs {
   const float* rope_cos;       // rotate-half RoPE tables [n_pos][d/2] for Q and K, or null
   const float* rope_sin;
   int q_pos0, k_pos0;          // position of token 0 of Q / K in the tables
+  uint32_t q_bias, k_bias, v_bias;  // block-scale rule of each output (kScaleBias*)
 };
 
 hipError_t launch_quantize_qkv(QuantizeArgs a, bool bf16, hipStream_t stream);
@@ -48,6 +55,7 @@ struct AppendArgs {
   uint8_t* v_scales;
   int B, Hq, Hkv, n_new, d, cap;
   int n_pos, q_pos0, k_pos0;
+  uint32_t q_bias, k_bias, v_bias;  // block-scale rule of each output (kScaleBias*)
   int64_t blocks_q, blocks_k, wg_q, wg_k, items_v;  // filled by the launcher
 };
 
@@ -91,6 +99,8 @@ struct AttnArgs {
   int dec_waves;           // decode: waves of the persistent grid
   float tau;               // lazy-rescale threshold, log2 units (0 = every increase)
   int direct_l;            // 1: l = sum of the fp32 P (vector ALU), 0: P-Reordering
+  uint32_t p_bias;         // block-scale rule of P_hat (kScaleBias*)
+  uint32_t q_bias;         // with q_raw: block-scale rule of the in-kernel Q quantisation
 };
 
 // Key tile width of the online-softmax frame for a head dim.

@@ -120,7 +120,7 @@ struct AppendRows {
 template <bool kBf16, int D, bool kRope, bool kAppend = false>
 __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
                                               const float* __restrict__ s, bool divide,
-                                              uint32_t part0, uint32_t n_parts, uint32_t H,
+                                              uint32_t bias, uint32_t part0, uint32_t n_parts, uint32_t H,
                                               uint32_t S, uint32_t group, uint32_t cap,
                                               uint8_t* __restrict__ codes,
                                               uint8_t* __restrict__ scales,
@@ -190,7 +190,7 @@ __device__ __forceinline__ void quantise_rows(const uint16_t* __restrict__ x,
     amax = fmaxf(amax, quad_xor(amax, 0xB1));  // lanes 1,0,3,2
     amax = fmaxf(amax, quad_xor(amax, 0x4E));  // lanes 2,3,0,1
     if (!rp[r].ok) continue;
-    const uint32_t sb = e8m0_from_amax(amax);
+    const uint32_t sb = e8m0_from_amax(amax, bias);
     *reinterpret_cast<uint32_t*>(codes + (size_t)rp[r].orow * (D / 2) + rp[r].j0 / 2) =
         encode8(v, e8m0_to_float(sb));
     if ((rp[r].j0 & 31u) == 0) scales[(size_t)rp[r].orow * NB + rp[r].j0 / 32] = (uint8_t)sb;
@@ -203,7 +203,7 @@ template <bool kBf16, int D>
 __device__ __forceinline__ void quantise_v_pair(const uint16_t* __restrict__ x, uint32_t item,
                                                 uint32_t S, uint32_t cap,
                                                 uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales) {
+                                                uint8_t* __restrict__ scales, uint32_t bias) {
   constexpr uint32_t HALF = D / 2;
   const uint32_t nblk_valid = (S + 31) / 32;
   const uint32_t c = item % HALF;
@@ -226,7 +226,7 @@ __device__ __forceinline__ void quantise_v_pair(const uint16_t* __restrict__ x, 
     ma = fmaxf(ma, fabsf(a[k]));
     mb = fmaxf(mb, fabsf(b[k]));
   }
-  const uint32_t sa = e8m0_from_amax(ma), sbb = e8m0_from_amax(mb);
+  const uint32_t sa = e8m0_from_amax(ma, bias), sbb = e8m0_from_amax(mb, bias);
   const float fa = e8m0_to_float(sa), fb = e8m0_to_float(sbb);
   uint32_t ca[4], cb[4];
 #pragma unroll
@@ -256,15 +256,15 @@ __global__ __launch_bounds__(kThreads) void quantize_qkv_kernel(QuantizeArgs a) 
   if (wg < wg_v) {
     const uint32_t item = wg * kThreads + threadIdx.x;
     if (item < (uint32_t)a.items_v)
-      quantise_v_pair<kBf16, D>(a.v, item, a.Sk, a.cap, a.v_codes, a.v_scales);
+      quantise_v_pair<kBf16, D>(a.v, item, a.Sk, a.cap, a.v_codes, a.v_scales, a.v_bias);
   } else if (wg < wg_v + wg_k) {
     const uint32_t part0 = (wg - wg_v) * kThreads * kRowParts + threadIdx.x;
-    quantise_rows<kBf16, D, kRope>(a.k, a.smooth, true, part0, (uint32_t)(4 * a.blocks_k), a.Hkv,
+    quantise_rows<kBf16, D, kRope>(a.k, a.smooth, true, a.k_bias, part0, (uint32_t)(4 * a.blocks_k), a.Hkv,
                                    a.Sk, 1, a.cap, a.k_codes, a.k_scales, a.rope_cos,
                                    a.rope_sin, (uint32_t)a.k_pos0);
   } else {
     const uint32_t part0 = (wg - wg_v - wg_k) * kThreads * kRowParts + threadIdx.x;  // 4 parts per block
-    quantise_rows<kBf16, D, kRope>(a.q, a.smooth, false, part0, (uint32_t)(4 * a.blocks_q), a.Hq,
+    quantise_rows<kBf16, D, kRope>(a.q, a.smooth, false, a.q_bias, part0, (uint32_t)(4 * a.blocks_q), a.Hq,
                                    a.Sq, a.Hq / a.Hkv, a.Sq, a.q_codes, a.q_scales, a.rope_cos,
                                    a.rope_sin, (uint32_t)a.q_pos0);
   }
@@ -326,7 +326,7 @@ __device__ __forceinline__ void append_v_pair(const AppendArgs& a, uint32_t item
       ma = fmaxf(ma, fabsf(va[k]));
       mb = fmaxf(mb, fabsf(vb[k]));
     }
-    const uint32_t sa = e8m0_from_amax(ma), sbb = e8m0_from_amax(mb);
+    const uint32_t sa = e8m0_from_amax(ma, a.v_bias), sbb = e8m0_from_amax(mb, a.v_bias);
     const float fa = e8m0_to_float(sa), fb = e8m0_to_float(sbb);
     uint32_t ca[4], cb[4];
 #pragma unroll
@@ -364,13 +364,13 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a) {
   } else if (wg < wg_v + wg_k) {
     const uint32_t part0 = (wg - wg_v) * kThreads * kRowParts + threadIdx.x;
     quantise_rows<kBf16, D, kRope, true>(
-        a.k, a.smooth, true, part0, (uint32_t)(4 * a.blocks_k), a.Hkv, a.n_new, 1, a.cap,
+        a.k, a.smooth, true, a.k_bias, part0, (uint32_t)(4 * a.blocks_k), a.Hkv, a.n_new, 1, a.cap,
         a.k_codes, a.k_scales, a.rope_cos, a.rope_sin, (uint32_t)a.k_pos0,
         AppendRows{a.lens, (uint32_t)a.cap, true, max_pos});
   } else {
     const uint32_t part0 = (wg - wg_v - wg_k) * kThreads * kRowParts + threadIdx.x;
     quantise_rows<kBf16, D, kRope, true>(
-        a.q, a.smooth, false, part0, (uint32_t)(4 * a.blocks_q), a.Hq, a.n_new, a.Hq / a.Hkv,
+        a.q, a.smooth, false, a.q_bias, part0, (uint32_t)(4 * a.blocks_q), a.Hq, a.n_new, a.Hq / a.Hkv,
         a.n_new, a.q_codes, a.q_scales, a.rope_cos, a.rope_sin, (uint32_t)a.q_pos0,
         AppendRows{a.lens, (uint32_t)a.cap, false, max_pos});
   }

@@ -69,7 +69,19 @@ typedef enum hifa4_dtype { HIFA4_BF16 = 0, HIFA4_FP16 = 1 } hifa4_dtype;
 typedef struct hifa4_mx_tensor {
   uint8_t* codes;
   uint8_t* scales;
+  int32_t scale_rule; /* hifa4_scale_rule the scales are computed with where this tensor is an
+                         output (quantise, append); ignored where it is an attention input */
 } hifa4_mx_tensor;
+
+/* Shared-exponent rule of a 32-element block with maximum magnitude amax.
+ * OCP: the OCP MX v1.0 exponent X = floor(log2(amax)) - 2 (clamped to the
+ * E8M0 range; 0 for an all-zero block); elements above 6 * 2^X saturate to 6.
+ * NOCLIP: X + 1 wherever amax > 6 * 2^X, else X: the smallest exponent at or
+ * above the OCP one at which no element saturates.  The abstract of "HiFA4:
+ * Training-Free 4-bit FlashAttention on Ascend HIF4 NPUs for LLM Inference"
+ * names a 4-bit block format without defining it; OCP MXFP4 stands in for it
+ * and NOCLIP is a variant of that stand-in. */
+typedef enum hifa4_scale_rule { HIFA4_SCALE_OCP = 0, HIFA4_SCALE_NOCLIP = 1 } hifa4_scale_rule;
 
 typedef struct hifa4_attn_params {
   int32_t B;          /* batch */
@@ -97,6 +109,9 @@ typedef struct hifa4_attn_params {
                                column.  1: the non-reordered form the pages compare it
                                with: l = sum(P) of the fp32 P before quantisation, summed
                                on the vector ALU, numerator still P_hat V.  Must be 0 for
+                               bf16_attn_fwd. */
+  int32_t scale_rule;       /* hifa4_scale_rule of the blocks the attention call quantises
+                               itself: P_hat, and Q in hifa4_attn_fwd_qraw.  Must be 0 for
                                bf16_attn_fwd. */
 } hifa4_attn_params;
 

@@ -64,6 +64,10 @@ def _quant(lib, **kw):
     (dict(q=None, k=None, v=None), hb.HIFA4_ERR_INVALID_ARGUMENT, "all NULL"),
     (dict(ko=_mx(A + 0x100)), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlaps"),
     (dict(vo=hb.MxTensorC(0x20000000, 0x61000000)), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlap"),
+    (dict(ko=hb.MxTensorC(0x40000000, 0x41000000, 2)), hb.HIFA4_ERR_INVALID_ARGUMENT,
+     "scale_rule"),
+    (dict(qo=hb.MxTensorC(0x20000000, 0x21000000, -1)), hb.HIFA4_ERR_INVALID_ARGUMENT,
+     "scale_rule"),
 ])
 def test_quantize_rejects_bad_arguments(lib, kw, status, msg):
     assert _quant(lib, **kw) == status
@@ -145,6 +149,8 @@ def _append(lib, rope=None, **kw):
     (None, dict(lens_out=0x9000000), hb.HIFA4_ERR_INVALID_ARGUMENT, "kv_lens_out overlaps input kv_lens"),
     (None, dict(tail=0x40000100), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlap"),
     (None, dict(kc=_mx(A + 0x40)), hb.HIFA4_ERR_INVALID_ARGUMENT, "overlaps input q"),
+    (None, dict(vc=hb.MxTensorC(0x60000000, 0x61000000, 3)), hb.HIFA4_ERR_INVALID_ARGUMENT,
+     "scale_rule"),
     (dict(n_pos=0), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "n_pos >= 1"),
     (dict(cos=None), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "table is NULL"),
     (dict(q_pos0=0x7FFFFF00), {}, hb.HIFA4_ERR_INVALID_ARGUMENT, "overflow"),
@@ -205,12 +211,13 @@ def test_calibrate_workspace_size(lib):
 
 def _params(**kw):
     p = dict(B=2, Hq=8, Hkv=2, Sq=128, Sk=128, d=128, causal=True, sm_scale=None, kv_stride=0,
-             kv_lens=None, decode_chunk=0, normaliser=0)
+             kv_lens=None, decode_chunk=0, normaliser=0, scale_rule=0)
     p.update(kw)
     lens = p.pop("kv_lens")
     params = hb.make_params(**{k: p[k] for k in ("B", "Hq", "Hkv", "Sq", "Sk", "d")},
                             causal=p["causal"], sm_scale=p["sm_scale"], kv_stride=p["kv_stride"],
-                            decode_chunk=p["decode_chunk"], normaliser=p["normaliser"])
+                            decode_chunk=p["decode_chunk"], normaliser=p["normaliser"],
+                            scale_rule=p["scale_rule"])
     if lens is not None:
         params.kv_lens = lens
     return params
@@ -263,6 +270,8 @@ def test_schedule_and_workspace_are_host_queries(lib):
     (dict(kv_stride=64), hb.HIFA4_ERR_INVALID_ARGUMENT, "kv_stride"),
     (dict(sm_scale=float("nan")), hb.HIFA4_ERR_INVALID_ARGUMENT, "sm_scale"),
     (dict(normaliser=2), hb.HIFA4_ERR_INVALID_ARGUMENT, "normaliser"),
+    (dict(scale_rule=2), hb.HIFA4_ERR_INVALID_ARGUMENT, "scale_rule"),
+    (dict(Sq=1, scale_rule=-1), hb.HIFA4_ERR_INVALID_ARGUMENT, "scale_rule"),
 ])
 def test_attn_rejects_bad_params(lib, kw, status, msg):
     assert _attn(lib, _params(**kw)) == status
@@ -311,6 +320,10 @@ def test_bf16_path_rejects_bad_arguments(lib):
     assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x3000000, None,
                              None, 0, None) == hb.HIFA4_ERR_INVALID_ARGUMENT
     assert "normaliser" in hb.hifa4_last_error()
+    p = _params(scale_rule=1)
+    assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x3000000, None,
+                             None, 0, None) == hb.HIFA4_ERR_INVALID_ARGUMENT
+    assert "scale_rule" in hb.hifa4_last_error()
 
 
 def test_status_strings(lib):

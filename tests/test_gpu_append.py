@@ -27,10 +27,10 @@ def _draw(rng, shape, dt):
     return torch.from_numpy(x).to(dt)
 
 
-def _oracle_cache(kseq, vseq, smooth, cos, sin, cap):
+def _oracle_cache(kseq, vseq, smooth, cos, sin, cap, rule=0):
     """One-shot oracle quantisation of one sequence's K, V [1, Hkv, L, d] (torch)."""
     k = oracle.rope_rows(W.to_f32(kseq), cos, sin, 0) if cos is not None else W.to_f32(kseq)
-    return oracle.quantize_qkv(None, k, W.to_f32(vseq), smooth, kv_cap=cap)
+    return oracle.quantize_qkv(None, k, W.to_f32(vseq), smooth, kv_cap=cap, rule=rule)
 
 
 def _check_seq(cache, b, L, ref):
@@ -47,9 +47,11 @@ def _check_seq(cache, b, L, ref):
     (2, 4, 4, 64, "fp16", 130, (31, 64), (1, 1, 2, 33, 1), 1e4, False),
     (2, 16, 8, 256, "bf16", 96, (32, 0), (40, 1, 23), None, True),
 ])
-def test_appends_equal_one_shot_quantisation(case):
+@pytest.mark.parametrize("rule", [hb.SCALE_OCP, hb.SCALE_NOCLIP])
+def test_appends_equal_one_shot_quantisation(case, rule):
+    """Under either block-scale rule (the cache's), appends equal a one-shot quantisation."""
     B, Hq, Hkv, d, dt, cap, starts, steps, theta, sm = case
-    print("kv append:", case, flush=True)
+    print("kv append:", case, "scale rule", rule, flush=True)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float16
     rng = np.random.default_rng(sum(starts) + cap)
     smooth = np.exp2(rng.uniform(-1, 1, (Hkv, d))).astype(np.float32) if sm else None
@@ -58,7 +60,7 @@ def test_appends_equal_one_shot_quantisation(case):
     if theta is not None:
         cos, sin = W.rope_tables(cap + 8, d, theta)
         cos_t, sin_t = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
-    cache = hb.alloc_mx(B, Hq, Hkv, 1, cap, d)
+    cache = hb.alloc_mx(B, Hq, Hkv, 1, cap, d, scale_rule=rule)
     tail = hb.alloc_v_tail(B, Hkv, d, dtype=tdt)
     # sequence b starts with starts[b] tokens quantised in bulk; the caller fills the tail
     kseq = [_draw(rng, (1, Hkv, L, d), tdt) for L in starts]
@@ -70,10 +72,11 @@ def test_appends_equal_one_shot_quantisation(case):
                       cache.v_codes[b:b + 1], cache.v_scales[b:b + 1], 1, Hq, Hkv, 0, L, d, cap)
         if theta is not None:
             hb.hifa4_quantize_qkv_rope(None, kseq[b].cuda(), vseq[b].cuda(), cos_t, sin_t,
-                                       smooth=smooth_t, kv_stride=cap, out=sl, Hkv=Hkv)
+                                       smooth=smooth_t, kv_stride=cap, out=sl, Hkv=Hkv,
+                                       scale_rule=rule)
         else:
             hb.hifa4_quantize_qkv(None, kseq[b].cuda(), vseq[b].cuda(), smooth_t, kv_stride=cap,
-                                  out=sl)
+                                  out=sl, scale_rule=rule)
         r = L % 32
         if r:
             tail[b, :, :r] = vseq[b][0, :, L - r:].cuda()
@@ -84,7 +87,7 @@ def test_appends_equal_one_shot_quantisation(case):
         v = _draw(rng, (B, Hkv, n, d), tdt)
         qc = hb.alloc_mx(B, Hq, Hkv, n, cap, d)
         step_cache = hb.MXQKV(qc.q_codes, qc.q_scales, cache.k_codes, cache.k_scales,
-                              cache.v_codes, cache.v_scales, B, Hq, Hkv, n, cap, d, cap)
+                              cache.v_codes, cache.v_scales, B, Hq, Hkv, n, cap, d, cap, rule)
         lens_out = torch.full((B,), -7, dtype=torch.int32, device="cuda")
         hb.hifa4_kv_append(q.cuda(), k.cuda(), v.cuda(), lens, step_cache, tail,
                            kv_lens_out=lens_out, smooth=smooth_t, cos=cos_t, sin=sin_t)
@@ -95,7 +98,7 @@ def test_appends_equal_one_shot_quantisation(case):
             qf = W.to_f32(q[b:b + 1])
             if theta is not None:
                 qf = oracle.rope_rows(qf, cos, sin, int(L[b]))
-            ref_q = oracle.quantize_rows(qf, smooth, divide=False)
+            ref_q = oracle.quantize_rows(qf, smooth, divide=False, rule=rule)
             np.testing.assert_array_equal(qc.q_codes[b:b + 1].cpu().numpy(), ref_q[0])
             np.testing.assert_array_equal(qc.q_scales[b:b + 1].cpu().numpy(), ref_q[1])
             kseq[b] = torch.cat([kseq[b], k[b:b + 1]], dim=2)
@@ -103,7 +106,7 @@ def test_appends_equal_one_shot_quantisation(case):
         lens = lens_out
     for b in range(B):
         Lb = kseq[b].shape[2]
-        _check_seq(cache, b, Lb, _oracle_cache(kseq[b], vseq[b], smooth, cos, sin, cap))
+        _check_seq(cache, b, Lb, _oracle_cache(kseq[b], vseq[b], smooth, cos, sin, cap, rule))
         r = Lb % 32
         if r:   # the tail holds the raw values of the open block
             assert torch.equal(tail[b, :, :r].cpu(), vseq[b][0, :, Lb - r:])

@@ -146,22 +146,23 @@ def test_prefill_full_size_sampled_rows(cfg):
         np.sqrt(np.mean((o.reshape(-1, cfg.d)[rows] - exact["o"]) ** 2))))
 
 
-def _decode_case(cfg, lens, cap, chunk=0, tau=0.0):
+def _decode_case(cfg, lens, cap, chunk=0, tau=0.0, rule=0):
     B, Hq, Hkv, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.d
     mx = hb.alloc_mx(B, Hq, Hkv, 1, cap, d)
     q = W.decode_q(cfg)
-    hb.hifa4_quantize_qkv(q.cuda(), None, None, None, out=mx)
+    hb.hifa4_quantize_qkv(q.cuda(), None, None, None, out=mx, scale_rule=rule)
     for b, L in enumerate(lens):
         if int(L) == 0:
             continue
         k, v = W.decode_kv(cfg, b, int(L))
         sl = hb.MXQKV(None, None, mx.k_codes[b:b + 1], mx.k_scales[b:b + 1], mx.v_codes[b:b + 1],
                       mx.v_scales[b:b + 1], 1, Hq, Hkv, 0, int(L), d, cap)
-        hb.hifa4_quantize_qkv(None, k.cuda(), v.cuda(), None, kv_stride=cap, out=sl)
+        hb.hifa4_quantize_qkv(None, k.cuda(), v.cuda(), None, kv_stride=cap, out=sl,
+                              scale_rule=rule)
     mx.Sq, mx.Sk, mx.kv_stride = 1, cap, cap
     lens_t = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
     out, lse = hb.hifa4_attn_fwd(mx, causal=True, kv_lens=lens_t, decode_chunk=chunk,
-                                 rescale_threshold=tau)
+                                 rescale_threshold=tau, scale_rule=rule)
     torch.cuda.synchronize()
     p = hb.make_params(B, Hq, Hkv, 1, cap, d, causal=True, kv_stride=cap, decode_chunk=chunk)
     bc, ch = hb.hifa4_attn_schedule(p)
@@ -188,12 +189,12 @@ def _decode_split(p, lens, Hkv):
     return 64 * pt, phases
 
 
-def _decode_oracle(cfg, q, b, L, bc, split, tau=0.0):
+def _decode_oracle(cfg, q, b, L, bc, split, tau=0.0, rule=0):
     chunk, phases = split
     k, v = W.decode_kv(cfg, b, int(L))
-    qq = oracle.quantize_qkv(W.to_f32(q[b:b + 1]), W.to_f32(k), W.to_f32(v), None)
+    qq = oracle.quantize_qkv(W.to_f32(q[b:b + 1]), W.to_f32(k), W.to_f32(v), None, rule=rule)
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=bc, chunk=chunk,
-                           chunk_phase=phases[b:b + 1], tau=tau)
+                           chunk_phase=phases[b:b + 1], tau=tau, p_rule=rule)
     vmax = np.abs(W.to_f32(v)).max()
     return ref, vmax
 
