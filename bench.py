@@ -19,7 +19,8 @@ defined in that frame; the CPU oracle takes the same value).
 Also reported (in "extra"): the step's kernels one by one, the unfused step
 (Q, K, V quantised in one launch, attention on Q codes), the step with RoPE of
 pre-rotation K inside the quantise launch, the attention with threshold 0 (the
-FlashAttention-2 frame) and with the pages' non-reordered normaliser, the bf16
+FlashAttention-2 frame) and with the pages' non-reordered normaliser, the step
+under the no-clip block-scale rule (a format variant), the bf16
 FlashAttention baseline on the same prefill (time ratio = the measured
 counterpart of the pages' projected latency cut), the split-K decode on 64
 sequences with 1k-32k MXFP4 cache entries (HBM GB/s, split + merge), the
@@ -327,6 +328,18 @@ def main():
     extra["p_reordering_over_direct_latency_ratio"] = attn_avg / float(d_ms.mean())
     log("attention with the direct normaliser: %.3f ms (P-Reordering / direct latency %.3f)"
         % (d_ms.mean(), extra["p_reordering_over_direct_latency_ratio"]))
+
+    # ---- the no-clip block-scale rule (a format variant): the same step with K and V
+    #      quantised, Q quantised in the prologue and P_hat scaled under it
+    def step_noclip():
+        hb.hifa4_quantize_qkv(None, k, v, smooth, out=mx, scale_rule=hb.SCALE_NOCLIP)
+        hb.hifa4_attn_fwd_qraw(q, smooth, mx, causal=cfg.causal, out=out, lse=lse,
+                               rescale_threshold=tau, scale_rule=hb.SCALE_NOCLIP)
+    settle(step_noclip, torch)
+    extra["step_noclip_ms"] = float(time_batch(step_noclip, max(5, args.steps // 2), torch))
+    log("step under the no-clip scale rule: %.3f ms (headline step %.3f ms GPU)"
+        % (extra["step_noclip_ms"], gpu_ms_per_step))
+    quantise()   # restore the step's codes
 
     # ---- bf16 FlashAttention baseline on the same inputs
     if not args.no_bf16:
