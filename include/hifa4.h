@@ -125,7 +125,8 @@ typedef struct hifa4_attn_params {
  *   smooth: device fp32 [Hkv][d] (query head h uses row h / (Hq / Hkv)), or NULL for s = 1
  * Outputs: q_out in the row layout with T = Sq; k_out in the row layout and
  *   v_out in the column layout, both with T = kv_stride (>= Sk, 0 means Sk).
- *   Only tokens < Sk are written; the tail value block is zero-padded.
+ *   Only tokens < Sk are written; the tail value block is zero-padded.  Each
+ *   output's scales follow its own scale_rule (an unknown rule is an error).
  * Any of q / k / v may be NULL (with its output ignored) to skip that tensor.
  * d must be 64, 128 or 256.
  */
@@ -194,7 +195,10 @@ HIFA4_API hifa4_status hifa4_quantize_qkv_rope(const void* q, const void* k, con
  *   kv_lens_out  device int32 [B] or NULL: receives min(L_b + n_new, kv_stride),
  *         ready for the next hifa4_attn_fwd decode call (must not be kv_lens);
  *   kv_stride    the cache capacity in tokens (> 0); k_cache / v_cache use the
- *         layouts of hifa4_mx_tensor with T = kv_stride;
+ *         layouts of hifa4_mx_tensor with T = kv_stride; the blocks written
+ *         (new rows, the requantised open value block, new Q) follow the
+ *         scale_rule of q_out / k_cache / v_cache, which should be the rule
+ *         the cache was built with for it to equal a one-shot quantisation;
  *   smooth, dtype as for hifa4_quantize_qkv; rope may be NULL (no rotation),
  *         else n_pos >= 1.
  * Lengths live on the device, so the host cannot check them: the caller
