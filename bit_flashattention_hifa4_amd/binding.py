@@ -206,11 +206,12 @@ def _rope_struct(cos: torch.Tensor, sin: torch.Tensor, q_pos0: int, k_pos0: int)
 def hifa4_quantize_qkv(q: Optional[torch.Tensor], k: Optional[torch.Tensor],
                        v: Optional[torch.Tensor], smooth: Optional[torch.Tensor] = None, *,
                        kv_stride: int = 0, out: Optional[MXQKV] = None, Hkv: Optional[int] = None,
-                       scale_rule: int = SCALE_OCP, stream=None) -> MXQKV:
+                       scale_rule: Optional[int] = None, stream=None) -> MXQKV:
     """Smooth-QK + MXFP4 quantisation; q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] bf16 or fp16 on the GPU.
 
     With k and v both None, pass Hkv (the smoothing rows are per KV head).  scale_rule
-    (SCALE_OCP or SCALE_NOCLIP) is recorded in the returned tensors.
+    (SCALE_OCP or SCALE_NOCLIP) is recorded in the returned tensors; None keeps out's rule
+    (SCALE_OCP for new tensors).
     """
     return _quantize(q, k, v, smooth, None, kv_stride=kv_stride, out=out, Hkv=Hkv,
                      scale_rule=scale_rule, stream=stream)
@@ -221,7 +222,7 @@ def hifa4_quantize_qkv_rope(q: Optional[torch.Tensor], k: Optional[torch.Tensor]
                             q_pos0: int = 0, k_pos0: int = 0,
                             smooth: Optional[torch.Tensor] = None, kv_stride: int = 0,
                             out: Optional[MXQKV] = None, Hkv: Optional[int] = None,
-                            scale_rule: int = SCALE_OCP, stream=None) -> MXQKV:
+                            scale_rule: Optional[int] = None, stream=None) -> MXQKV:
     """hifa4_quantize_qkv after rotate-half RoPE of Q and K with the tables cos / sin
     (float32 [n_pos, d/2] on the GPU); query token t sits at position q_pos0 + t, key
     token t at k_pos0 + t."""
@@ -253,7 +254,8 @@ def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, sc
         out.Sq = Sq
     if kk is not None:
         out.Sk, out.kv_stride = Sk, cap
-    out.scale_rule = int(scale_rule)
+    if scale_rule is not None:
+        out.scale_rule = int(scale_rule)
     r = out.scale_rule
     if smooth is not None and (smooth.dtype != torch.float32 or tuple(smooth.shape) != (Hkv, d)):
         raise ValueError("smooth must be float32 [Hkv, d]")

@@ -81,6 +81,14 @@ def test_noclip_quantize_extreme_values_bit_exact():
     ref = _oracle_quant(inp, NC)
     for n in ("q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales"):
         np.testing.assert_array_equal(getattr(mx, n).cpu().numpy(), ref[n], err_msg=n)
+    # quantising again into the same tensors without naming a rule keeps theirs
+    for n in ("q_scales", "k_scales", "v_scales"):
+        getattr(mx, n).zero_()
+    hb.hifa4_quantize_qkv(q, k, v, None, out=mx)
+    torch.cuda.synchronize()
+    assert mx.scale_rule == NC
+    for n in ("q_scales", "k_scales", "v_scales"):
+        np.testing.assert_array_equal(getattr(mx, n).cpu().numpy(), ref[n], err_msg=n)
 
 
 @pytest.mark.parametrize("tau", [0.0, TG.FAST])
