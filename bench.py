@@ -186,7 +186,7 @@ def main():
     # kernel, which smooths and quantises its own Q rows in its prologue (the
     # codes are bit-identical to quantising Q separately).
     def quantise():
-        hb.hifa4_quantize_qkv(None, k, v, smooth, out=mx)
+        hb.hifa4_quantize_qkv(None, k, v, smooth, out=mx, scale_rule=hb.SCALE_OCP)
 
     def attend():
         hb.hifa4_attn_fwd_qraw(q, smooth, mx, causal=cfg.causal, out=out, lse=lse,
