@@ -199,6 +199,31 @@ def _decode_oracle(cfg, q, b, L, bc, split, tau=0.0, rule=0):
     return ref, vmax
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_prefill_long_context_sampled_rows(d):
+    """A 32k-token causal prefill (2 query heads on one KV head): the longest rows and
+    the deepest tiles of the schedule, with Q quantised in the prologue, on sampled rows
+    that include the first and last queries of each head."""
+    S, Hq = 32768, 2
+    print("long-context prefill parity: S", S, "d", d, flush=True)
+    inp = W.random_case(1, Hq, 1, S, S, d, seed=d + 7, rope_theta=1e6, n_outliers=2,
+                        smooth_alpha=0.5)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    s = torch.from_numpy(inp["smooth"]).cuda()
+    mx = hb.hifa4_quantize_qkv(None, k, v, s, Hkv=1)
+    mx.Sq, mx.Hq = S, Hq
+    out, lse = hb.hifa4_attn_fwd_qraw(q, s, mx, causal=True, rescale_threshold=FAST)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([_sample_rows(1, Hq, S, 40, seed=d),
+                                     [0, S - 1, S, 2 * S - 1, S // 2 + 31]]))
+    qq = _oracle_quant(inp)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=64,
+                           rows=rows, tau=FAST)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    _check_rows(out.float().cpu().numpy().reshape(-1, d)[rows], lse.cpu().numpy().reshape(-1)[rows],
+                ref, vmax, "S %d d %d" % (S, d))
+
+
 @pytest.mark.parametrize("chunk,tau", [(0, 0.0), (64, 0.0), (192, 0.0), (0, FAST), (192, FAST)])
 def test_decode_small_matches_oracle(chunk, tau):
     cfg = W.DecodeConfig("small_decode", 5, 8, 2, 128, 1, 700)
