@@ -22,7 +22,8 @@ pre-rotation K inside the quantise launch, the attention with threshold 0 (the
 FlashAttention-2 frame) and with the pages' non-reordered normaliser, the step
 under the no-clip block-scale rule (a format variant), the bf16
 FlashAttention baseline on the same prefill (time ratio = the measured
-counterpart of the pages' projected latency cut), the split-K decode on 64
+counterpart of the pages' projected latency cut), the same attention kernel at
+8k-32k tokens (long-context prefill), the split-K decode on 64
 sequences with 1k-32k MXFP4 cache entries (HBM GB/s, split + merge), the
 decode step (one-token cache append + attention), and the HBM read rate of a
 plain streaming kernel on the same box.
@@ -148,6 +149,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the long-context prefill attention leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the step variant with Q quantised by the quantise kernel")
@@ -360,6 +363,8 @@ def main():
     # ---- split-K decode against the long MXFP4 cache
     if not args.no_decode:
         extra.update(decode_leg(W, hb, torch, np, dev, args))
+    if not args.no_context:
+        extra.update(context_leg(hb, torch, dev, tau))
 
     if args.copy_calibration:
         copy_calibration(torch, dev)
@@ -396,6 +401,37 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def context_leg(hb, torch, dev, tau):
+    """The step's attention kernel (Q quantised in its prologue) on the Qwen3-8B head
+    shape (32 query / 8 KV heads, d 128, causal, B 1) at 8k, 16k and 32k tokens: a
+    128-row item then runs up to 128, 256 and 512 key tiles instead of 64, so its
+    fixed costs weigh less.  Inputs: N(0, 1) bf16 drawn on the GPU (torch generator,
+    seed 0), no smoothing; settled clocks; back-to-back launches."""
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    B, Hq, Hkv, d = 1, 32, 8, 128
+    for S in (8192, 16384, 32768):
+        q = torch.randn(B, Hq, S, d, device=dev, generator=g).to(torch.bfloat16)
+        k = torch.randn(B, Hkv, S, d, device=dev, generator=g).to(torch.bfloat16)
+        v = torch.randn(B, Hkv, S, d, device=dev, generator=g).to(torch.bfloat16)
+        mx = hb.hifa4_quantize_qkv(None, k, v, None, Hkv=Hkv)
+        mx.Sq, mx.Hq = S, Hq
+        out = torch.empty(B, Hq, S, d, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, Hq, S, dtype=torch.float32, device=dev)
+        f = lambda: hb.hifa4_attn_fwd_qraw(q, None, mx, causal=True, out=out, lse=lse,
+                                           rescale_threshold=tau)
+        settle(f, torch)
+        ms = time_batch(f, max(5, 81920 // S), torch)
+        tflops = 4.0 * d * B * Hq * S * (S + 1) / 2 / (ms * 1e-3) / 1e12
+        res["context_%dk_attention_ms" % (S // 1024)] = ms
+        res["context_%dk_attention_tflops" % (S // 1024)] = tflops
+        log("long-context prefill attention, S %d: %.3f ms, %.1f TFLOP/s (%.1f%% of FP4 peak)"
+            % (S, ms, tflops, 100.0 * tflops / MXFP4_PEAK_TFLOPS))
+        del q, k, v, mx, out, lse
+    return res
 
 
 def read_ceiling(torch, dev, nbytes=2 << 30):
