@@ -857,6 +857,10 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // No load may still be writing this workgroup's LDS when it exits.
   HIFA4_WAIT_VMCNT(0);
 
+  // Wave priority 2 for the epilogue: a finishing item frees its slot sooner when
+  // the other workgroup on the SIMD is in its priority-1 product block (measured:
+  // 1.4 % faster on the Qwen3-8B shape, 0.2-0.4 % on the Llama and Gemma2 shapes).
+  __builtin_amdgcn_s_setprio(2);
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
   const float lsum = kDirect ? l_direct : __shfl(accl[0], n);
   if (q < a.Sq) {
