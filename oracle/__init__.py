@@ -44,7 +44,7 @@ class _AttnCfg(ctypes.Structure):
         ("causal", ctypes.c_int), ("sm_scale", ctypes.c_double),
         ("bc", ctypes.c_int), ("chunk", ctypes.c_int), ("quant_p", ctypes.c_int),
         ("br", ctypes.c_int), ("nthreads", ctypes.c_int), ("tau", ctypes.c_double),
-        ("p_rule", ctypes.c_int),
+        ("p_rule", ctypes.c_int), ("p_shift", ctypes.c_double),
     ]
 
 
@@ -105,6 +105,8 @@ def _open(path: str):
     lib.oracle_smooth_calibrate.restype = None
     lib.oracle_smooth_calibrate.argtypes = [_D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_double, _F]
+    lib.oracle_eps_tiles.restype = None
+    lib.oracle_eps_tiles.argtypes = [_D, _D, _D, _D, ctypes.c_long, _D, _D]
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_attention.argtypes = [ctypes.POINTER(_AttnCfg), _D, _D, _D, _I32, _I32, _I64,
                                      ctypes.c_long, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
@@ -250,12 +252,15 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
               chunk: int = 0, quant_p: bool = True, br: int = 128, kv_lens=None, rows=None,
               chunk_phase=None,
               want_weights: bool = False, want_eps: bool = False, nthreads: int | None = None,
-              tau: float = 0.0, p_rule: int = 0):
+              tau: float = 0.0, p_rule: int = 0, p_shift: float = 0.0):
     """Online-softmax attention over dequantised (or exact) operands, fp64.
 
     q [B,Hq,Sq,d]; k, v [B,Hkv,Sk,d] (float64).  tau: lazy-rescale threshold
     (log2 units, 0 = FlashAttention-2 frame).  p_rule: block-scale rule of
-    P_hat (0 OCP, 1 no-clip).  chunk > 0 splits each row's keys
+    P_hat (0 OCP, 1 no-clip).  p_shift (log2 units, normally 0): P is taken as
+    exp(S - m) * 2^p_shift, which leaves exact attention unchanged and moves
+    P_hat's decisions only for P within 2^|p_shift| of a boundary of the 4-bit
+    format (see the C source).  chunk > 0 splits each row's keys
     into runs that start from a fresh softmax state and are merged with the
     log-sum-exp rule; chunk_phase [B,Hkv] (keys, multiples of bc below chunk)
     shifts that grid: a run starts at every key t > 0 with (t + phase) % chunk
@@ -271,7 +276,7 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
     cfg = _AttnCfg(B, Hq, Hkv, Sq, Sk, d, int(causal),
                    float(sm_scale if sm_scale is not None else 1.0 / np.sqrt(d)),
                    int(bc), int(chunk), int(quant_p), int(br),
-                   int(nthreads or default_threads()), float(tau), int(p_rule))
+                   int(nthreads or default_threads()), float(tau), int(p_rule), float(p_shift))
     lens = None
     if kv_lens is not None:
         lens = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
@@ -310,12 +315,14 @@ def attention(q, k, v, *, causal: bool, sm_scale: float | None = None, bc: int =
     if w is not None:
         out["w"] = w.reshape(shape + (Sk,))
     if eps is not None:
-        cnt = eps[1]
-        with np.errstate(invalid="ignore", divide="ignore"):
-            out["eps_tile_mean"] = np.where(cnt > 0, eps[0] / np.maximum(cnt, 1), np.nan)
-            out["eps_tile_pooled"] = np.where(cnt > 0, eps[2] / np.where(eps[3] > 0, eps[3], 1)
-                                              - 1.0, np.nan)
-        out["eps_tile_rows"] = cnt
+        mean = np.zeros_like(eps[0])
+        pooled = np.zeros_like(eps[0])
+        _load().oracle_eps_tiles(_ptr(eps[0], _D), _ptr(eps[1], _D), _ptr(eps[2], _D),
+                                 _ptr(eps[3], _D), eps[0].size, _ptr(mean, _D),
+                                 _ptr(pooled, _D))
+        out["eps_tile_mean"] = mean
+        out["eps_tile_pooled"] = pooled
+        out["eps_tile_rows"] = eps[1]
     return out
 
 

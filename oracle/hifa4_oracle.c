@@ -297,6 +297,13 @@ typedef struct {
                       tile's row max only if that exceeds it by more than tau; 0 gives the
                       FlashAttention-2 frame (P <= 1) */
   int p_rule;      /* block-scale rule of P_hat: 0 OCP, 1 no-clip (see oracle_mx_block) */
+  double p_shift;  /* log2 units, normally 0: every P is taken as exp(S - m) * 2^p_shift.
+                      Exact attention, O and the weights do not depend on it (the LSE is
+                      corrected for it); P_hat does, where a P lies within 2^|p_shift| of a
+                      rounding or block-exponent boundary of the 4-bit format.  A small
+                      +-p_shift brackets an implementation that computes P in lower
+                      precision (fp32 scores, a hardware exponential), so that its
+                      quantisation decisions at such boundaries can be matched. */
 } oracle_attn_cfg;
 
 typedef struct {
@@ -359,7 +366,7 @@ static void attn_row(attn_job* J, int b, int h, int i, size_t out, double* S, do
       double m_new = smax > m + c->tau * M_LN2 ? smax : m;
       double sumP = 0.0, sumPh = 0.0;
       for (long u = 0; u < n; u++) {
-        P[u] = exp(S[u] - m_new);
+        P[u] = exp(S[u] - m_new + c->p_shift * M_LN2);
         sumP += P[u];
       }
       if (c->quant_p) {
@@ -431,7 +438,7 @@ static void attn_row(attn_job* J, int b, int h, int i, size_t out, double* S, do
     if (o) o[j] = acc[j] / lsum;
     if (on) on[j] = acc[j] / lnsum;
   }
-  if (J->lse) J->lse[out] = M + log(lsum);
+  if (J->lse) J->lse[out] = M + log(lsum) - c->p_shift * M_LN2;
   if (J->l_out) J->l_out[out] = lsum;
   if (J->l_naive_out) J->l_naive_out[out] = lnsum;
   if (wr)
@@ -540,4 +547,28 @@ int oracle_attention(const oracle_attn_cfg* cfg, const double* q, const double* 
   free(th);
   pthread_mutex_destroy(&J.mu);
   return 0;
+}
+
+/*
+ * The per-tile statistic of the inconsistent normaliser (Abstract, P-Reordering:
+ * a normaliser from the unquantised P scales each output row by
+ * sum(P_hat) / sum(P), and the pages report that mismatch per attention tile).
+ * From the accumulators oracle_attention fills over n tiles:
+ *   mean[t]   = eps_sum[t] / eps_cnt[t]: the mean over the tile's rows (those
+ *               with sum(P) > 0 in that tile) of sum(P_hat) / sum(P) - 1;
+ *   pooled[t] = ph_sum[t] / p_sum[t] - 1: the tile's total P_hat mass over its
+ *               total P mass, minus one;
+ * both NaN for a tile no row contributed to.
+ */
+void oracle_eps_tiles(const double* eps_sum, const double* eps_cnt, const double* ph_sum,
+                      const double* p_sum, long n, double* mean, double* pooled) {
+  for (long t = 0; t < n; t++) {
+    if (eps_cnt[t] > 0.0) {
+      mean[t] = eps_sum[t] / eps_cnt[t];
+      pooled[t] = ph_sum[t] / p_sum[t] - 1.0;
+    } else {
+      mean[t] = NAN;
+      pooled[t] = NAN;
+    }
+  }
 }

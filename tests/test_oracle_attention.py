@@ -153,6 +153,44 @@ def test_single_tile_mxfp4_p_closed_form(Sk, p_rule):
     assert np.abs(ph - p).max() > 1e-3
 
 
+@pytest.mark.parametrize("shift", [0.37, -1.5])
+def test_p_shift_leaves_exact_attention_unchanged(shift):
+    """P taken as exp(S - m) * 2^shift: without quantisation the factor cancels in O and
+    is taken out of the LSE, so the result is the textbook one for any shift."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 2, 70, 32))
+    k = rng.standard_normal((1, 1, 90, 32))
+    v = rng.standard_normal((1, 1, 90, 32))
+    r = oracle.attention(q, k, v, causal=True, bc=32, quant_p=False, p_shift=shift)
+    o, lse = brute_attention(q, k, v, True, 1.0 / np.sqrt(32))
+    np.testing.assert_allclose(r["o"], o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("shift", [0.3, -0.45])
+def test_p_shift_closed_form(shift):
+    """One key tile with MXFP4 P_hat of P = exp(S - rowmax) * 2^shift: O is
+    sum(P_hat V) / sum(P_hat) and the LSE rowmax + log(sum P_hat) - shift ln 2, with
+    the block quantiser written in this file; and the shift does change P_hat."""
+    rng = np.random.default_rng(21)
+    Sq, Sk, d = 7, 96, 64
+    q = rng.standard_normal((1, 1, Sq, d)) * 2
+    k = rng.standard_normal((1, 1, Sk, d))
+    v = rng.standard_normal((1, 1, Sk, d))
+    sm = 1.0 / np.sqrt(d)
+    r = oracle.attention(q, k, v, causal=False, sm_scale=sm, bc=128, quant_p=True, p_shift=shift)
+    s = q[0, 0] @ k[0, 0].T * sm
+    p = np.exp(s - s.max(axis=1, keepdims=True)) * 2.0 ** shift
+    ph = mx_quantize_rows_np(p)
+    np.testing.assert_allclose(r["o"][0, 0], ph @ v[0, 0] / ph.sum(axis=1, keepdims=True),
+                               rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["lse"][0, 0],
+                               s.max(axis=1) + np.log(ph.sum(axis=1)) - shift * np.log(2.0),
+                               rtol=1e-13)
+    r0 = oracle.attention(q, k, v, causal=False, sm_scale=sm, bc=128, quant_p=True)
+    assert np.abs(r0["o"] - r["o"]).max() > 1e-4
+
+
 @pytest.mark.parametrize("pow2", [True, False])
 def test_smooth_qk_invariance_exact(pow2):
     rng = np.random.default_rng(5 + pow2)
@@ -236,6 +274,76 @@ def test_epsilon_bar_sign_on_synthetic_scores():
     assert eps.size >= 40          # 2 heads x 20 causal (128-row x 64-key) tiles
     assert (eps < 0).mean() > 0.9
     assert -0.2 < np.median(eps) < 0
+
+
+@pytest.mark.parametrize("p_rule", [0, 1])
+def test_epsilon_tiles_single_key_tile_closed_form(p_rule):
+    """One key tile (Sk <= bc, non-causal): in every query tile of br rows the
+    statistic is the mean over its rows of sum(P_hat) / sum(P) - 1, and the pooled
+    form is the tile's total P_hat mass over its total P mass minus one, with
+    P = exp(S - rowmax) and P_hat from the block quantiser written in this file
+    (Abstract, P-Reordering: the inconsistent normaliser scales each row by that
+    ratio)."""
+    rng = np.random.default_rng(31 + p_rule)
+    B, H, Sq, Sk, d, br = 1, 2, 11, 90, 32, 4
+    q = rng.standard_normal((B, H, Sq, d)) * 2
+    k = rng.standard_normal((B, H, Sk, d))
+    v = rng.standard_normal((B, H, Sk, d))
+    sm = 1.0 / np.sqrt(d)
+    r = oracle.attention(q, k, v, causal=False, sm_scale=sm, bc=128, br=br, quant_p=True,
+                         want_eps=True, p_rule=p_rule)
+    n_qt = -(-Sq // br)
+    assert r["eps_tile_mean"].shape == (B, H, n_qt, 1)
+    for h in range(H):
+        s = q[0, h] @ k[0, h].T * sm
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        ph = mx_quantize_rows_np(p, p_rule)
+        ratio = ph.sum(axis=1) / p.sum(axis=1) - 1.0
+        for t in range(n_qt):
+            rows = slice(t * br, min(Sq, (t + 1) * br))
+            np.testing.assert_allclose(r["eps_tile_mean"][0, h, t, 0], ratio[rows].mean(),
+                                       rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(r["eps_tile_pooled"][0, h, t, 0],
+                                       ph[rows].sum() / p[rows].sum() - 1.0,
+                                       rtol=1e-12, atol=1e-14)
+            assert r["eps_tile_rows"][0, h, t, 0] == rows.stop - rows.start
+
+
+def test_epsilon_tiles_hand_worked_two_by_two():
+    """Two query tiles (br = 2 rows) by two key tiles (bc = 32 keys), scores set
+    one by one (one-hot keys, so S[i][t] = q[i][t]).  A score of -1e4 gives
+    P = 0.  P_hat per 32-key block, worked by hand with the OCP MXFP4 rule:
+      row 0, tile 0: P = (1, .3)       -> amax 1, X = -2: (4, 1.2) -> (4, 1)
+                     P_hat = (1, .25)                               eps = 1.25/1.3 - 1
+      row 0, tile 1: P = (.6)          -> X = -3: 4.8 -> 4, P_hat = .5, eps = .5/.6 - 1
+      row 1, tile 0: P = (1)           -> eps = 0
+      row 1, tile 1: every P = 0       -> sum(P) = 0: the row does not count
+      row 2, tile 0: P = (1, .3, .3)   -> P_hat = (1, .25, .25),       eps = 1.5/1.6 - 1
+      row 2, tile 1: scores (ln 2, 0): the frame moves to ln 2, P = (1, .5) exactly on
+                     the grid,                                          eps = 0
+      row 3, tile 0: P = (1, .6, .3)   -> (4, 2.4, 1.2) -> (4, 2, 1), eps = 1.75/1.9 - 1
+      row 3, tile 1: P = (.3)          -> X = -4: 4.8 -> 4, P_hat = .25, eps = .25/.3 - 1
+    """
+    d, Sk, big = 64, 64, -1.0e4
+    q = np.full((1, 1, 4, d), big)
+    ln = np.log
+    q[0, 0, 0, [0, 1, 32]] = [0.0, ln(0.3), ln(0.6)]
+    q[0, 0, 1, [0]] = [0.0]
+    q[0, 0, 2, [0, 1, 2, 32, 33]] = [0.0, ln(0.3), ln(0.3), ln(2.0), 0.0]
+    q[0, 0, 3, [0, 1, 2, 32]] = [0.0, ln(0.6), ln(0.3), ln(0.3)]
+    k = np.eye(Sk, d)[None, None]
+    v = np.random.default_rng(3).standard_normal((1, 1, Sk, d))
+    r = oracle.attention(q, k, v, causal=False, sm_scale=1.0, bc=32, br=2, quant_p=True,
+                         want_eps=True)
+    e = {(0, 0): 1.25 / 1.3 - 1, (0, 1): 0.5 / 0.6 - 1, (1, 0): 0.0,
+         (2, 0): 1.5 / 1.6 - 1, (2, 1): 0.0, (3, 0): 1.75 / 1.9 - 1, (3, 1): 0.25 / 0.3 - 1}
+    want_mean = np.array([[(e[0, 0] + e[1, 0]) / 2, e[0, 1]],
+                          [(e[2, 0] + e[3, 0]) / 2, (e[2, 1] + e[3, 1]) / 2]])
+    want_pooled = np.array([[2.25 / 2.3 - 1, 0.5 / 0.6 - 1],
+                            [3.25 / 3.5 - 1, 1.75 / 1.8 - 1]])
+    np.testing.assert_allclose(r["eps_tile_rows"][0, 0], [[2, 1], [2, 2]])
+    np.testing.assert_allclose(r["eps_tile_mean"][0, 0], want_mean, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r["eps_tile_pooled"][0, 0], want_pooled, rtol=1e-12, atol=1e-14)
 
 
 @pytest.mark.parametrize("chunk", [64, 128, 192])

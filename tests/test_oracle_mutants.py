@@ -42,7 +42,11 @@ MUTANTS = [
     ("rescale_dropped", "for (int j = 0; j < d; j++) acc_c[j] *= alpha;", "", 0),
     ("merge_weight_dropped", "lsum = a_old * lsum + a_new * l;", "lsum = a_old * lsum + l;", 0),
     ("sm_scale_dropped", "s *= c->sm_scale;", "s *= 1.0;", 0),
-    ("lse_from_naive_sum", "J->lse[out] = M + log(lsum);", "J->lse[out] = M + log(lnsum);", 0),
+    ("lse_from_naive_sum", "J->lse[out] = M + log(lsum) -", "J->lse[out] = M + log(lnsum) -", 0),
+    ("p_shift_lse_correction_dropped", "J->lse[out] = M + log(lsum) - c->p_shift * M_LN2;",
+     "J->lse[out] = M + log(lsum);", 0),
+    ("p_shift_sign_flipped", "P[u] = exp(S[u] - m_new + c->p_shift * M_LN2);",
+     "P[u] = exp(S[u] - m_new - c->p_shift * M_LN2);", 0),
     ("p_block_misaligned", "for (long a0 = t0 - (t0 % 32); a0 < t1; a0 += 32)",
      "for (long a0 = t0 - (t0 % 32) - 16; a0 < t1; a0 += 32)", 0),
     ("v_tail_amax_over_padding", "col[k] = k < n ? (double)xh[(size_t)(t0 + k) * d + c] : 0.0;",
@@ -66,6 +70,16 @@ MUTANTS = [
      "if (rule == 1 && amax >= ldexp(6.0, e)) e += 1;", 0),
     ("p_rule_not_passed", "(void)oracle_mx_block(blk, 32, 1, codes, dq, 1, c->p_rule);",
      "(void)oracle_mx_block(blk, 32, 1, codes, dq, 1, 0);", 0),
+    ("eps_tile_row_index_by_key_tile", "J->n_qt + i / c->br) * J->n_kt",
+     "J->n_qt + i / c->bc) * J->n_kt", 0),
+    ("eps_rows_without_mass_counted", "if (J->eps_sum && sumP > 0.0) {", "if (J->eps_sum) {", 0),
+    ("eps_row_ratio_inverted", "J->eps_sum[ti] += sumPh / sumP - 1.0;",
+     "J->eps_sum[ti] += sumP / sumPh - 1.0;", 0),
+    ("eps_pooled_ratio_inverted", "pooled[t] = ph_sum[t] / p_sum[t] - 1.0;",
+     "pooled[t] = p_sum[t] / ph_sum[t] - 1.0;", 0),
+    ("eps_pooled_from_unquantised_p", "J->ph_sum[ti] += sumPh;", "J->ph_sum[ti] += sumP;", 0),
+    ("eps_mean_not_divided_by_rows", "mean[t] = eps_sum[t] / eps_cnt[t];",
+     "mean[t] = eps_sum[t];", 0),
     ("dot_product_drops_last_channel", "for (int j = 0; j < d; j++) s += qr[j] * kr[j];",
      "for (int j = 0; j < d - 1; j++) s += qr[j] * kr[j];", 0),
 ]
@@ -90,12 +104,16 @@ def _pin_checks():
         checks.append(lambda case=case: TA.test_exact_mode_equals_textbook_softmax(case, 64, 0.0))
     checks += [
         lambda: TA.test_single_tile_mxfp4_p_closed_form(75, 0),
+        lambda: TA.test_p_shift_closed_form(0.3),
+        lambda: TA.test_p_shift_leaves_exact_attention_unchanged(0.37),
         lambda: TA.test_single_tile_mxfp4_p_closed_form(160, 1),
         lambda: TA.test_lazy_rescale_frame_hand_worked(8.0, 64, 1.0),
         lambda: TA.test_lazy_rescale_frame_hand_worked(2.0, 32, 1.7),
         lambda: TA.test_smooth_qk_invariance_exact(True),
         lambda: TA.test_p_reordering_convex_weights(True, 64, 8.0),
         TA.test_inconsistent_normaliser_is_coherent_row_scaling,
+        TA.test_epsilon_tiles_hand_worked_two_by_two,
+        lambda: TA.test_epsilon_tiles_single_key_tile_closed_form(0),
         lambda: TA.test_split_k_mxfp4_equals_merge_of_chunk_runs(64),
         lambda: TA.test_split_k_exact_equals_unsplit(128),
         lambda: TA.test_split_phase_mxfp4_equals_merge_of_runs(128, [[0, 64], [64, 0]]),
