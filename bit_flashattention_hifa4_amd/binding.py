@@ -8,7 +8,8 @@ the tensors are not on the GPU, the calls raise.
 
 The Python names match the C entry points: ``hifa4_quantize_qkv``,
 ``hifa4_quantize_qkv_rope``, ``hifa4_kv_append``, ``hifa4_smooth_calibrate``,
-``hifa4_smooth_calibrate_workspace_size``, ``hifa4_attn_fwd``, ``hifa4_attn_fwd_qraw``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
+``hifa4_smooth_calibrate_workspace_size``, ``hifa4_attn_fwd``,
+``hifa4_attn_fwd_qraw``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
 ``hifa4_attn_decode_piece_tiles``, ``hifa4_attn_workspace_size``,
 ``hifa4_status_string``, ``hifa4_last_error``.
 """
@@ -166,6 +167,43 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise ValueError("dtype must be bfloat16 or float16, got %s" % dt)
 
 
+def _need_bytes(t: Optional[torch.Tensor], nbytes: int, name: str) -> None:
+    """The C ABI takes bare pointers and cannot see sizes: a buffer smaller than what the
+    kernels address is refused here, before anything is enqueued."""
+    if t is None:
+        raise ValueError("%s is missing" % name)
+    if t.dtype != torch.uint8:
+        raise ValueError("%s must be uint8, got %s" % (name, t.dtype))
+    if t.numel() < nbytes:
+        raise ValueError("%s holds %d bytes, the call addresses %d" % (name, t.numel(), nbytes))
+
+
+def _need_shape(t: torch.Tensor, shape, dtypes, name: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s (allowed: %s)" % (name, t.dtype, dtypes))
+
+
+def _check_row_mx(codes, scales, rows: int, d: int, name: str) -> None:
+    """Row layout (queries, keys): rows x d/2 code bytes and rows x d/32 scale bytes."""
+    _need_bytes(codes, rows * (d // 2), name + "_codes")
+    _need_bytes(scales, rows * (d // 32), name + "_scales")
+
+
+def _check_col_mx(codes, scales, heads: int, cap: int, d: int, name: str) -> None:
+    """Column layout (values): ceil(cap / 32) blocks of d x 16 code bytes and d scales."""
+    nblk = (cap + 31) // 32
+    _need_bytes(codes, heads * nblk * d * 16, name + "_codes")
+    _need_bytes(scales, heads * nblk * d, name + "_scales")
+
+
+def _check_out_lse(out, lse, B, Hq, Sq, d) -> None:
+    _need_shape(out, (B, Hq, Sq, d), (torch.bfloat16, torch.float16), "out")
+    if lse is not None:
+        _need_shape(lse, (B, Hq, Sq), (torch.float32,), "lse")
+
+
 @dataclasses.dataclass
 class MXQKV:
     """Quantised operands in the library's layouts (see include/hifa4.h)."""
@@ -259,6 +297,16 @@ def _quantize(q, k, v, smooth, rope: Optional[RopeC], *, kv_stride, out, Hkv, sc
     r = out.scale_rule
     if smooth is not None and (smooth.dtype != torch.float32 or tuple(smooth.shape) != (Hkv, d)):
         raise ValueError("smooth must be float32 [Hkv, d]")
+    if q is not None:
+        _check_row_mx(out.q_codes, out.q_scales, B * Hq * Sq, d, "q")
+    if k is not None:
+        if tuple(k.shape) != (B, Hkv, Sk, d):
+            raise ValueError("k must be [B, Hkv, Sk, d] = %s" % ((B, Hkv, Sk, d),))
+        _check_row_mx(out.k_codes, out.k_scales, B * Hkv * cap, d, "k")
+    if v is not None:
+        if tuple(v.shape) != (B, Hkv, Sk, d):
+            raise ValueError("v must be [B, Hkv, Sk, d] = %s" % ((B, Hkv, Sk, d),))
+        _check_col_mx(out.v_codes, out.v_scales, B * Hkv, cap, d, "v")
     lib = load_library()
     mq = MxTensorC(_ptr(out.q_codes) if q is not None else None,
                    _ptr(out.q_scales) if q is not None else None, r)
@@ -308,6 +356,13 @@ def hifa4_kv_append(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
         raise ValueError("v_tail must be [B, Hkv, 32, d] in k's dtype")
     if q is not None and tuple(cache.q_codes.shape) != (B, Hq, n, d // 2):
         raise ValueError("cache.q_codes must be [B, Hq, n, d/2]")
+    if q is not None:
+        _check_row_mx(cache.q_codes, cache.q_scales, B * Hq * n, d, "cache.q")
+    if (cache.B, cache.Hkv, cache.d) != (B, Hkv, d):
+        raise ValueError("cache is [B=%d, Hkv=%d, d=%d], k is [%d, %d, ., %d]"
+                         % (cache.B, cache.Hkv, cache.d, B, Hkv, d))
+    _check_row_mx(cache.k_codes, cache.k_scales, B * Hkv * cache.kv_stride, d, "cache.k")
+    _check_col_mx(cache.v_codes, cache.v_scales, B * Hkv, cache.kv_stride, d, "cache.v")
     rope = None
     if cos is not None or sin is not None:
         if cos is None or sin is None:
@@ -402,9 +457,17 @@ def hifa4_attn_fwd(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,
         out = torch.empty((mx.B, mx.Hq, mx.Sq, mx.d), dtype=out_dtype, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((mx.B, mx.Hq, mx.Sq), dtype=torch.float32, device=dev)
+    _check_out_lse(out, lse, mx.B, mx.Hq, mx.Sq, mx.d)
+    _check_row_mx(mx.q_codes, mx.q_scales, mx.B * mx.Hq * mx.Sq, mx.d, "q")
+    cap = mx.kv_stride or mx.Sk
+    if cap:
+        _check_row_mx(mx.k_codes, mx.k_scales, mx.B * mx.Hkv * cap, mx.d, "k")
+        _check_col_mx(mx.v_codes, mx.v_scales, mx.B * mx.Hkv, cap, mx.d, "v")
     need = hifa4_attn_workspace_size(p)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if need:
+        _need_bytes(workspace, need, "workspace")
     lib = load_library()
     _check(lib.hifa4_attn_fwd(ctypes.byref(p), MxTensorC(_ptr(mx.q_codes), _ptr(mx.q_scales)),
                               MxTensorC(_ptr(mx.k_codes), _ptr(mx.k_scales)),
@@ -439,6 +502,11 @@ def hifa4_attn_fwd_qraw(q: torch.Tensor, smooth: Optional[torch.Tensor], mx: MXQ
         out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check_out_lse(out, lse, B, Hq, Sq, d)
+    cap = mx.kv_stride or mx.Sk
+    if cap:
+        _check_row_mx(mx.k_codes, mx.k_scales, B * mx.Hkv * cap, d, "k")
+        _check_col_mx(mx.v_codes, mx.v_scales, B * mx.Hkv, cap, d, "v")
     _check(load_library().hifa4_attn_fwd_qraw(
         ctypes.byref(p), _ptr(q), _dtype_code(q.dtype), _ptr(smooth),
         MxTensorC(_ptr(mx.k_codes), _ptr(mx.k_scales)), MxTensorC(_ptr(mx.v_codes), _ptr(mx.v_scales)),
@@ -456,12 +524,17 @@ def bf16_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: 
     for t in (q, k, v):
         if t.dtype != torch.bfloat16:
             raise ValueError("bf16_attn_fwd takes bfloat16 tensors")
+    if tuple(k.shape) != (B, Hkv, Sk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must both be [B, Hkv, Sk, d] with q's B and d")
     p = make_params(B, Hq, Hkv, Sq, Sk, d, causal=causal, sm_scale=sm_scale,
                     rescale_threshold=rescale_threshold)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _need_shape(out, (B, Hq, Sq, d), (torch.bfloat16,), "out")
+    if lse is not None:
+        _need_shape(lse, (B, Hq, Sq), (torch.float32,), "lse")
     _check(load_library().bf16_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                         _ptr(lse), None, 0, _stream(stream)))
     return out, lse

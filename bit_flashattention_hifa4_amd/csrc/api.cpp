@@ -61,6 +61,8 @@ hifa4_status check_disjoint(const Span* in, int n_in, const Span* out, int n_out
 
 bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
 
+constexpr float kMaxRescaleThreshold = 64.0f;
+
 int64_t row_codes_bytes(int64_t rows, int d) { return rows * (d / 2); }
 int64_t row_scales_bytes(int64_t rows, int d) { return rows * (d / 32); }
 int64_t col_blocks(int64_t heads, int cap) { return heads * ((cap + 31) / 32); }
@@ -85,8 +87,12 @@ hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
   if (!supported_d(p->d)) return fail(HIFA4_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128, 256)", p->d);
   if (!std::isfinite(p->sm_scale))
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "sm_scale is not finite");
-  if (!std::isfinite(p->rescale_threshold) || p->rescale_threshold < 0.0f)
-    return fail(HIFA4_ERR_INVALID_ARGUMENT, "rescale_threshold must be finite and >= 0");
+  // P reaches 2^threshold and l up to Sk * 2^threshold in fp32: past 64 the
+  // accumulators could overflow where exact arithmetic does not
+  if (!std::isfinite(p->rescale_threshold) || p->rescale_threshold < 0.0f ||
+      p->rescale_threshold > kMaxRescaleThreshold)
+    return fail(HIFA4_ERR_INVALID_ARGUMENT, "rescale_threshold must be finite and in [0, %g]",
+                (double)kMaxRescaleThreshold);
   if (p->normaliser != 0 && p->normaliser != 1)
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "normaliser %d (0: P-Reordering, 1: direct)",
                 p->normaliser);
@@ -95,6 +101,10 @@ hifa4_status check_params(const hifa4_attn_params* p, int* cap, int* chunk) {
     return fail(HIFA4_ERR_INVALID_ARGUMENT, "scale_rule %d (0: OCP, 1: no-clip)", p->scale_rule);
   *cap = p->kv_stride ? p->kv_stride : p->Sk;
   if (*cap < p->Sk) return fail(HIFA4_ERR_INVALID_ARGUMENT, "kv_stride %d < Sk %d", *cap, p->Sk);
+  // a head's K / V codes are addressed through 32-bit buffer ranges and offsets
+  if ((int64_t)(*cap + 31) / 32 * 32 * (p->d / 2) >= ((int64_t)1 << 31))
+    return fail(HIFA4_ERR_UNSUPPORTED, "key capacity %d x d %d: a head's codes exceed 2^31 bytes",
+                *cap, p->d);
   if (p->kv_lens && p->Sq != 1)
     return fail(HIFA4_ERR_UNSUPPORTED, "kv_lens is only supported with Sq == 1 (decode)");
   *chunk = 0;

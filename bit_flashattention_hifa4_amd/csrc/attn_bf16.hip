@@ -44,7 +44,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
   constexpr int NJ = D / 16;     // QK MFMAs per 32-key tile
   constexpr int NC = D / 32;     // channel tiles
   constexpr int VT = kBN + 8;    // padded key stride of the transposed V tile (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBN * D];
+  // K rows padded by 16 bytes: the 16 lanes of one LDS read phase take 16 different
+  // rows at one column, which a power-of-two row stride would put in the same banks
+  constexpr int KS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBN * KS];
   __shared__ __attribute__((aligned(16))) uint16_t lds_vt[2][D * VT];
   // per thread and tile: KL 16-byte K chunks, VL groups of (4 keys, 8 channels)
   constexpr int KL = kBN * D / 8 / 256;
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
     for (int i = 0; i < KL; i++) {
       const int ci = tid + 256 * i;
       const int row = ci / (D / 8), off = (ci % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(lds_k[buf] + row * D + off) = kr[i];
+      *reinterpret_cast<uint4*>(lds_k[buf] + row * KS + off) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < VL; i++) {
@@ -173,8 +176,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
       v8s k0, k1;
-      uint4 w0 = *reinterpret_cast<const uint4*>(lk + r0 * D + 16 * j + 8 * h);
-      uint4 w1 = *reinterpret_cast<const uint4*>(lk + r1 * D + 16 * j + 8 * h);
+      uint4 w0 = *reinterpret_cast<const uint4*>(lk + r0 * KS + 16 * j + 8 * h);
+      uint4 w1 = *reinterpret_cast<const uint4*>(lk + r1 * KS + 16 * j + 8 * h);
       __builtin_memcpy(&k0, &w0, 16);
       __builtin_memcpy(&k1, &w1, 16);
       s0 = mfma_bf16_32x32x16(k0, qa[j], s0);

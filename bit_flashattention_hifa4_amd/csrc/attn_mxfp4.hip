@@ -551,8 +551,19 @@ __device__ __forceinline__ void v_load(const uint8_t* vbuf, int n, int h, VOps<D
   }
 }
 
+// Two workgroups (eight waves) per compute unit, two waves per SIMD, for every
+// head dim: d = 256 fits by running its step as two phases (below), so that
+// its 32 x 256 accumulator tile can sit in the accumulation registers.
 template <int D>
-constexpr int prefill_min_blocks() { return D >= 256 ? 1 : 2; }  // also used by decode
+constexpr int prefill_min_blocks() { return 2; }
+
+// d = 256 runs the step in two phases, softmax then products, instead of
+// interleaving the next tile's Q K^T with the current softmax in one wave:
+// one S tile per wave instead of two, operands read from LDS just before their
+// MFMA.  The two waves sharing a SIMD take turns, one in its softmax while the
+// other keeps the matrix core busy.
+template <int D>
+constexpr bool prefill_two_phase() { return D == 256; }
 
 // Smooth-QK (Q * s in fp32) and MXFP4 of the lane's blocks 2j + h (j < D/64)
 // of query row `row`, from the bf16 / fp16 activations: the same arithmetic as
@@ -829,7 +840,89 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     __syncthreads();
   };
 
-  v16f sa0, sa1, sb0, sb1;
+  // Two-phase step (d = 256) on tile kt, RP = kt mod 4; the scores of tile kt
+  // are in (s0, s1):
+  //   1. loads of K tile kt+3 and V tile kt+2 into the ring (as above);
+  //   2. softmax of tile kt: mask, running max, exponentials, P_hat (vector ALU);
+  //   3. rescale of the accumulators (rarely: only when some row's frame moved);
+  //   4. at wave priority 1, the products: [acc | l] += P_hat [V | 1] for tile kt
+  //      and the next tile's scores, S = Q K^T of tile kt+1, into (s0, s1), with
+  //      each operand read from LDS just before its MFMA;
+  //   5. wait for the loads issued last step, barrier.
+  // Same ring, waits and LDS layouts as the one-phase step: step kt reads V
+  // tile kt (landed: issued two steps earlier) and K tile kt+1.
+  //
+  // Registers: the K-operand offsets of the second 32-key tile are those of
+  // the first plus a constant (with chunk pairs j and j ^ 2 swapped at
+  // d = 256, see KX), and the normaliser is kept as one
+  // value per lane (l2, lanes of row 0 of the ones-column product), the
+  // product itself starting from zero every step: the live state fits two
+  // waves per SIMD without spills.
+  float l2 = 0.0f;
+  auto step2 = [&](auto ring, int kt, v16f& s0, v16f& s1) {
+    // row 32 + n's chunk swizzle is row n's XOR 4 at d = 256 and the same at
+    // d = 64 / 128 (k_swz), so its chunk 2j + h is row n's chunk 2 (j ^ KX) + h
+    constexpr int KX = D == 256 ? 2 : 0;
+    constexpr int RP = decltype(ring)::value;
+    constexpr int NS = T::STAGES;
+    const int n0 = kt * kBN;
+    const bool do_sm = n0 < wave_end;  // uniform per wave
+    issue_k<D, (RP + 3) % NS>(hd, kt + 3, n_tiles, wd, lane, tl);
+    issue_v<D, (RP + 2) % NS>(hd, kt + 2, n_tiles, wd, lane, vlane, vslane);
+
+    if (!do_sm || n0 + kBN > wave_full)
+      mask_scores(s0, s1, n0 + 32 * h, do_sm ? row_lim : 0);
+    const SoftmaxMax sx = softmax_max(s0, s1, m_run, c, a.tau);
+    uint4 pz = make_uint4(0, 0, 0, 0);
+    const SoftmaxStep st = softmax_exp(s0, s1, sx, c, a.p_bias, pz);
+    if constexpr (kDirect) l_direct = __builtin_fmaf(l_direct, st.alpha, row_sum_p(s0, s1));
+    if (kt != 0 && __any(st.alpha != 1.0f)) {
+#pragma unroll
+      for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
+      l2 *= st.alpha;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    const uint8_t* vbuf = lds_v + RP * T::V_BYTES;
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) {
+      const int ch = 32 * cc + n;
+      const uint4 va = *reinterpret_cast<const uint4*>(vbuf + (h * D + ch) * 16);
+      const int vs = vbuf[T::VS_OFF + h * D + ch];
+      acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
+    }
+    if constexpr (!kDirect) {
+      const v16f lt = mfma_fp4_32x32x64(ones, st.p_codes, v16f{}, ones_scale, st.p_scale);
+      l2 += lt[0];
+    }
+    const uint8_t* kbuf = lds_k + ((RP + 1) % NS) * T::K_BYTES;
+    const uint8_t* ksc = kbuf + T::KS_OFF;
+    s0 = v16f{};
+    s1 = v16f{};
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const uint4 k0 = *reinterpret_cast<const uint4*>(kbuf + koff[0][j]);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(kbuf + 32 * DB + koff[0][j ^ KX]);
+      const int ks0 = k_scale_word<DS>(ksc + n * T::KSS, j, h);
+      const int ks1 = k_scale_word<DS>(ksc + (32 + n) * T::KSS, j, h);
+      if (j % 2 == 0) {
+        s0 = mfma_fp4_sel<0>(k0, qa[j], s0, ks0, qsw[j / 2]);
+        s1 = mfma_fp4_sel<0>(k1, qa[j], s1, ks1, qsw[j / 2]);
+      } else {
+        s0 = mfma_fp4_sel<2>(k0, qa[j], s0, ks0, qsw[j / 2]);
+        s1 = mfma_fp4_sel<2>(k1, qa[j], s1, ks1, qsw[j / 2]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    // K tile kt+2 and V tile kt+1 (issued one and two steps ago) have landed;
+    // this step's loads stay in flight.
+    HIFA4_WAIT_VMCNT(T::N_LOADS);
+    __syncthreads();
+  };
+
+  // a wave whose rows see no key never computes (sa0, sa1): zeros, then masked
+  v16f sa0{}, sa1{}, sb0, sb1;
   if (0 < wave_end) {
     KOps<D> ko;
     qk_load<D>(lds_k, koff, n, h, ko);
@@ -839,20 +932,34 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   using R1 = std::integral_constant<int, 1>;
   using R2 = std::integral_constant<int, 2>;
   using R3 = std::integral_constant<int, 3>;
-  for (int kt = 0; kt < n_tiles; kt += 4) {
-    step(R0{}, kt, sa0, sa1, sb0, sb1);
-    if (kt + 1 >= n_tiles) break;
-    step(R1{}, kt + 1, sb0, sb1, sa0, sa1);
-    if (kt + 2 >= n_tiles) break;
-    step(R2{}, kt + 2, sa0, sa1, sb0, sb1);
-    if (kt + 3 >= n_tiles) break;
-    step(R3{}, kt + 3, sb0, sb1, sa0, sa1);
-  }
-  // the last tile's P V
-  if (n_tiles > 0) {
-    VOps<D> vo;
-    v_load<D>(lds_v + ((n_tiles - 1) % T::STAGES) * T::V_BYTES, n, h, vo);
-    pv_mfma(vo, pend_p, pend_s);
+  if constexpr (prefill_two_phase<D>()) {
+    (void)step;
+    for (int kt = 0; kt < n_tiles; kt += 4) {
+      step2(R0{}, kt, sa0, sa1);
+      if (kt + 1 >= n_tiles) break;
+      step2(R1{}, kt + 1, sa0, sa1);
+      if (kt + 2 >= n_tiles) break;
+      step2(R2{}, kt + 2, sa0, sa1);
+      if (kt + 3 >= n_tiles) break;
+      step2(R3{}, kt + 3, sa0, sa1);
+    }
+  } else {
+    (void)step2;
+    for (int kt = 0; kt < n_tiles; kt += 4) {
+      step(R0{}, kt, sa0, sa1, sb0, sb1);
+      if (kt + 1 >= n_tiles) break;
+      step(R1{}, kt + 1, sb0, sb1, sa0, sa1);
+      if (kt + 2 >= n_tiles) break;
+      step(R2{}, kt + 2, sa0, sa1, sb0, sb1);
+      if (kt + 3 >= n_tiles) break;
+      step(R3{}, kt + 3, sb0, sb1, sa0, sa1);
+    }
+    // the last tile's P V
+    if (n_tiles > 0) {
+      VOps<D> vo;
+      v_load<D>(lds_v + ((n_tiles - 1) % T::STAGES) * T::V_BYTES, n, h, vo);
+      pv_mfma(vo, pend_p, pend_s);
+    }
   }
   // No load may still be writing this workgroup's LDS when it exits.
   HIFA4_WAIT_VMCNT(0);
@@ -862,7 +969,7 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // 1.4 % faster on the Qwen3-8B shape, 0.2-0.4 % on the Llama and Gemma2 shapes).
   __builtin_amdgcn_s_setprio(2);
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
-  const float lsum = kDirect ? l_direct : __shfl(accl[0], n);
+  const float lsum = kDirect ? l_direct : __shfl(prefill_two_phase<D>() ? l2 : accl[0], n);
   if (q < a.Sq) {
     const int64_t row = bhq * a.Sq + q;
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
@@ -967,14 +1074,23 @@ __device__ __forceinline__ void dec_issue(const HeadDescs& hd, int n0, bool live
 }
 
 // ---------------------------------------------------------------------------
-// Balanced split-K schedule.  Pair s = (sequence b, KV head g), s = b * Hkv + g,
-// has tiles(L_b) = ceil(L_b / 64) key tiles; the pairs' tiles laid end to end
-// (sequence outer) form one sequence of `total` tiles, cut into pieces of
-// decode_piece_tiles(...) tiles.  Wave w of the persistent grid takes pieces
-// w, w + W, ...; a piece runs the online softmax from a fresh state and
-// restarts where it crosses into the next pair.  Each (piece, pair) run leaves
-// one partial row per query head of the pair at workspace row piece + s, which
-// is unique: a later piece never covers an earlier pair.
+// Split-K schedules.  Pair s = (sequence b, KV head g), s = b * Hkv + g, has
+// tiles(L_b) = ceil(L_b / 64) key tiles.  Wave w of the persistent grid takes
+// pieces w, w + W, ...; a piece runs the online softmax from a fresh state.
+//
+// Balanced (decode_chunk == 0): the pairs' tiles laid end to end (sequence
+// outer) form one sequence of `total` tiles, cut into pieces of
+// decode_piece_tiles(...) tiles, an even share per wave; a piece restarts
+// where it crosses into the next pair.  Each (piece, pair) run leaves one
+// partial row per query head of the pair at workspace row piece + s, which is
+// unique: a later piece never covers an earlier pair.  Where a pair's runs
+// start depends on the lengths of the sequences before it.
+//
+// Per pair (decode_chunk > 0, pt = decode_chunk / 64 tiles): pair s is cut
+// from its own key 0 into ceil(tiles / pt) pieces of pt tiles (the last one
+// shorter), numbered pair after pair; piece p leaves its partial rows at
+// workspace row p.  A pair's runs, and so its result, depend on its own length
+// only.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int dec_len(const AttnArgs& a, int b) {
   if (b >= a.B) return 0;
@@ -1042,6 +1158,47 @@ __device__ DecCursor dec_locate(const AttnArgs& a, int t, int lane) {
       const int off = t - (__shfl(incl, i) - c.nt * a.Hkv);
       c.g = off / c.nt;
       c.lt = off - c.g * c.nt;
+      break;
+    }
+    base = __shfl(incl, 63);
+  }
+  return {uniform(c.b), uniform(c.g), uniform(c.lt), uniform(c.nt), uniform(c.L)};
+}
+
+__device__ __forceinline__ int dec_pair_pieces(int nt, int pt) { return (nt + pt - 1) / pt; }
+
+// Per-pair schedule: pieces of all pairs (b_end = B), or of the pairs of the
+// sequences before b_end.
+__device__ __forceinline__ int dec_pieces_before(const AttnArgs& a, int b_end, int pt, int lane) {
+  int tot = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    tot += bb < b_end ? dec_pair_pieces(dec_tiles(dec_len(a, bb)), pt) : 0;
+  }
+  return uniform(wave_sum_i(tot) * a.Hkv);
+}
+
+// Per-pair schedule: the pair of piece p < (all pieces) and the piece's first tile
+// within it.
+__device__ DecCursor dec_locate_piece(const AttnArgs& a, int p, int pt, int lane) {
+  DecCursor c{0, 0, 0, 1, 0};
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int L = dec_len(a, bb);
+    const int nt = dec_tiles(L);
+    const int np = dec_pair_pieces(nt, pt);
+    const int incl = base + wave_scan_i(np * a.Hkv, lane);
+    const uint64_t hit = __ballot(bb < a.B && incl > p);
+    if (hit) {
+      const int i = __builtin_ctzll(hit);  // first sequence whose pieces reach past p
+      const int npi = __shfl(np, i);
+      c.b = b0 + i;
+      c.L = __shfl(L, i);
+      c.nt = __shfl(nt, i);
+      const int off = p - (__shfl(incl, i) - npi * a.Hkv);
+      c.g = off / npi;
+      c.lt = (off - c.g * npi) * pt;
       break;
     }
     base = __shfl(incl, 63);
@@ -1119,9 +1276,10 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
   const int lane = threadIdx.x;
   const int h = lane >> 5, n = lane & 31;
   const int G = a.Hq / a.Hkv;
+  const bool per_pair = a.chunk > 0;
   const int total = dec_totals(a, 0, lane).total;
   const int pt = decode_piece_tiles(a.chunk, a.dec_waves, total);
-  const int n_pieces = (total + pt - 1) / pt;
+  const int n_pieces = per_pair ? dec_pieces_before(a, a.B, pt, lane) : (total + pt - 1) / pt;
   if ((int)blockIdx.x >= n_pieces) return;  // uniform per wave
 
   const DecLanes<D> dl = dec_lanes<D>(lane);
@@ -1170,8 +1328,19 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
 
   uint4 pk = make_uint4(0, 0, 0, 0);
   for (int piece = blockIdx.x; piece < n_pieces; piece += gridDim.x) {
-    const int t_beg = piece * pt, t_end = min(total, t_beg + pt);
-    DecCursor cc = dec_locate(a, t_beg, lane);  // pair of the tile being computed
+    // [t_beg, t_end): the piece's tiles (flattened indices for the balanced
+    // schedule, counted from 0 within its one pair for the per-pair schedule)
+    int t_beg, t_end;
+    DecCursor cc;  // pair of the tile being computed
+    if (per_pair) {
+      cc = dec_locate_piece(a, piece, pt, lane);
+      t_beg = 0;
+      t_end = min(pt, cc.nt - cc.lt);
+    } else {
+      t_beg = piece * pt;
+      t_end = min(total, t_beg + pt);
+      cc = dec_locate(a, t_beg, lane);
+    }
     DecCursor ic = cc;                           // pair of the next tile to load
     HeadDescs hd = dec_descs<D>(a, ic);
     int ti = t_beg;                              // next tile to load
@@ -1232,7 +1401,7 @@ __global__ __launch_bounds__(64, DecRing<D>::WAVES_PER_CU / 4) void attn_decode_
         accl = mfma_fp4_32x32x64(ones, sm.p_codes, accl, ones_scale, sm.p_scale);
 
       if (pair_end || t + 1 == t_end) {
-        dec_flush<D>(a, piece + cc.b * a.Hkv + cc.g, G, n, h, m_run,
+        dec_flush<D>(a, per_pair ? piece : piece + cc.b * a.Hkv + cc.g, G, n, h, m_run,
                      kDirect ? l_direct : __shfl(accl[0], n), acc);
         m_run = -INFINITY;
         l_direct = 0.0f;
@@ -1279,10 +1448,17 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(AttnArgs a) {
   const float* part = a.partials;
   if (nt > 0) {
     const int pt = decode_piece_tiles(a.chunk, a.dec_waves, tt.total);
-    const int first = tt.before + g * nt;  // flattened index of the pair's first tile
-    const int j0 = first / pt;
-    nc = (first + nt - 1) / pt - j0 + 1;
-    part += ((int64_t)(j0 + b * a.Hkv + g) * G + hh) * (D + 4);
+    int64_t row0;  // the pair's first partial row; its runs' rows follow it
+    if (a.chunk > 0) {
+      nc = dec_pair_pieces(nt, pt);
+      row0 = dec_pieces_before(a, b, pt, lane) + g * nc;
+    } else {
+      const int first = tt.before + g * nt;  // flattened index of the pair's first tile
+      const int j0 = first / pt;
+      nc = (first + nt - 1) / pt - j0 + 1;
+      row0 = j0 + b * a.Hkv + g;
+    }
+    part += (row0 * G + hh) * (D + 4);
   }
   float M = -INFINITY, lsum = 0.0f;
   float o[CPL];

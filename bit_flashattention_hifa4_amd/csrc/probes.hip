@@ -131,6 +131,28 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* out, int iters) {
   out[blockIdx.x * blockDim.x + l] = t;
 }
 
+// The same for the 16 x 16 x 128 FP4 MFMA (half the multiply-adds of the
+// 32 x 32 x 64 form per instruction, a quarter of its accumulator): eight
+// independent chains per wave.
+__global__ __launch_bounds__(256) void mfma16_rate_kernel(float* out, int iters) {
+  const int l = threadIdx.x;
+  v8i A = {(int)(0x22222222u ^ l), 0x12345678, 0, 0x76543210, 0, 0, 0, 0};
+  v8i B = {0x11111111, (int)(0x22222222u ^ l), 0x33333333, 0, 0, 0, 0, 0};
+  v4f c[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) c[j] = v4f{};
+  int s = 127 + (l & 1);
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(j & 1 ? B : A, j & 2 ? A : B, c[j],
+                                                              kFmtFp4, kFmtFp4, 0, s, 0, s);
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) t += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  out[blockIdx.x * blockDim.x + l] = t;
+}
 
 // Memory -> LDS buffer loads (the LDS-destination form): one wave loads
 // `size`-byte elements, lane i from source byte offset size*i, with M0 = 64;
@@ -282,6 +304,13 @@ int probe_exp2_rate(float* out, int n_blocks, int iters, void* stream) {
 int probe_mfma_rate(float* out, int n_blocks, int iters, void* stream) {
   if (n_blocks <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_rate_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, out,
+                     iters);
+  return status(hipGetLastError());
+}
+
+int probe_mfma16_rate(float* out, int n_blocks, int iters, void* stream) {
+  if (n_blocks <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(mfma16_rate_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, out,
                      iters);
   return status(hipGetLastError());
 }

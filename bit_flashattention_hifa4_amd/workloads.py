@@ -90,8 +90,9 @@ class DecodeConfig:
     seed: int = BASE_SEED + 500
 
 
-# The five workloads.  Index 0 is the small case the oracle finishes in
-# seconds; index 1 (the Qwen3-8B-shaped causal prefill) is the headline one.
+# The five workloads.  The first is the small case the oracle finishes in
+# seconds; the Gemma2-9B-shaped causal prefill, the largest, is the benchmark's
+# headline, and the other prefill shapes and the decode cache are its legs.
 TINY = PrefillConfig("tiny_b1_h1_s128_d64", 1, 1, 1, 128, 64, False, "fp16", None, 0, 8.0,
                      fixed_outliers=(3, 17), smooth_alpha=0.5, calib_tokens=0,
                      seed=BASE_SEED + 100)

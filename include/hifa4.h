@@ -95,10 +95,11 @@ typedef struct hifa4_attn_params {
   int32_t kv_stride;  /* token capacity of the K/V buffers (>= Sk); 0 means Sk */
   const int32_t* kv_lens; /* device [B] per-sequence key count L (<= Sk), or NULL (L = Sk);
                              only with Sq == 1 */
-  int32_t decode_chunk;   /* decode piece length in tokens (a multiple of the key tile), or 0
-                             for the balanced split over the library's persistent grid
-                             (see hifa4_attn_fwd) */
-  float rescale_threshold;  /* log2 units, >= 0.  A row's running max moves only when a key
+  int32_t decode_chunk;   /* decode run length in tokens (a multiple of the key tile): every
+                             (sequence, KV head) is cut from its own key 0, independently of
+                             the batch; or 0 for the balanced split over the library's
+                             persistent grid (see hifa4_attn_fwd) */
+  float rescale_threshold;  /* log2 units, in [0, 64].  A row's running max moves only when a key
                                tile's max exceeds it by more than this, so P may reach
                                2^threshold; 0 = move on every increase (P <= 1, the
                                FlashAttention-2 frame).  Exact attention is the same for any
@@ -254,19 +255,29 @@ HIFA4_API size_t hifa4_attn_workspace_size(const hifa4_attn_params* p);
  * (P-Reordering with the fused normaliser).  The running max is updated once
  * per key tile (width from hifa4_attn_schedule).
  * Decode (Sq == 1) splits the keys and merges the runs' (m, l, acc) with the
- * log-sum-exp rule.  The valid keys of all (sequence, KV head) pairs, pairs in
- * order b * Hkv + g, are laid end to end as 64-key tiles (a pair has
- * ceil(L_b / 64) tiles, the last possibly partial), T tiles in all, and cut
- * into pieces of hifa4_attn_decode_piece_tiles(p, T) tiles: each piece runs
- * from a fresh softmax state and restarts where it crosses into the next pair.
- * So a fresh state starts at key t of pair s whenever t == 0 or
- * (first_tile(s) * 64 + t) is a multiple of 64 * piece_tiles.
+ * log-sum-exp rule; each run starts from a fresh softmax state.  A (sequence b,
+ * KV head g) pair has ceil(L_b / 64) key tiles of 64, the last possibly partial.
+ *   decode_chunk > 0 (per pair): every pair is cut from its own key 0 into runs
+ *      of decode_chunk keys (the last one shorter): a fresh state starts at key
+ *      t of a pair whenever t is a multiple of decode_chunk.  A sequence's
+ *      result depends on its own length only, not on the rest of the batch.
+ *   decode_chunk == 0 (balanced): the tiles of all pairs, pairs in order
+ *      b * Hkv + g, are laid end to end, T tiles in all, and cut into pieces of
+ *      hifa4_attn_decode_piece_tiles(p, T) tiles, one per wave of the
+ *      persistent grid; a piece restarts where it crosses into the next pair.
+ *      So a fresh state starts at key t of pair s whenever t == 0 or
+ *      (first_tile(s) * 64 + t) is a multiple of 64 * piece_tiles, where
+ *      first_tile(s) counts the tiles of every pair before s: the runs, and
+ *      so P_hat and the output (within the tolerance of the method, not bit
+ *      for bit), depend on the lengths of the other sequences in the batch.
  * q, k, v: MX tensors from hifa4_quantize_qkv (T = Sq for q, kv_stride for k, v;
  *      with a key capacity of 0 the k and v buffers are empty and may be NULL).
  * out: device [B][Hq][Sq][d] in out_dtype, O = acc / l (rows without any
  *      visible key are 0).  B * Hq * Sq == 0 enqueues nothing.
  * lse: device fp32 [B][Hq][Sq] natural-log sum-exp of the scaled scores
  *      (m + ln l; -inf for rows without a visible key), or NULL.
+ * Limits: a head's K / V codes (kv_stride * d / 2 bytes, rounded up to whole value
+ *      blocks) must stay below 2^31 bytes, else HIFA4_ERR_UNSUPPORTED.
  * workspace: device scratch of hifa4_attn_workspace_size(p) bytes (may be NULL if 0).
  *      Decode keeps there one fp32 partial row (m, l, 2 unused, acc[d]) per
  *      query head and per (piece, pair) run; prefill needs none.

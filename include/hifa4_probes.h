@@ -57,6 +57,9 @@ HIFA4_PROBE_API int probe_half_swap(const float* x, float* out, int n_waves, voi
  * out: [n_blocks * 256] floats (keeps the work alive). */
 HIFA4_PROBE_API int probe_exp2_rate(float* out, int n_blocks, int iters, void* stream);
 HIFA4_PROBE_API int probe_mfma_rate(float* out, int n_blocks, int iters, void* stream);
+/* Throughput of the 16 x 16 x 128 FP4 MFMA: 256-thread blocks, each wave runs eight
+ * independent chains of `iters` MFMAs (65536 flops each); out[n_blocks * 256]. */
+HIFA4_PROBE_API int probe_mfma16_rate(float* out, int n_blocks, int iters, void* stream);
 
 /* One wave of memory -> LDS buffer loads of `size` bytes per lane (1, 2, 4 or
  * 16), lane i reading src bytes [size*i, size*(i+1)) (src: 1024 bytes), with

@@ -211,13 +211,14 @@ def test_calibrate_workspace_size(lib):
 
 def _params(**kw):
     p = dict(B=2, Hq=8, Hkv=2, Sq=128, Sk=128, d=128, causal=True, sm_scale=None, kv_stride=0,
-             kv_lens=None, decode_chunk=0, normaliser=0, scale_rule=0)
+             kv_lens=None, decode_chunk=0, normaliser=0, scale_rule=0, rescale_threshold=0.0)
     p.update(kw)
     lens = p.pop("kv_lens")
     params = hb.make_params(**{k: p[k] for k in ("B", "Hq", "Hkv", "Sq", "Sk", "d")},
                             causal=p["causal"], sm_scale=p["sm_scale"], kv_stride=p["kv_stride"],
                             decode_chunk=p["decode_chunk"], normaliser=p["normaliser"],
-                            scale_rule=p["scale_rule"])
+                            scale_rule=p["scale_rule"],
+                            rescale_threshold=p["rescale_threshold"])
     if lens is not None:
         params.kv_lens = lens
     return params
@@ -272,10 +273,22 @@ def test_schedule_and_workspace_are_host_queries(lib):
     (dict(normaliser=2), hb.HIFA4_ERR_INVALID_ARGUMENT, "normaliser"),
     (dict(scale_rule=2), hb.HIFA4_ERR_INVALID_ARGUMENT, "scale_rule"),
     (dict(Sq=1, scale_rule=-1), hb.HIFA4_ERR_INVALID_ARGUMENT, "scale_rule"),
+    # P reaches 2^threshold: past 64 the fp32 accumulators could overflow
+    (dict(rescale_threshold=64.5), hb.HIFA4_ERR_INVALID_ARGUMENT, "rescale_threshold"),
+    (dict(rescale_threshold=-1.0), hb.HIFA4_ERR_INVALID_ARGUMENT, "rescale_threshold"),
+    # a head's codes are addressed with 32-bit offsets: Sk * d / 2 must stay below 2^31
+    (dict(Sk=1 << 24, d=256), hb.HIFA4_ERR_UNSUPPORTED, "2^31 bytes"),
+    (dict(Sq=1, Sk=(1 << 24) - 16, d=256), hb.HIFA4_ERR_UNSUPPORTED, "2^31 bytes"),
 ])
 def test_attn_rejects_bad_params(lib, kw, status, msg):
     assert _attn(lib, _params(**kw)) == status
     assert msg in hb.hifa4_last_error()
+
+
+def test_attn_limits_accept_their_bounds(lib):
+    # validation only (no launch): the largest threshold and head size still accepted
+    assert hb.hifa4_attn_schedule(_params(rescale_threshold=64.0))[0] == 64
+    assert hb.hifa4_attn_schedule(_params(Sk=(1 << 24) - 32, Sq=1 << 23, d=256))[0] == 64
 
 
 def test_attn_workspace_and_pointer_checks(lib):
@@ -330,3 +343,4 @@ def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4):
         assert hb.hifa4_status_string(s)
     assert hb.hifa4_status_string(5) == "unknown status"
+

@@ -6,9 +6,29 @@ chunk (read from hifa4_attn_schedule) in fp64.  The bf16 baseline is gated
 against exact fp64 softmax attention at 1e-2 * max|V|.  Errors against exact
 attention are printed for the 4-bit path as well.
 
-Small cases compare every output; the full-size workloads (Qwen3-8B-,
-Llama-3.1-8B-, Gemma2-9B-shaped prefill and the 64-sequence decode) run in the
-benchmark's launch configuration and compare sampled rows.
+Beside that gate, the root-mean-square of the same differences must stay below
+2e-3 * max|V|: what separates the two sides is the bf16 rounding of O (at most
+2^-9 |O| <= 2^-9 max|V| per element, so its RMS is below 2e-3 max|V|), fp32
+against fp64 sums, and the rare P_hat element whose fp32 exponential lands on
+the other side of an E2M1 rounding boundary; a systematic error in the kernel
+(a wrong frame, tile or scale) moves the RMS long before the worst element.
+
+One family of rows is exempt from the strict comparison, and checked instead
+against the other result the method admits there.  The kernel computes P from
+fp32 scores with the hardware exponential, the oracle in fp64, so P differs by
+a relative 2^-20 or less; where a P block's maximum lies that close to a power
+of two (with the lazy frame the block maxima land anywhere) the two sides can
+take different E8M0 exponents, and the block's top element then saturates to
+6 on one side and not the other (a 25 % step), as can an element that close to
+an E2M1 rounding boundary.  Both are correct roundings of the same P.  So a row
+that fails the strict gate must pass it against the oracle run with P scaled by
+2^+P_SHIFT or 2^-P_SHIFT (oracle p_shift, which moves exactly those decisions),
+and such rows must stay rare.
+
+Small cases and the full-size workloads alike (Qwen3-8B-, Llama-3.1-8B-,
+Gemma2-9B-shaped prefill in the benchmark's launch configuration, and every
+sequence of the 64-sequence decode, whose cache is also checked bit-exact)
+compare every output row; only the 32k-token prefill compares sampled rows.
 """
 import numpy as np
 import pytest
@@ -23,6 +43,11 @@ pytestmark = pytest.mark.gpu
 O_TOL = 2e-2      # times max|V|, MXFP4 path vs the oracle
 BF16_TOL = 1e-2   # times max|V|, bf16 path vs exact attention
 LSE_TOL = 2e-2    # absolute, natural log units
+RMS_TOL = 2e-3    # times max|V|: root-mean-square of the MXFP4 path vs the oracle
+# log2 units: brackets the kernel's P (fp32 scores times the fp32 log2(e) scale, the
+# frame subtracted in fp32, the hardware exp2: a relative error below 2^-20 for
+# exponent arguments up to 2^4) several times over
+P_SHIFT = 3e-5
 
 
 FAST = hb.RESCALE_THRESHOLD_FAST   # the benchmark's launch configuration
@@ -45,16 +70,61 @@ def _oracle_quant(inp):
     return oracle.quantize_qkv(f(inp["q"]), f(inp["k"]), f(inp["v"]), inp["smooth"])
 
 
-def _check_rows(o_gpu, lse_gpu, ref, vmax, what):
-    err = np.abs(o_gpu - ref["o"])
-    worst = err.max() if err.size else 0.0
-    fin = np.isfinite(ref["lse"])
-    assert np.array_equal(np.isfinite(lse_gpu), fin), what + ": rows without keys differ"
-    lerr = np.abs(lse_gpu[fin] - ref["lse"][fin]).max() if fin.any() else 0.0
-    print("%s: max|O - oracle| = %.4g (bound %.4g), max|lse diff| = %.3g"
-          % (what, worst, O_TOL * vmax, lerr), flush=True)
+def _row_fail(o, lse, ro, rlse, vmax):
+    """Per row: does it miss the strict gate against (ro, rlse)?"""
+    fin = np.isfinite(rlse)
+    lerr = np.where(fin, np.abs(np.where(fin, lse, 0.0) - np.where(fin, rlse, 0.0)), 0.0)
+    return (np.abs(o - ro).max(axis=1) > O_TOL * vmax) | (lerr > LSE_TOL)
+
+
+def _check_rows(o_gpu, lse_gpu, ref, vmax, what, redo=None):
+    """Gate every row of o_gpu / lse_gpu against the oracle's ref.  redo(rows, shift)
+    reruns the oracle with p_shift = shift on the given row positions (indices into
+    the flattened rows of o_gpu) and returns its dict; rows that miss the strict gate
+    must pass it against the run with +P_SHIFT or -P_SHIFT (see the module doc)."""
+    d = o_gpu.shape[-1]
+    o2, r2 = o_gpu.reshape(-1, d), ref["o"].reshape(-1, d)
+    l2, rl2 = lse_gpu.reshape(-1), ref["lse"].reshape(-1)
+    fin = np.isfinite(rl2)
+    assert np.array_equal(np.isfinite(l2), fin), what + ": rows without keys differ"
+    err = np.abs(o2 - r2)
+    rms = float(np.sqrt(np.mean(err.astype(np.float64) ** 2))) if err.size else 0.0
+    bad = np.nonzero(_row_fail(o2, l2, r2, rl2, vmax))[0] if err.size else np.zeros(0, int)
+    good = np.ones(o2.shape[0], bool)
+    good[bad] = False
+    worst = err[good].max() if good.any() and d else 0.0
+    lerr = np.abs(l2[good & fin] - rl2[good & fin]).max() if (good & fin).any() else 0.0
+    print("%s: max|O - oracle| = %.4g (bound %.4g), rms %.3g (bound %.3g), max|lse diff| = %.3g;"
+          " %d of %d rows at a rounding boundary" % (what, worst, O_TOL * vmax, rms,
+                                                     RMS_TOL * vmax, lerr, bad.size, o2.shape[0]),
+          flush=True)
+    if bad.size:
+        assert redo is not None, what + ": %d rows miss the gate" % bad.size
+        # a decision at a rounding boundary needs a P within 2^-17 of it: rare
+        assert bad.size <= max(4, o2.shape[0] // 1000), what + ": %d rows" % bad.size
+        ok = np.zeros(bad.size, bool)
+        for sh in (P_SHIFT, -P_SHIFT):
+            alt = redo(bad, sh)
+            ao, al = alt["o"].reshape(-1, d), alt["lse"].reshape(-1)
+            ok |= ~_row_fail(o2[bad], l2[bad], ao, al, vmax)
+        for i in np.nonzero(~ok)[0]:
+            r = bad[i]
+            print("  row %d: max|O - oracle| = %.4g, lse %.4g vs %.4g" % (
+                r, np.abs(o2[r] - r2[r]).max(), l2[r], rl2[r]), flush=True)
+        assert ok.all(), what + ": rows differ beyond the rounding boundaries"
     assert worst <= O_TOL * vmax
+    assert rms <= RMS_TOL * vmax
     assert lerr <= LSE_TOL
+
+
+def _redo(qq, rows=None, **kw):
+    """redo for _check_rows: the oracle on the quantised operands qq with the call's
+    settings; rows maps positions in the checked set to oracle row ids."""
+    def f(pos, shift):
+        ids = pos if rows is None else np.asarray(rows)[pos]
+        return oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], rows=ids, p_shift=shift,
+                                **kw)
+    return f
 
 
 SMALL = [
@@ -83,7 +153,8 @@ def test_prefill_small_cases_match_oracle(case, tau):
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=bc,
                            quant_p=True, tau=tau)
     vmax = np.abs(W.to_f32(inp["v"])).max()
-    _check_rows(o, lse, ref, vmax, "case %s" % (case,))
+    _check_rows(o, lse, ref, vmax, "case %s" % (case,),
+                redo=_redo(qq, causal=causal, bc=bc, quant_p=True, tau=tau))
     # P-Reordering: every output row is a convex combination of the visible
     # dequantised V rows (bf16 output rounding as slack)
     vd = qq["v_deq"]
@@ -108,7 +179,7 @@ def test_tiny_workload_all_outputs():
     qq = _oracle_quant(inp)
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=cfg.causal, bc=bc)
     vmax = np.abs(W.to_f32(inp["v"])).max()
-    _check_rows(o, lse, ref, vmax, cfg.name)
+    _check_rows(o, lse, ref, vmax, cfg.name, redo=_redo(qq, causal=cfg.causal, bc=bc))
     exact = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
                              causal=cfg.causal, bc=bc, quant_p=False)
     print("%s: max|O - exact attention| = %.4g" % (cfg.name, np.abs(o - exact["o"]).max()))
@@ -128,25 +199,38 @@ def _sample_rows(B, Hq, Sq, n, seed):
 FULL = [W.QWEN3_8B, W.LLAMA31_8B, W.GEMMA2_9B]
 
 
-@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
-def test_prefill_full_size_sampled_rows(cfg):
-    print("full-size prefill parity:", cfg.name, flush=True)
+@pytest.mark.parametrize("cfg,tau", [(c, FAST) for c in FULL] + [(W.QWEN3_8B, 0.0)],
+                         ids=lambda c: c.name if hasattr(c, "name") else "tau%g" % c)
+def test_prefill_full_size_every_row(cfg, tau):
+    """The prefill workloads at full size in the benchmark's launch configuration (Q
+    quantised in the attention prologue), every output row and LSE against the oracle;
+    the Qwen3-8B shape also in the FlashAttention-2 frame (threshold 0)."""
+    print("full-size prefill parity:", cfg.name, "tau", tau, flush=True)
     inp = W.prefill_inputs(cfg)
-    o, lse, bc, _ = _run_hifa4(inp, cfg.causal, tau=FAST)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    s = torch.from_numpy(inp["smooth"]).cuda() if inp["smooth"] is not None else None
+    mx = hb.hifa4_quantize_qkv(None, k, v, s, Hkv=cfg.Hkv)
+    mx.Sq, mx.Hq = cfg.S, cfg.Hq
+    out, lse = hb.hifa4_attn_fwd_qraw(q, s, mx, causal=cfg.causal, rescale_threshold=tau)
+    torch.cuda.synchronize()
+    o, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    del q, k, v, mx, out
     qq = _oracle_quant(inp)
-    rows = _sample_rows(cfg.B, cfg.Hq, cfg.S, 192, seed=cfg.seed)
-    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=cfg.causal, bc=bc,
-                           rows=rows, tau=FAST)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=cfg.causal, bc=64,
+                           tau=tau)
     vmax = np.abs(W.to_f32(inp["v"])).max()
-    _check_rows(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], ref, vmax, cfg.name)
+    _check_rows(o, lse, ref, vmax, "%s (every row)" % cfg.name,
+                redo=_redo(qq, causal=cfg.causal, bc=64, tau=tau))
+    del ref, qq
+    rows = _sample_rows(cfg.B, cfg.Hq, cfg.S, 192, seed=cfg.seed)
+    o = o.reshape(-1, cfg.d)[rows]
     exact = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
-                             causal=cfg.causal, bc=bc, quant_p=False, rows=rows)
+                             causal=cfg.causal, bc=64, quant_p=False, rows=rows)
     print("%s: sampled max|O - exact attention| = %.4g, rms %.4g" % (
-        cfg.name, np.abs(o.reshape(-1, cfg.d)[rows] - exact["o"]).max(),
-        np.sqrt(np.mean((o.reshape(-1, cfg.d)[rows] - exact["o"]) ** 2))))
+        cfg.name, np.abs(o - exact["o"]).max(), np.sqrt(np.mean((o - exact["o"]) ** 2))))
 
 
-def _decode_case(cfg, lens, cap, chunk=0, tau=0.0, rule=0):
+def _decode_case(cfg, lens, cap, chunk=0, tau=0.0, rule=0, keep_cache=False):
     B, Hq, Hkv, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.d
     mx = hb.alloc_mx(B, Hq, Hkv, 1, cap, d)
     q = W.decode_q(cfg)
@@ -168,19 +252,23 @@ def _decode_case(cfg, lens, cap, chunk=0, tau=0.0, rule=0):
     bc, ch = hb.hifa4_attn_schedule(p)
     assert ch == chunk
     split = _decode_split(p, lens, Hkv)
-    return q, out.float().cpu().numpy(), lse.cpu().numpy(), bc, split
+    res = (q, out.float().cpu().numpy(), lse.cpu().numpy(), bc, split)
+    return res + (mx,) if keep_cache else res
 
 
 def _decode_split(p, lens, Hkv):
-    """The library's decode split as the oracle's chunk grid (include/hifa4.h):
-    pair (b, g) starts at flattened tile first = Hkv * sum(tiles before b) + g * tiles(L_b),
-    pieces are cut every pt tiles of the flattened sequence, so the pair's fresh states
-    start where (first * 64 + t) % (64 * pt) == 0, i.e. chunk 64 * pt with phase
-    64 * (first % pt)."""
+    """The library's decode split as the oracle's chunk grid (include/hifa4.h).
+    With a caller's chunk every pair is cut from its own key 0: chunk 64 * pt, phase 0.
+    Balanced: pair (b, g) starts at flattened tile first = Hkv * sum(tiles before b) +
+    g * tiles(L_b), pieces are cut every pt tiles of the flattened sequence, so the pair's
+    fresh states start where (first * 64 + t) % (64 * pt) == 0, i.e. chunk 64 * pt with
+    phase 64 * (first % pt)."""
     nt = [-(-int(L) // 64) for L in lens]
     pt = hb.hifa4_attn_decode_piece_tiles(p, Hkv * sum(nt))
     assert pt >= 1
     phases = np.zeros((len(lens), Hkv), np.int32)
+    if p.decode_chunk > 0:
+        return 64 * pt, phases
     first = 0
     for b, n in enumerate(nt):
         for g in range(Hkv):
@@ -189,13 +277,15 @@ def _decode_split(p, lens, Hkv):
     return 64 * pt, phases
 
 
-def _decode_oracle(cfg, q, b, L, bc, split, tau=0.0, rule=0):
+def _decode_oracle(cfg, q, b, L, bc, split, tau=0.0, rule=0, with_redo=False):
     chunk, phases = split
     k, v = W.decode_kv(cfg, b, int(L))
     qq = oracle.quantize_qkv(W.to_f32(q[b:b + 1]), W.to_f32(k), W.to_f32(v), None, rule=rule)
-    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=bc, chunk=chunk,
-                           chunk_phase=phases[b:b + 1], tau=tau, p_rule=rule)
+    kw = dict(causal=True, bc=bc, chunk=chunk, chunk_phase=phases[b:b + 1], tau=tau, p_rule=rule)
+    ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], **kw)
     vmax = np.abs(W.to_f32(v)).max()
+    if with_redo:
+        return ref, vmax, _redo(qq, **kw)
     return ref, vmax
 
 
@@ -221,7 +311,8 @@ def test_prefill_long_context_sampled_rows(d):
                            rows=rows, tau=FAST)
     vmax = np.abs(W.to_f32(inp["v"])).max()
     _check_rows(out.float().cpu().numpy().reshape(-1, d)[rows], lse.cpu().numpy().reshape(-1)[rows],
-                ref, vmax, "S %d d %d" % (S, d))
+                ref, vmax, "S %d d %d" % (S, d), redo=_redo(qq, rows=rows, causal=True, bc=64,
+                                                              tau=FAST))
 
 
 @pytest.mark.parametrize("chunk,tau", [(0, 0.0), (64, 0.0), (192, 0.0), (0, FAST), (192, FAST)])
@@ -231,15 +322,16 @@ def test_decode_small_matches_oracle(chunk, tau):
     print("decode parity: lens", lens, "chunk", chunk, "tau", tau, flush=True)
     q, o, lse, bc, split = _decode_case(cfg, lens, cap=704, chunk=chunk, tau=tau)
     for b, L in enumerate(lens):
-        ref, vmax = _decode_oracle(cfg, q, b, L, bc, split, tau=tau)
-        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L))
+        ref, vmax, redo = _decode_oracle(cfg, q, b, L, bc, split, tau=tau, with_redo=True)
+        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L),
+                        redo=redo)
 
 
 @pytest.mark.parametrize("d,Hq,Hkv,lens,chunk", [
     (64, 8, 8, [300, 1, 0, 129, 64], 0),          # G = 1
-    (64, 8, 2, [1, 64, 65, 130, 0, 3, 257], 1280),  # a piece spans several pairs
+    (64, 8, 2, [1, 64, 65, 130, 0, 3, 257], 1280),  # one run per pair (chunk > every L)
     (256, 16, 2, [500, 63, 200], 0),              # G = 8
-    (256, 16, 2, [500, 63, 200], 320),            # pieces of 5 tiles straddle pairs
+    (256, 16, 2, [500, 63, 200], 320),            # runs of 5 tiles from each pair's key 0
     (128, 32, 1, [900, 450], 0),                  # G = 32, the whole MFMA width
 ])
 def test_decode_head_dims_and_groups_match_oracle(d, Hq, Hkv, lens, chunk):
@@ -251,16 +343,35 @@ def test_decode_head_dims_and_groups_match_oracle(d, Hq, Hkv, lens, chunk):
         if L == 0:
             assert not o[b].any() and np.isneginf(lse[b]).all()
             continue
-        ref, vmax = _decode_oracle(cfg, q, b, L, bc, split, tau=FAST)
-        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode d=%d b=%d L=%d" % (d, b, L))
+        ref, vmax, redo = _decode_oracle(cfg, q, b, L, bc, split, tau=FAST, with_redo=True)
+        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode d=%d b=%d L=%d" % (d, b, L),
+                    redo=redo)
+
+
+@pytest.mark.parametrize("chunk", [64, 320])
+def test_decode_with_chunk_is_batch_invariant(chunk):
+    """With a caller's chunk every (sequence, KV head) is cut from its own key 0, so a
+    sequence's output does not depend on the lengths of the sequences batched with it:
+    the same sequences in two batches with different neighbours give identical bits."""
+    cfg = W.DecodeConfig("batch_invariance", 4, 8, 2, 128, 1, 900)
+    base = [900, 257, 64, 1]
+    other = [13, 257, 700, 1]        # sequences 1 and 3 keep their lengths
+    outs = []
+    for lens in (base, other):
+        print("decode batch invariance: lens", lens, "chunk", chunk, flush=True)
+        q, o, lse, bc, split = _decode_case(cfg, lens, cap=960, chunk=chunk, tau=FAST)
+        outs.append((o, lse))
+    for b in (1, 3):
+        assert np.array_equal(outs[0][0][b], outs[1][0][b]), "sequence %d" % b
+        assert np.array_equal(outs[0][1][b], outs[1][1][b]), "sequence %d" % b
 
 
 def test_decode_zero_length_sequence_gives_zero_rows():
     cfg = W.DecodeConfig("zero_len", 2, 4, 1, 64, 0, 100)
     q, o, lse, bc, split = _decode_case(cfg, [0, 100], cap=128)
     assert not o[0].any() and np.isneginf(lse[0]).all()
-    ref, vmax = _decode_oracle(cfg, q, 1, 100, bc, split)
-    _check_rows(o[1:2], lse[1:2], ref, vmax, "decode L=100 next to L=0")
+    ref, vmax, redo = _decode_oracle(cfg, q, 1, 100, bc, split, with_redo=True)
+    _check_rows(o[1:2], lse[1:2], ref, vmax, "decode L=100 next to L=0", redo=redo)
 
 
 def test_decode_all_sequences_empty():
@@ -269,16 +380,35 @@ def test_decode_all_sequences_empty():
     assert not o.any() and np.isneginf(lse).all()
 
 
-def test_decode_full_size_sampled_sequences():
+def test_decode_full_size_every_sequence_and_cache():
+    """The 64-sequence decode workload: every sequence's output against the oracle, and
+    the whole 4-bit cache (the valid rows of K, the value blocks covering the valid
+    tokens, codes and scales) bit-exact against the oracle's quantisation."""
     cfg = W.DECODE
     lens = W.decode_lengths(cfg)
     cap = int(-(-lens.max() // 64) * 64)
     print("full-size decode parity: sum(L) =", int(lens.sum()), flush=True)
-    q, o, lse, bc, split = _decode_case(cfg, lens, cap=cap, tau=FAST)
+    q, o, lse, bc, split, mx = _decode_case(cfg, lens, cap=cap, tau=FAST, keep_cache=True)
     print("piece length", split[0], "keys", flush=True)
-    for b in (0, int(np.argmax(lens)), int(np.argmin(lens)), 37):
-        ref, vmax = _decode_oracle(cfg, q, b, lens[b], bc, split, tau=FAST)
-        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, lens[b]))
+    worst = 0.0
+    for b in range(cfg.B):
+        L = int(lens[b])
+        k, v = W.decode_kv(cfg, b, L)
+        qq = oracle.quantize_qkv(W.to_f32(q[b:b + 1]), W.to_f32(k), W.to_f32(v), None)
+        nb = -(-L // 32)
+        for name, got, want in (
+                ("k_codes", mx.k_codes[b, :, :L], qq["k_codes"][0]),
+                ("k_scales", mx.k_scales[b, :, :L], qq["k_scales"][0]),
+                ("v_codes", mx.v_codes[b, :, :nb], qq["v_codes"][0]),
+                ("v_scales", mx.v_scales[b, :, :nb], qq["v_scales"][0])):
+            assert np.array_equal(got.cpu().numpy(), want), "cache %s of sequence %d" % (name, b)
+        kw = dict(causal=True, bc=bc, chunk=split[0], chunk_phase=split[1][b:b + 1], tau=FAST)
+        ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], **kw)
+        vmax = np.abs(W.to_f32(v)).max()
+        worst = max(worst, float(np.abs(o[b:b + 1] - ref["o"]).max() / vmax))
+        _check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L),
+                    redo=_redo(qq, **kw))
+    print("decode: worst max|O - oracle| / max|V| over the 64 sequences = %.4g" % worst)
 
 
 @pytest.mark.parametrize("tau", [0.0, FAST])
@@ -339,12 +469,18 @@ def test_prefill_with_q_from_activations_full_size():
     assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
 
 
-def _check_rows_direct(o_gpu, lse_gpu, ref, vmax, what):
-    """The non-reordered variant against the oracle's o_naive / l_naive."""
+def _naive(ref):
+    """The oracle's non-reordered quantities as (o, lse)."""
     fin = np.isfinite(ref["lse"])
     lse_naive = np.where(fin, ref["lse"] - np.log(np.where(fin, ref["l"], 1.0))
                          + np.log(np.where(fin, ref["l_naive"], 1.0)), -np.inf)
-    _check_rows(o_gpu, lse_gpu, dict(o=ref["o_naive"], lse=lse_naive), vmax, what + " (direct l)")
+    return dict(o=ref["o_naive"], lse=lse_naive)
+
+
+def _check_rows_direct(o_gpu, lse_gpu, ref, vmax, what, redo=None):
+    """The non-reordered variant against the oracle's o_naive / l_naive."""
+    redo_n = (lambda rows, sh: _naive(redo(rows, sh))) if redo is not None else None
+    _check_rows(o_gpu, lse_gpu, _naive(ref), vmax, what + " (direct l)", redo=redo_n)
 
 
 @pytest.mark.parametrize("tau", [0.0, FAST])
@@ -368,7 +504,8 @@ def test_prefill_direct_normaliser_matches_oracle(case, tau):
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=64,
                            quant_p=True, tau=tau)
     vmax = np.abs(W.to_f32(inp["v"])).max()
-    _check_rows_direct(out.float().cpu().numpy(), lse.cpu().numpy(), ref, vmax, "case %s" % (case,))
+    _check_rows_direct(out.float().cpu().numpy(), lse.cpu().numpy(), ref, vmax, "case %s" % (case,),
+                       redo=_redo(qq, causal=causal, bc=64, quant_p=True, tau=tau))
 
 
 @pytest.mark.parametrize("chunk", [0, 192])
@@ -394,8 +531,9 @@ def test_decode_direct_normaliser_matches_oracle(chunk):
     p = hb.make_params(B, Hq, Hkv, 1, cap, d, causal=True, kv_stride=cap, decode_chunk=chunk)
     split = _decode_split(p, lens, Hkv)
     for b, L in enumerate(lens):
-        ref, vmax = _decode_oracle(cfg, q, b, L, 64, split, tau=FAST)
-        _check_rows_direct(o[b:b + 1], l[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L))
+        ref, vmax, redo = _decode_oracle(cfg, q, b, L, 64, split, tau=FAST, with_redo=True)
+        _check_rows_direct(o[b:b + 1], l[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L),
+                           redo=redo)
 
 
 def test_normaliser_ab_accuracy_full_size():
@@ -417,8 +555,9 @@ def test_normaliser_ab_accuracy_full_size():
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=True, bc=64,
                            quant_p=True, rows=rows, tau=FAST)
     vmax = np.abs(W.to_f32(inp["v"])).max()
-    _check_rows(res[0][0][rows], res[0][1][rows], ref, vmax, "P-Reordering")
-    _check_rows_direct(res[1][0][rows], res[1][1][rows], ref, vmax, "direct")
+    redo = _redo(qq, rows=rows, causal=True, bc=64, quant_p=True, tau=FAST)
+    _check_rows(res[0][0][rows], res[0][1][rows], ref, vmax, "P-Reordering", redo=redo)
+    _check_rows_direct(res[1][0][rows], res[1][1][rows], ref, vmax, "direct", redo=redo)
     exact = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
                              causal=True, bc=64, quant_p=False, rows=rows)
     for norm, name in ((0, "P-Reordering"), (1, "direct l")):

@@ -113,7 +113,8 @@ def test_noclip_prefill_matches_oracle(case, tau):
     ref = oracle.attention(qq["q_deq"], qq["k_deq"], qq["v_deq"], causal=causal, bc=64,
                            quant_p=True, tau=tau, p_rule=NC)
     vmax = np.abs(W.to_f32(inp["v"])).max()
-    TG._check_rows(out.float().cpu().numpy(), lse.cpu().numpy(), ref, vmax, "case %s" % (case,))
+    TG._check_rows(out.float().cpu().numpy(), lse.cpu().numpy(), ref, vmax, "case %s" % (case,),
+                   redo=TG._redo(qq, causal=causal, bc=64, quant_p=True, tau=tau, p_rule=NC))
 
 
 @pytest.mark.parametrize("chunk,tau", [(0, TG.FAST), (192, 0.0)])
@@ -123,8 +124,10 @@ def test_noclip_decode_matches_oracle(chunk, tau):
     print("no-clip decode parity: chunk", chunk, "tau", tau, flush=True)
     q, o, lse, bc, split = TG._decode_case(cfg, lens, cap=704, chunk=chunk, tau=tau, rule=NC)
     for b, L in enumerate(lens):
-        ref, vmax = TG._decode_oracle(cfg, q, b, L, bc, split, tau=tau, rule=NC)
-        TG._check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L))
+        ref, vmax, redo = TG._decode_oracle(cfg, q, b, L, bc, split, tau=tau, rule=NC,
+                                            with_redo=True)
+        TG._check_rows(o[b:b + 1], lse[b:b + 1], ref, vmax, "decode b=%d L=%d" % (b, L),
+                       redo=redo)
 
 
 def test_noclip_vs_ocp_accuracy_qwen3_slice():

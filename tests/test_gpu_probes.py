@@ -48,6 +48,7 @@ def lib():
     l.probe_half_swap.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_exp2_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    l.probe_mfma16_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_lds_dma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_buffer_range.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p]
@@ -280,6 +281,13 @@ def test_issue_rates_report(lib):
     print("fp4 32x32x64 MFMA: %.3g TFLOP/s (%.1f%% of 10.066 PFLOP/s), %.1f cycles per MFMA per SIMD"
           % (flops / t / 1e12, flops / t / 10.066e15 * 100, t * 2.4e9 * 1024 / mfmas))
     assert per_cu_clk > 4 and flops / t > 1e15
+    t16 = _time(lambda: lib.probe_mfma16_rate(out.data_ptr(), n_blocks, iters, _stream()))
+    mfmas16 = n_blocks * 4 * iters * 8
+    flops16 = mfmas16 * 2 * 16 * 16 * 128
+    print("fp4 16x16x128 MFMA: %.3g TFLOP/s (%.1f%% of 10.066 PFLOP/s), %.1f cycles per MFMA per "
+          "SIMD" % (flops16 / t16 / 1e12, flops16 / t16 / 10.066e15 * 100,
+                    t16 * 2.4e9 * 1024 / mfmas16))
+    assert flops16 / t16 > 1e15
 
 
 @pytest.mark.parametrize("size", [1, 2, 4, 16])
