@@ -8,7 +8,7 @@ the tensors are not on the GPU, the calls raise.
 
 The Python names match the C entry points: ``hifa4_quantize_qkv``,
 ``hifa4_quantize_qkv_rope``, ``hifa4_kv_append``, ``hifa4_smooth_calibrate``,
-``hifa4_smooth_calibrate_workspace_size``, ``hifa4_attn_fwd``,
+``hifa4_smooth_calibrate_workspace_size``, ``hifa4_attn_fwd``, ``hifa4_attn_fwd_noalloc``,
 ``hifa4_attn_fwd_qraw``, ``bf16_attn_fwd``, ``hifa4_attn_schedule``,
 ``hifa4_attn_decode_piece_tiles``, ``hifa4_attn_workspace_size``,
 ``hifa4_status_string``, ``hifa4_last_error``.
@@ -34,6 +34,9 @@ HIFA4_BF16 = 0
 HIFA4_FP16 = 1
 SCALE_OCP = 0     # hifa4_scale_rule: OCP MX shared exponent
 SCALE_NOCLIP = 1  # one higher wherever OCP would saturate an element
+
+# Device scratch behind hifa4_attn_fwd_noalloc, per GPU (HIFA4_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # Lazy-rescale threshold (log2 units) the benchmark and the full-size tests run
 # with: a row's running max moves only when a key tile raises it by more than
@@ -112,6 +115,9 @@ def load_library(path: str = LIB_PATH):
     lib.hifa4_attn_fwd.restype = st
     lib.hifa4_attn_fwd.argtypes = [ctypes.POINTER(AttnParamsC), MxTensorC, MxTensorC, MxTensorC,
                                    vp, st, vp, vp, ctypes.c_size_t, vp]
+    lib.hifa4_attn_fwd_noalloc.restype = st
+    lib.hifa4_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnParamsC), MxTensorC, MxTensorC,
+                                           MxTensorC, vp, st, vp, vp]
     lib.hifa4_attn_fwd_qraw.restype = st
     lib.hifa4_attn_fwd_qraw.argtypes = [ctypes.POINTER(AttnParamsC), vp, st, vp, MxTensorC,
                                         MxTensorC, vp, st, vp, vp, ctypes.c_size_t, vp]
@@ -475,6 +481,34 @@ def hifa4_attn_fwd(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,
                               _dtype_code(out.dtype), _ptr(lse), _ptr(workspace),
                               workspace.numel() if workspace is not None else 0,
                               _stream(stream)))
+    return out, lse
+
+
+def hifa4_attn_fwd_noalloc(mx: MXQKV, *, causal: bool, sm_scale: Optional[float] = None,
+                           kv_lens: Optional[torch.Tensor] = None, decode_chunk: int = 0,
+                           out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                           rescale_threshold: float = 0.0, normaliser: int = 0,
+                           scale_rule: int = SCALE_OCP, stream=None):
+    """hifa4_attn_fwd with the decode partials in the library's own device scratch: the
+    caller passes every buffer (out, and lse or None) and nothing is allocated.  Calls that
+    overlap on one GPU share that scratch and must be serialised by the caller."""
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != mx.B):
+        raise ValueError("kv_lens must be int32 [B]")
+    p = make_params(mx.B, mx.Hq, mx.Hkv, mx.Sq, mx.Sk, mx.d, causal=causal, sm_scale=sm_scale,
+                    kv_stride=mx.kv_stride, kv_lens=kv_lens, decode_chunk=decode_chunk,
+                    rescale_threshold=rescale_threshold, normaliser=normaliser,
+                    scale_rule=scale_rule)
+    _check_out_lse(out, lse, mx.B, mx.Hq, mx.Sq, mx.d)
+    _check_row_mx(mx.q_codes, mx.q_scales, mx.B * mx.Hq * mx.Sq, mx.d, "q")
+    cap = mx.kv_stride or mx.Sk
+    if cap:
+        _check_row_mx(mx.k_codes, mx.k_scales, mx.B * mx.Hkv * cap, mx.d, "k")
+        _check_col_mx(mx.v_codes, mx.v_scales, mx.B * mx.Hkv, cap, mx.d, "v")
+    _check(load_library().hifa4_attn_fwd_noalloc(
+        ctypes.byref(p), MxTensorC(_ptr(mx.q_codes), _ptr(mx.q_scales)),
+        MxTensorC(_ptr(mx.k_codes), _ptr(mx.k_scales)),
+        MxTensorC(_ptr(mx.v_codes), _ptr(mx.v_scales)), _ptr(out), _dtype_code(out.dtype),
+        _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhifa4.so")
 PROBES_LIB = os.path.join(PKG, "libhifa4_probes.so")
 
-LIB_SOURCES = ["api.cpp", "quantize.hip", "attn_mxfp4.hip", "attn_bf16.hip"]
+LIB_SOURCES = ["api.cpp", "quantize.hip", "attn_mxfp4.hip", "attn_bf16.hip", "scratch.hip"]
 PROBE_SOURCES = ["probes.hip"]
 
 

@@ -607,6 +607,30 @@ hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tensor q, hifa4
                        workspace_bytes, stream);
 }
 
+hifa4_status hifa4_attn_fwd_noalloc(const hifa4_attn_params* p, hifa4_mx_tensor q,
+                                    hifa4_mx_tensor k, hifa4_mx_tensor v, void* out,
+                                    hifa4_dtype out_dtype, float* lse, void* stream) {
+  g_last_error.clear();
+  int cap, chunk;
+  hifa4_status st = check_params(p, &cap, &chunk);
+  if (st != HIFA4_OK) return st;
+  const size_t need = decode_workspace(p, chunk);
+  static_assert(hifa4::kStaticScratchBytes == HIFA4_NOALLOC_SCRATCH_BYTES,
+                "the header states the scratch size");
+  if (need > hifa4::kStaticScratchBytes)
+    return fail(HIFA4_ERR_UNSUPPORTED,
+                "decode partials need %zu bytes, more than the %zu-byte device scratch of "
+                "hifa4_attn_fwd_noalloc (use hifa4_attn_fwd with a workspace)",
+                need, hifa4::kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need) {
+    const hipError_t e = hifa4::static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "device scratch lookup");
+  }
+  return attn_fwd_impl(p, q, nullptr, HIFA4_BF16, nullptr, k, v, out, out_dtype, lse, ws,
+                       need ? hifa4::kStaticScratchBytes : 0, stream);
+}
+
 hifa4_status hifa4_attn_fwd_qraw(const hifa4_attn_params* p, const void* q, hifa4_dtype q_dtype,
                                  const float* smooth, hifa4_mx_tensor k, hifa4_mx_tensor v,
                                  void* out, hifa4_dtype out_dtype, float* lse, void* workspace,

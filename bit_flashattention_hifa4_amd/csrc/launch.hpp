@@ -119,6 +119,11 @@ __host__ __device__ inline int decode_piece_tiles(int chunk, int waves, int tota
 hipError_t launch_attn_prefill_mxfp4(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_decode_mxfp4(const AttnArgs& a, hipStream_t stream);
 
+// Device scratch of the allocation-free entry point: bytes per device, and its
+// device address on the current device (looked up on the first call there).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(void** ptr);
+
 struct Bf16AttnArgs {
   const uint16_t* q;
   const uint16_t* k;

@@ -286,6 +286,28 @@ HIFA4_API hifa4_status hifa4_attn_fwd(const hifa4_attn_params* p, hifa4_mx_tenso
                             hifa4_mx_tensor v, void* out, hifa4_dtype out_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch behind hifa4_attn_fwd_noalloc, per GPU. */
+#define HIFA4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * hifa4_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments, layouts and errors as hifa4_attn_fwd, but
+ * the decode partials live in a device array inside the library
+ * (HIFA4_NOALLOC_SCRATCH_BYTES on every GPU it runs on, held until the process
+ * ends) instead of a caller workspace.  The caller still passes inputs and
+ * outputs.  A problem whose partials need more (hifa4_attn_workspace_size)
+ * returns HIFA4_ERR_UNSUPPORTED with nothing enqueued; prefill needs none.
+ * The call allocates nothing: the first call on a device looks up the array's
+ * address there (the device current at the call must be the stream's).
+ * Every call on one GPU shares that array, so calls that may overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller; each call writes every partial it reads, so nothing needs clearing.
+ */
+HIFA4_API hifa4_status hifa4_attn_fwd_noalloc(const hifa4_attn_params* p, hifa4_mx_tensor q,
+                                              hifa4_mx_tensor k, hifa4_mx_tensor v, void* out,
+                                              hifa4_dtype out_dtype, float* lse, void* stream);
+
 /*
  * hifa4_attn_fwd for prefill (Sq > 1) with Q given as activations: q is device
  * [B][Hq][Sq][d] in q_dtype (bf16 or fp16, contiguous, 16-byte aligned) and

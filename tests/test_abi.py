@@ -344,3 +344,22 @@ def test_status_strings(lib):
         assert hb.hifa4_status_string(s)
     assert hb.hifa4_status_string(5) == "unknown status"
 
+
+def test_noalloc_refuses_partials_beyond_its_scratch(lib):
+    """hifa4_attn_fwd_noalloc: decode partials larger than its device scratch are refused
+    before any HIP call (64 sequences x 8 KV heads x 32 query heads each at d = 256)."""
+    B, Hkv, G, d, cap = 64, 8, 32, 256, 32768
+    p = hb.make_params(B, Hkv * G, Hkv, 1, cap, d, causal=True, kv_stride=cap)
+    assert hb.hifa4_attn_workspace_size(p) > hb.NOALLOC_SCRATCH_BYTES
+    st = lib.hifa4_attn_fwd_noalloc(ctypes.byref(p), _mx(0x10000000), _mx(0x30000000),
+                                    _mx(0x50000000), 0x70000000, hb.HIFA4_BF16, None, None)
+    assert st == hb.HIFA4_ERR_UNSUPPORTED
+    assert "scratch" in hb.hifa4_last_error()
+    # parameters are validated first, as in hifa4_attn_fwd
+    st = lib.hifa4_attn_fwd_noalloc(ctypes.byref(_params(d=32)), _mx(0x10000000),
+                                    _mx(0x30000000), _mx(0x50000000), 0x70000000, hb.HIFA4_BF16,
+                                    None, None)
+    assert st == hb.HIFA4_ERR_UNSUPPORTED and "head dim" in hb.hifa4_last_error()
+    assert lib.hifa4_attn_fwd_noalloc(None, _mx(0x10000000), _mx(0x30000000), _mx(0x50000000),
+                                      0x70000000, hb.HIFA4_BF16, None, None) \
+        == hb.HIFA4_ERR_INVALID_ARGUMENT
