@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "hifa4.h"
@@ -14,6 +16,16 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// HIFA4_LOG set to a non-empty value other than "0": every attention launch
+// prints its schedule (workgroups, key tile, decode split, workspace) to stderr.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("HIFA4_LOG");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
 
 hifa4_status fail(hifa4_status s, const char* fmt, ...) {
   char buf[512];
@@ -229,6 +241,23 @@ static hifa4_status attn_fwd_impl(const hifa4_attn_params* p, hifa4_mx_tensor q,
   a.direct_l = p->normaliser;
   scale_bias(p->scale_rule, &a.p_bias);  // checked in check_params
   a.q_bias = a.p_bias;
+  if (log_enabled()) {
+    const int bn = hifa4::attn_block_n(d);
+    if (p->Sq == 1)
+      std::fprintf(stderr,
+                   "[hifa4] decode B=%d Hq=%d Hkv=%d d=%d cap=%d key tile %d, %s split "
+                   "(%d-token runs), persistent grid %d waves, workspace %zu bytes%s\n",
+                   p->B, p->Hq, p->Hkv, d, cap, bn, chunk ? "per-pair" : "balanced",
+                   chunk, a.dec_waves, need, p->normaliser ? ", direct normaliser" : "");
+    else
+      std::fprintf(stderr,
+                   "[hifa4] prefill B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d %s, %lld workgroups of "
+                   "128 queries (4 waves), key tile %d, threshold %g, Q %s%s\n",
+                   p->B, p->Hq, p->Hkv, p->Sq, p->Sk, d, p->causal ? "causal" : "non-causal",
+                   (long long)((p->Sq + 127) / 128) * p->B * p->Hq, bn, (double)a.tau,
+                   q_raw ? "quantised in the prologue" : "as MX codes",
+                   p->normaliser ? ", direct normaliser" : "");
+  }
   hipError_t e = p->Sq == 1 ? hifa4::launch_attn_decode_mxfp4(a, (hipStream_t)stream)
                             : hifa4::launch_attn_prefill_mxfp4(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported)
