@@ -154,6 +154,63 @@ __global__ __launch_bounds__(256) void mfma16_rate_kernel(float* out, int iters)
   out[blockIdx.x * blockDim.x + l] = t;
 }
 
+// Co-execution of the matrix core and the vector ALU: 512-thread blocks (two
+// waves per SIMD), per iteration 16 FP4 32x32x64 MFMAs (four independent
+// chains) and 32 exp2(fma) pairs (eight independent chains).  mode 0: MFMAs
+// only; 1: vector work only; 2: both, interleaved in every wave; 3: waves 0-3
+// (one per SIMD) the MFMAs, waves 4-7 the vector work, so each SIMD holds one
+// wave of each kind.
+__global__ __launch_bounds__(512) void coexec_kernel(float* out, int mode, int iters) {
+  const int l = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const uint4 a = make_uint4(0x22222222u ^ l, 0x12345678u, 0x0u, 0x76543210u);
+  const uint4 b = make_uint4(0x11111111u, 0x22222222u ^ l, 0x33333333u, 0x0u);
+  v16f c[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) c[j] = v16f{};
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) x[j] = 0.001f * (threadIdx.x + j);
+  const int s = 127 + (l & 1);
+  const bool do_m = mode == 0 || mode == 2 || (mode == 3 && w < 4);
+  const bool do_v = mode == 1 || mode == 2 || (mode == 3 && w >= 4);
+  if (mode == 2) {
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) c[i % 4] = mfma_fp4_32x32x64(i & 1 ? a : b, i & 2 ? b : a, c[i % 4], s, s);
+#pragma unroll
+      for (int j = 0; j < 32; j++)
+        x[j % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j % 8], 0.5f, -0.25f));
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    }
+  } else {
+    if (do_m)
+      for (int it = 0; it < iters; it++) {
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+          c[i % 4] = mfma_fp4_32x32x64(i & 1 ? a : b, i & 2 ? b : a, c[i % 4], s, s);
+      }
+    if (do_v)
+      for (int it = 0; it < iters; it++) {
+#pragma unroll
+        for (int j = 0; j < 32; j++)
+          x[j % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j % 8], 0.5f, -0.25f));
+      }
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) t += c[j][r];
+#pragma unroll
+  for (int j = 0; j < 8; j++) t += x[j];
+  out[blockIdx.x * 512 + threadIdx.x] = t;
+}
+
 // Memory -> LDS buffer loads (the LDS-destination form): one wave loads
 // `size`-byte elements, lane i from source byte offset size*i, with M0 = 64;
 // the LDS window is pre-filled with 0xEE and copied out afterwards, so the
@@ -311,6 +368,13 @@ int probe_mfma_rate(float* out, int n_blocks, int iters, void* stream) {
 int probe_mfma16_rate(float* out, int n_blocks, int iters, void* stream) {
   if (n_blocks <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma16_rate_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, out,
+                     iters);
+  return status(hipGetLastError());
+}
+
+int probe_coexec(float* out, int mode, int n_blocks, int iters, void* stream) {
+  if (n_blocks <= 0 || iters <= 0 || mode < 0 || mode > 3) return -1;
+  hipLaunchKernelGGL(coexec_kernel, dim3(n_blocks), dim3(512), 0, (hipStream_t)stream, out, mode,
                      iters);
   return status(hipGetLastError());
 }

@@ -61,6 +61,15 @@ HIFA4_PROBE_API int probe_mfma_rate(float* out, int n_blocks, int iters, void* s
  * independent chains of `iters` MFMAs (65536 flops each); out[n_blocks * 256]. */
 HIFA4_PROBE_API int probe_mfma16_rate(float* out, int n_blocks, int iters, void* stream);
 
+/* Co-execution of FP4 MFMAs and vector work: n_blocks x 512 threads (two waves
+ * per SIMD), per iteration 16 FP4 32x32x64 MFMAs (4 independent chains) and 32
+ * exp2(fma) pairs (8 independent chains), iters times.  mode 0: MFMAs only;
+ * 1: vector work only; 2: both in every wave, interleaved; 3: waves 0-3 the
+ * MFMAs and waves 4-7 the vector work (one wave of each kind per SIMD).
+ * out: [n_blocks * 512] floats (keeps the work alive).  Returns -1 on a bad
+ * argument. */
+HIFA4_PROBE_API int probe_coexec(float* out, int mode, int n_blocks, int iters, void* stream);
+
 /* One wave of memory -> LDS buffer loads of `size` bytes per lane (1, 2, 4 or
  * 16), lane i reading src bytes [size*i, size*(i+1)) (src: 1024 bytes), with
  * M0 = LDS window + 64.  out: the 1088-byte window afterwards (pre-filled

@@ -49,6 +49,8 @@ def lib():
     l.probe_exp2_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_mfma16_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    l.probe_coexec.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_void_p]
     l.probe_lds_dma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_buffer_range.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p]
@@ -288,6 +290,29 @@ def test_issue_rates_report(lib):
           "SIMD" % (flops16 / t16 / 1e12, flops16 / t16 / 10.066e15 * 100,
                     t16 * 2.4e9 * 1024 / mfmas16))
     assert flops16 / t16 > 1e15
+
+
+def test_mfma_and_vector_co_execution_report(lib):
+    """How much FP4 MFMA work and exp2 / fma work overlap on a SIMD: alone, interleaved
+    inside each of two waves, and split over two waves of one kind each.  Cycles per
+    SIMD per iteration (16 MFMAs and 32 exp2(fma) pairs per wave-iteration)."""
+    n_blocks, iters = 256, 2000
+    out = torch.zeros(n_blocks * 512, device="cuda")
+    cyc = {}
+    for mode, name in ((0, "mfma only"), (1, "vector only"), (2, "both, every wave"),
+                       (3, "one wave of each kind")):
+        t = _time(lambda: lib.probe_coexec(out.data_ptr(), mode, n_blocks, iters, _stream()))
+        # two waves per SIMD; modes 0-2 give each SIMD two waves' worth of the work
+        cyc[mode] = t * 2.4e9 / iters
+        print("co-execution, %s: %.0f cycles per SIMD per iteration" % (name, cyc[mode]))
+    assert lib.probe_coexec(out.data_ptr(), 4, n_blocks, iters, _stream()) == -1
+    # in mode 3 each SIMD does half of mode 2's work: one wave's MFMAs beside one wave's
+    # vector work; that overlap is near perfect when the pair costs no more than the
+    # slower kind alone (half of modes 0 / 1) plus a quarter of the faster one
+    one = max(cyc[0], cyc[1]) / 2 + min(cyc[0], cyc[1]) / 8
+    print("one of each kind: %.0f cycles against %.0f for the slower kind alone"
+          % (cyc[3], max(cyc[0], cyc[1]) / 2))
+    assert cyc[3] < one * 1.2
 
 
 @pytest.mark.parametrize("size", [1, 2, 4, 16])
