@@ -5,20 +5,26 @@
 // summed on the vector ALU from the unrounded P.
 //
 // Same skeleton as the MXFP4 kernel: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
-// with the K rows loaded in a permuted order so that each lane's accumulator
+// with the K rows staged in a permuted order so that each lane's accumulator
 // registers already hold the keys of its P V operand (K = 16 keys per MFMA:
-// lane (q, h) needs keys 16u + 8h .. + 7 of MFMA u).  V is staged in LDS
-// transposed (channel-major) so its A operand is one 16-byte LDS read.  Tiles
-// are double-buffered: the next tile is loaded into registers while the
-// current one is computed, then written to the other LDS buffer (V transposed
-// four keys at a time, one 8-byte LDS write per channel).
+// lane (q, h) needs keys 16u + 8h .. + 7 of MFMA u).  K and V tiles go from
+// memory straight into LDS (buffer loads with the LDS destination) through
+// two-stage rings; V keeps its row-major layout and its operand (8 keys of
+// one channel per lane) is read with the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16).  K runs one tile ahead of V: step kt loads K tile
+// kt+2 and V tile kt+1, and, at raised wave priority, runs the Q K^T MFMAs of
+// tile kt+1 interleaved with the softmax of tile kt, then the P V MFMAs of
+// tile kt.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_dma.hpp"
 
 namespace hifa4 {
 namespace {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 64;
 constexpr int kBR = 128;
@@ -33,29 +39,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
-// Key (within the 64-key step) loaded as A row m of 32-key tile t.
+// Key (within the 64-key step) staged as A row m of 32-key tile t.
 __device__ __forceinline__ int perm_row_bf16(int t, int m) {
   const int j = m >> 3, hh = (m >> 2) & 1, i = m & 3;
   return 32 * t + 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + i;
 }
 
+// LDS stage layouts (one stage = one 64-key tile of K or of V, D bf16 per key).
+// Rows of RB = 2D bytes, NCH 16-byte chunks each; chunk c of row R sits in slot
+// c ^ swizzle(R), so that the operand reads of one LDS pass fall in distinct
+// banks (64 banks of 4 bytes):
+//  - K: row R = 32t + m holds key perm_row_bf16(t, m); a Q K^T read takes rows
+//    m = 0..15 at one chunk: the swizzle spreads them over the 16 bank groups;
+//  - V: row R holds key R; a transpose read takes rows r..r+3 (r % 4 == 0) at
+//    chunks 4cc..4cc+3: the swizzle 4 * (R % 4) puts the 16 in distinct groups.
+template <int D>
+struct Bf16Stage {
+  static constexpr int RB = 2 * D;
+  static constexpr int NCH = RB / 16;
+  static constexpr int BYTES = kBN * RB;
+  static constexpr int LOADS = BYTES / 1024 / 4;  // 1 KB loads per wave (4 waves)
+  static_assert(LOADS >= 1 && LOADS * 4096 == BYTES, "a stage splits into 1 KB loads per wave");
+};
+template <int D>
+__device__ __forceinline__ int k_swz_bf16(int R) {
+  return D == 64 ? (R >> 1) & 7 : R & 15;
+}
+template <int D>
+__device__ __forceinline__ int v_swz_bf16(int R) {
+  return D == 64 ? 4 * ((R >> 1) & 1) : 4 * (R & 3);
+}
+
 template <int D, bool kCausal>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bf16_kernel(Bf16AttnArgs a) {
+  using T = Bf16Stage<D>;
   constexpr int NJ = D / 16;     // QK MFMAs per 32-key tile
   constexpr int NC = D / 32;     // channel tiles
-  constexpr int VT = kBN + 8;    // padded key stride of the transposed V tile (elements)
-  // K rows padded by 16 bytes: the 16 lanes of one LDS read phase take 16 different
-  // rows at one column, which a power-of-two row stride would put in the same banks
-  constexpr int KS = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[2][D * VT];
-  // per thread and tile: KL 16-byte K chunks, VL groups of (4 keys, 8 channels)
-  constexpr int KL = kBN * D / 8 / 256;
-  constexpr int VITEMS = (kBN / 4) * (D / 8);
-  constexpr int VL = (VITEMS + 255) / 256;
-  static_assert(KL >= 1 && KL * 256 == kBN * D / 8, "K tile must split evenly over the workgroup");
+  constexpr int RB = T::RB;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2 * T::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * T::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
   const int G = a.Hq / a.Hkv;
   const int n_kv = a.B * a.Hkv;
@@ -73,19 +98,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
   const int q_wave0 = qt * kBR + wave * 32;
   const int q = q_wave0 + n;
 
-  v8s qa[NJ];
-  if (q < a.Sq) {
-    const uint16_t* qr = a.q + (bhq * a.Sq + q) * D;
-#pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      uint4 w = *reinterpret_cast<const uint4*>(qr + 16 * j + 8 * h);
-      __builtin_memcpy(&qa[j], &w, 16);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NJ; j++) qa[j] = v8s{};
-  }
-
   int kv_end = L, wave_end = L, wave_full = L;
   if (kCausal) {
     const int last_q = min(a.Sq, (qt + 1) * kBR) - 1;
@@ -99,121 +111,203 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
   const int row_lim = kCausal ? min(L, q + L - a.Sq + 1) : L;
   const float c = a.sm_log2;
 
+  // Staging: one descriptor per (batch, KV head) over its L valid keys (rows
+  // past them read zeros); lane i of load ii of this wave fills LDS slot
+  // p = (wave * LOADS + ii) * 64 + i of a stage, i.e. row p / NCH, slot p % NCH.
+  const v4i kdesc = buffer_desc(a.k + bkv * a.cap * D, (uint32_t)L * RB);
+  const v4i vdesc = buffer_desc(a.v + bkv * a.cap * D, (uint32_t)L * RB);
+  uint32_t koff_src[T::LOADS], voff_src[T::LOADS];
+#pragma unroll
+  for (int ii = 0; ii < T::LOADS; ii++) {
+    const int p = (wave * T::LOADS + ii) * 64 + lane;
+    const int R = p / T::NCH, sl = p % T::NCH;
+    koff_src[ii] = (uint32_t)(perm_row_bf16(R >> 5, R & 31) * RB + ((sl ^ k_swz_bf16<D>(R)) * 16));
+    voff_src[ii] = (uint32_t)(R * RB + ((sl ^ v_swz_bf16<D>(R)) * 16));
+  }
+  const uint32_t kdst = lds_addr(lds_k) + wave * T::LOADS * 1024;
+  const uint32_t vdst = lds_addr(lds_v) + wave * T::LOADS * 1024;
+  auto issue_k = [&](auto stage, int tile) {
+    constexpr int ST = decltype(stage)::value;
+    const int so = tile < n_tiles ? tile * kBN * RB : 0x7FFFFFF0;
+#pragma unroll
+    for (int ii = 0; ii < T::LOADS; ii++) {
+      switch (ii) {  // the LDS immediate must be a constant
+#define HIFA4_BF16_K(I) case I: if constexpr (I < T::LOADS) load_lds16<ST * T::BYTES + I * 1024>(kdesc, koff_src[I], so, kdst); break;
+        HIFA4_BF16_K(0) HIFA4_BF16_K(1) HIFA4_BF16_K(2) HIFA4_BF16_K(3)
+        HIFA4_BF16_K(4) HIFA4_BF16_K(5) HIFA4_BF16_K(6) HIFA4_BF16_K(7)
+#undef HIFA4_BF16_K
+      }
+    }
+  };
+  auto issue_v = [&](auto stage, int tile) {
+    constexpr int ST = decltype(stage)::value;
+    const int so = tile < n_tiles ? tile * kBN * RB : 0x7FFFFFF0;
+#pragma unroll
+    for (int ii = 0; ii < T::LOADS; ii++) {
+      switch (ii) {
+#define HIFA4_BF16_V(I) case I: if constexpr (I < T::LOADS) load_lds16<ST * T::BYTES + I * 1024>(vdesc, voff_src[I], so, vdst); break;
+        HIFA4_BF16_V(0) HIFA4_BF16_V(1) HIFA4_BF16_V(2) HIFA4_BF16_V(3)
+        HIFA4_BF16_V(4) HIFA4_BF16_V(5) HIFA4_BF16_V(6) HIFA4_BF16_V(7)
+#undef HIFA4_BF16_V
+      }
+    }
+  };
+  static_assert(T::LOADS <= 8, "at most eight loads per wave and tile");
+
+  // Q operand (B of S^T = K Q^T): query q, elements 16j + 8h .. + 7
+  v8s qa[NJ];
+  if (q < a.Sq) {
+    const uint16_t* qr = a.q + (bhq * a.Sq + q) * D;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      uint4 w = *reinterpret_cast<const uint4*>(qr + 16 * j + 8 * h);
+      __builtin_memcpy(&qa[j], &w, 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; j++) qa[j] = v8s{};
+  }
+
+  // The lane's K operand offsets in a stage: row n (tile 0; tile 1 adds 32
+  // rows, whose swizzle is the same), chunk 2j + h.
+  uint32_t koff[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; j++) koff[j] = (uint32_t)(n * RB + (((2 * j + h) ^ k_swz_bf16<D>(n)) * 16));
+  // The lane's V transpose-read offsets: in its 16-lane group gq = lane / 16
+  // the lane (4i + a4) points at key 8 (gq / 2) + i (plus 16u + 4r per read)
+  // and channels 32cc + 16 (gq % 2) + 4 a4 .. + 3; the read returns channel
+  // 32cc + n of keys 16u + 8h + 4r .. + 3 to lane (n, h).
+  uint32_t voff[NC];
+  {
+    const int gq = lane >> 4, jl = lane & 15, i4 = jl >> 2, a4 = jl & 3;
+    const int R = 8 * (gq >> 1) + i4;
+#pragma unroll
+    for (int cc = 0; cc < NC; cc++) {
+      const int byte = 2 * (32 * cc + 16 * (gq & 1) + 4 * a4);  // within the row
+      voff[cc] = (uint32_t)(R * RB + (((byte >> 4) ^ v_swz_bf16<D>(R)) << 4) + (byte & 15));
+    }
+  }
+
   float m_run = -INFINITY, l_run = 0.0f;
   v16f acc[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; cc++) acc[cc] = v16f{};
 
-  // tile loads into registers (keys past L read as zeros) and their LDS stores
-  uint4 kr[KL], vr[VL][4];
-  auto load_tile = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < KL; i++) {
-      const int ci = tid + 256 * i;
-      const int row = ci / (D / 8), off = (ci % (D / 8)) * 8;
-      kr[i] = n0 + row < L
-                  ? *reinterpret_cast<const uint4*>(a.k + (bkv * a.cap + n0 + row) * D + off)
-                  : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VL; i++) {
-      const int ci = tid + 256 * i;
-      const int k4 = ci % (kBN / 4), cg = (ci / (kBN / 4)) * 8;
-#pragma unroll
-      for (int kk = 0; kk < 4; kk++) {
-        const int key = 4 * k4 + kk;
-        vr[i][kk] = ci < VITEMS && n0 + key < L
-                        ? *reinterpret_cast<const uint4*>(a.v + (bkv * a.cap + n0 + key) * D + cg)
-                        : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KL; i++) {
-      const int ci = tid + 256 * i;
-      const int row = ci / (D / 8), off = (ci % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(lds_k[buf] + row * KS + off) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VL; i++) {
-      const int ci = tid + 256 * i;
-      if (ci >= VITEMS) break;
-      const int k4 = ci % (kBN / 4), cg = (ci / (kBN / 4)) * 8;
-      const uint32_t wk[4][4] = {{vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w},
-                                 {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w},
-                                 {vr[i][2].x, vr[i][2].y, vr[i][2].z, vr[i][2].w},
-                                 {vr[i][3].x, vr[i][3].y, vr[i][3].z, vr[i][3].w}};
-      // channel c of keys 4 k4 .. 4 k4 + 3: one 8-byte write
-#pragma unroll
-      for (int c2 = 0; c2 < 4; c2++) {
-        const uint32_t w0 = wk[0][c2], w1 = wk[1][c2], w2 = wk[2][c2], w3 = wk[3][c2];
-        // low halves: channel cg + 2 c2, high halves: channel cg + 2 c2 + 1
-        const uint2 lo = make_uint2((w0 & 0xFFFFu) | (w1 << 16), (w2 & 0xFFFFu) | (w3 << 16));
-        const uint2 hi = make_uint2((w0 >> 16) | (w1 & 0xFFFF0000u), (w2 >> 16) | (w3 & 0xFFFF0000u));
-        *reinterpret_cast<uint2*>(lds_vt[buf] + (cg + 2 * c2) * VT + 4 * k4) = lo;
-        *reinterpret_cast<uint2*>(lds_vt[buf] + (cg + 2 * c2 + 1) * VT + 4 * k4) = hi;
-      }
-    }
-  };
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; kt++) {
-    const int n0 = kt * kBN;
-    const int buf = kt & 1;
-    const bool more = kt + 1 < n_tiles;  // uniform
-    if (more) load_tile(n0 + kBN);
-    const uint16_t* lk = lds_k[buf];
-    const uint16_t* lv = lds_vt[buf];
-    if (n0 < wave_end) {
-
-    v16f s0 = v16f{}, s1 = v16f{};
-    const int r0 = perm_row_bf16(0, n), r1 = perm_row_bf16(1, n);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // S^T = K Q^T of the tile in K stage ks
+  auto qk = [&](int ks_bytes, v16f& s0, v16f& s1) {
+    const uint8_t* lk = lds_k + ks_bytes;
+    s0 = v16f{};
+    s1 = v16f{};
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
       v8s k0, k1;
-      uint4 w0 = *reinterpret_cast<const uint4*>(lk + r0 * KS + 16 * j + 8 * h);
-      uint4 w1 = *reinterpret_cast<const uint4*>(lk + r1 * KS + 16 * j + 8 * h);
+      const uint4 w0 = *reinterpret_cast<const uint4*>(lk + koff[j]);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(lk + 32 * RB + koff[j]);
       __builtin_memcpy(&k0, &w0, 16);
       __builtin_memcpy(&k1, &w1, 16);
       s0 = mfma_bf16_32x32x16(k0, qa[j], s0);
       s1 = mfma_bf16_32x32x16(k1, qa[j], s1);
     }
-    // lane (q, h): tile t register r holds key 32t + 16*(r/8) + 8h + r%8
+  };
+
+  // prologue: K tiles 0, 1 and V tile 0
+  issue_k(S0{}, 0);
+  issue_v(S0{}, 0);
+  issue_k(S1{}, 1);
+  HIFA4_WAIT_VMCNT(0);
+  __syncthreads();
+  // a wave whose rows see no key never computes (sa0, sa1): zeros, then masked
+  v16f sa0 = v16f{}, sa1 = v16f{}, sb0, sb1;
+  if (n_tiles > 0) qk(0, sa0, sa1);
+  // step 0 refills K stage 0: every wave's reads of it come first
+  __syncthreads();
+
+  // One step on tile kt (K and V stage kt % 2 = ST), scores in (c0, c1): loads
+  // of K tile kt+2 (into K stage ST, whose tile kt was read by step kt-1) and
+  // V tile kt+1 (into V stage ST ^ 1, whose tile kt-1 step kt-1 read); at wave
+  // priority 1 the softmax of tile kt interleaved with the Q K^T MFMAs of tile
+  // kt+1 (K stage ST ^ 1, into (n0r, n1r)), then the P V MFMAs of tile kt;
+  // wait for this step's loads; barrier.  A wave whose rows see no key of tile
+  // kt masks all its scores (P = 0, the running max stays); the products of a
+  // tile past the last read finite stale LDS and are discarded.
+  auto step = [&](auto stage, int kt, v16f& c0, v16f& c1, v16f& n0r, v16f& n1r) {
+    constexpr int ST = decltype(stage)::value;
+    using SN = std::integral_constant<int, ST ^ 1>;
+    const int n0 = kt * kBN;
+    issue_k(stage, kt + 2);
+    issue_v(SN{}, kt + 1);
     float s[32];
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-      s[r] = s0[r];
-      s[16 + r] = s1[r];
+      s[r] = c0[r];
+      s[16 + r] = c1[r];
     }
-    if (n0 + kBN > wave_full) {
+    // lane (q, h): tile t register r holds key 32t + 16*(r/8) + 8h + r%8
+    if (n0 >= wave_end || n0 + kBN > wave_full) {
+      const int lim = n0 < wave_end ? row_lim : 0;
 #pragma unroll
       for (int k = 0; k < 32; k++) {
         const int key = n0 + 32 * (k >> 4) + 16 * ((k >> 3) & 1) + 8 * h + (k & 7);
-        if (key >= row_lim) s[k] = -INFINITY;
+        if (key >= lim) s[k] = -INFINITY;
       }
     }
-    float bm = s[0];
+    // max3 tree over the 32 scores, then the partner half's
+    float u[11];
 #pragma unroll
-    for (int k = 1; k < 32; k++) bm = fmaxf(bm, s[k]);
+    for (int i = 0; i < 10; i++)
+      u[i] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[3 * i], s[3 * i + 1]),
+                                           s[3 * i + 2]);
+    u[10] = __builtin_elementwise_maximum(s[30], s[31]);
+    float bm = u[0];
+#pragma unroll
+    for (int i = 1; i < 11; i++) bm = __builtin_elementwise_maximum(bm, u[i]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
                                                      false, false);
-    const float rmc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    const float rmc =
+        __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
     // lazy rescale (same rule as the MXFP4 kernel; exact attention is frame-free)
     const float m_new = rmc > m_run + a.tau ? rmc : m_run;
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float p[32];
-    float ps = 0.0f;
+    asm volatile("" : "+v"(qa[0][0]) : "v"(m_use));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    qk((ST ^ 1) * T::BYTES, n0r, n1r);
 #pragma unroll
-    for (int k = 0; k < 32; k++) {
-      p[k] = __builtin_amdgcn_exp2f(fmaf(s[k], c, -m_use));
-      ps += p[k];
+    for (int k = 0; k < 32; k++) s[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k], c, -m_use));
+    // row sum as a tree
+    float t16[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) t16[k] = s[2 * k] + s[2 * k + 1];
+#pragma unroll
+    for (int k = 0; k < 8; k++) t16[k] = t16[2 * k] + t16[2 * k + 1];
+#pragma unroll
+    for (int k = 0; k < 4; k++) t16[k] = t16[2 * k] + t16[2 * k + 1];
+    float ps = (t16[0] + t16[1]) + (t16[2] + t16[3]);
+    v8s pb[4];
+#pragma unroll
+    for (int uu = 0; uu < 4; uu++) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int k = 16 * (uu >> 1) + 8 * (uu & 1) + 2 * i;
+        pw[i] = pack_bf16x2(s[k], s[k + 1]);
+      }
+      __builtin_memcpy(&pb[uu], pw, 16);
     }
+    // the K operand reads two MFMAs ahead; each Q K^T MFMA followed by a few
+    // vector instructions of the softmax (4 at d = 128: 156.7 -> 144.7 us on the
+    // Qwen3 shape; 8 at d = 256)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NJ; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, D == 64 ? 12 : (D == 128 ? 4 : 8), 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     {
       const auto pw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps),
                                                        false, false);
@@ -225,28 +319,40 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(Bf16AttnArgs a) {
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) acc[cc] *= alpha;
     }
-    // P V: 4 MFMAs of 16 keys; MFMA u = 2t + j2 takes registers 8*j2 .. +7 of tile t
+    // P V: MFMA (u, cc) takes keys 16u .. 16u + 15 of channel tile cc; the
+    // lane's operand is two transpose reads of 4 keys each (keys 16u + 8h + 4r)
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const uint8_t* lv = lds_v + ST * T::BYTES;
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      uint32_t pw[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int k = 16 * (u >> 1) + 8 * (u & 1) + 2 * i;
-        pw[i] = pack_bf16x2(p[k], p[k + 1]);
-      }
-      v8s pb;
-      __builtin_memcpy(&pb, pw, 16);
+    for (int uu = 0; uu < 4; uu++) {
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
-        v8s va;
-        uint4 w = *reinterpret_cast<const uint4*>(lv + (32 * cc + n) * VT + 16 * u + 8 * h);
-        __builtin_memcpy(&va, &w, 16);
-        acc[cc] = mfma_bf16_32x32x16(va, pb, acc[cc]);
+        const uint8_t* p0 = lv + voff[cc] + (16 * uu) * RB;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s)(__attribute__((address_space(3))) uint8_t*)p0);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s)(__attribute__((address_space(3))) uint8_t*)(p0 + 4 * RB));
+        const v8s va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[cc] = mfma_bf16_32x32x16(va, pb[uu], acc[cc]);
       }
     }
-    }  // n0 < wave_end
-    if (more) store_tile(buf ^ 1);
+    // the V operand reads two MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * NC; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+    // the next tile's scores may not sink past the barrier into the next step
+    asm volatile("" : "+v"(n0r[0]), "+v"(n1r[0]));
+    __builtin_amdgcn_s_setprio(0);
+    HIFA4_WAIT_VMCNT(0);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    step(S0{}, kt, sa0, sa1, sb0, sb1);
+    if (kt + 1 >= n_tiles) break;
+    step(S1{}, kt + 1, sb0, sb1, sa0, sa1);
   }
 
   if (q < a.Sq) {

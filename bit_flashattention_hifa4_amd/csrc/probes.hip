@@ -211,6 +211,21 @@ __global__ __launch_bounds__(512) void coexec_kernel(float* out, int mode, int i
   out[blockIdx.x * 512 + threadIdx.x] = t;
 }
 
+// The gfx950 LDS transpose read of 16-bit elements (ds_read_b64_tr_b16):
+// LDS holds element i = i (as 16 bits) over 4096 elements; lane l reads at
+// element offset addr[l] (a multiple of 4) and returns 4 elements to
+// out[4l .. 4l+3].
+typedef short v4s_probe __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(64) void lds_read_tr16_kernel(const int* addr, short* out) {
+  __shared__ __attribute__((aligned(16))) short lds[4096];
+  for (int i = threadIdx.x; i < 4096; i += 64) lds[i] = (short)i;
+  __syncthreads();
+  typedef __attribute__((address_space(3))) v4s_probe* lp;
+  const lp p = (lp)((__attribute__((address_space(3))) short*)lds + addr[threadIdx.x]);
+  const v4s_probe r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+  for (int e = 0; e < 4; e++) out[threadIdx.x * 4 + e] = r[e];
+}
+
 // Memory -> LDS buffer loads (the LDS-destination form): one wave loads
 // `size`-byte elements, lane i from source byte offset size*i, with M0 = 64;
 // the LDS window is pre-filled with 0xEE and copied out afterwards, so the
@@ -376,6 +391,11 @@ int probe_coexec(float* out, int mode, int n_blocks, int iters, void* stream) {
   if (n_blocks <= 0 || iters <= 0 || mode < 0 || mode > 3) return -1;
   hipLaunchKernelGGL(coexec_kernel, dim3(n_blocks), dim3(512), 0, (hipStream_t)stream, out, mode,
                      iters);
+  return status(hipGetLastError());
+}
+
+int probe_lds_read_tr16(const int* addr, short* out, void* stream) {
+  hipLaunchKernelGGL(lds_read_tr16_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, addr, out);
   return status(hipGetLastError());
 }
 

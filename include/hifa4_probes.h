@@ -70,6 +70,12 @@ HIFA4_PROBE_API int probe_mfma16_rate(float* out, int n_blocks, int iters, void*
  * argument. */
 HIFA4_PROBE_API int probe_coexec(float* out, int mode, int n_blocks, int iters, void* stream);
 
+/* The LDS transpose read of 16-bit elements (ds_read_b64_tr_b16): LDS holds
+ * element i = i over 4096 16-bit elements; lane l (one wave) reads at element
+ * offset addr[l] (device, 64 ints, each a multiple of 4 and at most 4092) and
+ * writes its 4 results to out[4l .. 4l+3] (device, 256 shorts). */
+HIFA4_PROBE_API int probe_lds_read_tr16(const int* addr, short* out, void* stream);
+
 /* One wave of memory -> LDS buffer loads of `size` bytes per lane (1, 2, 4 or
  * 16), lane i reading src bytes [size*i, size*(i+1)) (src: 1024 bytes), with
  * M0 = LDS window + 64.  out: the 1088-byte window afterwards (pre-filled

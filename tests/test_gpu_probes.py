@@ -51,6 +51,7 @@ def lib():
     l.probe_mfma16_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_coexec.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_void_p]
+    l.probe_lds_read_tr16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     l.probe_lds_dma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_buffer_range.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p]
@@ -290,6 +291,40 @@ def test_issue_rates_report(lib):
           "SIMD" % (flops16 / t16 / 1e12, flops16 / t16 / 10.066e15 * 100,
                     t16 * 2.4e9 * 1024 / mfmas16))
     assert flops16 / t16 > 1e15
+
+
+@pytest.mark.parametrize("pattern", ["contiguous", "rows", "bf16_v_operand"])
+def test_lds_transpose_read_layout(lib, pattern):
+    """ds_read_b64_tr_b16, as the bf16 kernel's V operand read uses it: each group of
+    16 lanes reads the 16 x 4 matrix M[j] = the 4 elements at lane j's address and lane
+    L of the group receives M[4i + L // 4][L % 4] for i = 0..3."""
+    lanes = np.arange(64)
+    if pattern == "contiguous":
+        addr = 4 * lanes
+    elif pattern == "rows":
+        addr = 64 * lanes
+    else:
+        # the kernel's pattern for one channel tile: lane (group gq, 4 i + a) points at
+        # key 8 (gq // 2) + i, channels 16 (gq % 2) + 4 a of 64-channel rows
+        gq, jl = lanes // 16, lanes % 16
+        addr = 64 * (8 * (gq // 2) + jl // 4) + 16 * (gq % 2) + 4 * (jl % 4)
+    a = torch.tensor(addr, dtype=torch.int32, device="cuda")
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    assert lib.probe_lds_read_tr16(a.data_ptr(), out.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(64, 4)
+    want = np.zeros((64, 4), np.int64)
+    for lane in range(64):
+        g0, L = 16 * (lane // 16), lane % 16
+        for i in range(4):
+            want[lane, i] = addr[g0 + 4 * i + L // 4] + L % 4
+    assert np.array_equal(got.astype(np.int64), want), pattern
+    if pattern == "bf16_v_operand":
+        # lane (n, h) = lane 32 h + n gets channel n of keys 8h .. 8h + 3
+        for lane in range(64):
+            n, h = lane % 32, lane // 32
+            assert [v % 64 for v in got[lane]] == [n] * 4
+            assert [v // 64 for v in got[lane]] == [8 * h + i for i in range(4)]
 
 
 def test_mfma_and_vector_co_execution_report(lib):
