@@ -693,6 +693,10 @@ hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void
   hifa4_status st = check_params(p ? &pp : nullptr, &cap, &chunk);
   if (st != HIFA4_OK) return st;
   const int d = p->d;
+  // a head's bf16 K / V rows are addressed through 32-bit buffer ranges and offsets
+  if ((int64_t)cap * d * 2 >= ((int64_t)1 << 31))
+    return fail(HIFA4_ERR_UNSUPPORTED, "key capacity %d x d %d: a head's bf16 keys exceed 2^31 bytes",
+                cap, d);
   const int64_t rq = (int64_t)p->B * p->Hq * p->Sq;
   const int64_t rcap = (int64_t)p->B * p->Hkv * cap;
   if (rq == 0) return HIFA4_OK;

@@ -330,7 +330,8 @@ HIFA4_API hifa4_status hifa4_attn_fwd_qraw(const hifa4_attn_params* p, const voi
  * compare against (Abstract): bf16 MFMA products, fp32 softmax state, no
  * quantisation and no smoothing.  q [B][Hq][Sq][d], k / v [B][Hkv][kv_stride][d]
  * bf16 device; out bf16 [B][Hq][Sq][d]; lse as for hifa4_attn_fwd.
- * kv_lens must be NULL.
+ * kv_lens must be NULL.  One head's keys (kv_stride * d * 2 bytes) must stay
+ * below 2^31 bytes (HIFA4_ERR_UNSUPPORTED otherwise).
  */
 HIFA4_API hifa4_status bf16_attn_fwd(const hifa4_attn_params* p, const void* q, const void* k,
                            const void* v, void* out, float* lse, void* workspace,

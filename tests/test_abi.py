@@ -333,6 +333,11 @@ def test_bf16_path_rejects_bad_arguments(lib):
     assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x3000000, None,
                              None, 0, None) == hb.HIFA4_ERR_INVALID_ARGUMENT
     assert "normaliser" in hb.hifa4_last_error()
+    # bf16 keys of one head past 2^31 bytes (a capacity the 4-bit path still takes)
+    p = _params(Sk=1 << 22, d=256)
+    assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x3000000, None,
+                             None, 0, None) == hb.HIFA4_ERR_UNSUPPORTED
+    assert "2^31 bytes" in hb.hifa4_last_error()
     p = _params(scale_rule=1)
     assert lib.bf16_attn_fwd(ctypes.byref(p), A, A + 0x1000000, A + 0x2000000, A + 0x3000000, None,
                              None, 0, None) == hb.HIFA4_ERR_INVALID_ARGUMENT
