@@ -416,6 +416,11 @@ def test_decode_full_size_every_sequence_and_cache():
     (1, 4, 2, 200, 200, 128, True),
     (2, 2, 1, 130, 300, 64, False),
     (1, 4, 2, 257, 300, 256, True),
+    (1, 2, 2, 96, 40, 128, True),      # Sq > Sk: one partial tile, the first rows see no key
+    (1, 1, 1, 5, 1, 64, False),        # a single key
+    (2, 8, 2, 64, 64, 256, False),     # group of 4, one whole tile
+    (1, 4, 4, 300, 1000, 128, True),   # Sq < Sk: the causal diagonal offset by 700 keys
+    (1, 3, 1, 33, 161, 64, True),
 ])
 def test_bf16_baseline_matches_exact_attention(case, tau):
     B, Hq, Hkv, Sq, Sk, d, causal = case
@@ -430,6 +435,28 @@ def test_bf16_baseline_matches_exact_attention(case, tau):
     fin = np.isfinite(ref["lse"])
     lerr = np.abs(lse.cpu().numpy()[fin] - ref["lse"][fin]).max()
     print("bf16 %s: max|O - exact| = %.4g (bound %.4g), lse %.3g" % (case, err, BF16_TOL * vmax, lerr))
+    assert err <= BF16_TOL * vmax and lerr < 1e-2
+
+
+@pytest.mark.parametrize("cfg", [W.QWEN3_8B, W.GEMMA2_9B], ids=lambda c: c.name)
+def test_bf16_baseline_full_size_sampled_rows(cfg):
+    """The bf16 baseline at the benchmark's shapes and launch configuration, sampled rows
+    (including each head's first and last query) against exact fp64 attention."""
+    print("bf16 full-size:", cfg.name, flush=True)
+    inp = W.prefill_inputs(cfg)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    out, lse = hb.bf16_attn_fwd(q, k, v, causal=cfg.causal, rescale_threshold=FAST)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    del q, k, v, out
+    rows = _sample_rows(cfg.B, cfg.Hq, cfg.S, 192, seed=cfg.seed)
+    ref = oracle.attention(W.to_f32(inp["q"]), W.to_f32(inp["k"]), W.to_f32(inp["v"]),
+                           causal=cfg.causal, bc=64, quant_p=False, rows=rows)
+    vmax = np.abs(W.to_f32(inp["v"])).max()
+    err = np.abs(o.reshape(-1, cfg.d)[rows] - ref["o"]).max()
+    lerr = np.abs(l.reshape(-1)[rows] - ref["lse"]).max()
+    print("bf16 %s: sampled max|O - exact| = %.4g (bound %.4g), lse %.3g"
+          % (cfg.name, err, BF16_TOL * vmax, lerr))
     assert err <= BF16_TOL * vmax and lerr < 1e-2
 
 
