@@ -216,15 +216,21 @@ __device__ __forceinline__ void mask_scores(v16f& s0, v16f& s1, int kb, int lim)
   }
 }
 
-// Output rows: each half-wave holds 4 of every 8 consecutive channels of its
-// query's row; one lane swap per dword (lane n with lane n + 32) gives every
-// lane 8 consecutive channels of one group, stored as 16 bytes (8 stores per
-// 32 output channels' worth of 4 groups instead of 16 8-byte ones; measured
-// 4 % faster on a 4096-item launch, 0.7 % on the Qwen3 shape, same bits).
+// Output tile of a wave (rows row0 .. row0 + nrows - 1, nrows <= 32) through
+// LDS.  Each half-wave holds 4 of every 8 consecutive channels of its query's
+// row; one lane swap per dword (lane n with lane n + 32) gives every lane 8
+// consecutive channels of one group, written to the staging rows as 16 bytes.
+// The tile then goes to memory as whole rows: lane l stores 16 bytes of row
+// l / (D / 8) of each group of 512 / D rows, so a store instruction writes
+// 1 KB in full 128-byte lines instead of 32 bytes in each of 32 rows
+// (measured 2-3.6 % faster over the whole launch on the Gemma2-, Llama- and
+// Qwen3-shaped prefill layers, same bits).
 template <int NC, bool kHalf>
-__device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row, int h, const v16f (&acc)[NC],
-                                          float inv) {
+__device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row0, int nrows, int n,
+                                          int h, int lane, const v16f (&acc)[NC], float inv,
+                                          uint8_t* stage) {
   constexpr int D = NC * 32;
+  constexpr int STRIDE = 2 * D + 16;
   // two channels to one packed word with the hardware's round-to-nearest-even
   // converts (gfx950 packs two fp32 into bf16 / fp16 in one instruction)
   auto cvt2 = [&](float x, float y) -> uint32_t {
@@ -241,7 +247,7 @@ __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row, int h,
   for (int c = 0; c < NC; c++) {
 #pragma unroll
     for (int gp = 0; gp < 2; gp++) {
-      // groups ga (stored by the lower half-wave) and gb (upper): lane (n, h)
+      // groups ga (kept by the lower half-wave) and gb (upper): lane (n, h)
       // holds channels 8 g + 4 h .. + 3 of both
       const int ga = 2 * gp, gb = 2 * gp + 1;
       const uint32_t a0 = cvt2(acc[c][4 * ga] * inv, acc[c][4 * ga + 1] * inv);
@@ -252,9 +258,18 @@ __device__ __forceinline__ void write_out(const AttnArgs& a, int64_t row, int h,
       const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
       const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
       const int ch = 32 * c + 8 * (h ? gb : ga);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + row * D + ch) =
-          make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      *reinterpret_cast<uint4*>(stage + n * STRIDE + 2 * ch) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
     }
+  }
+  constexpr int LPR = D / 8;    // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR; // rows per store instruction
+  const int rr = lane / LPR, cb = (lane % LPR) * 16;
+  uint8_t* out = static_cast<uint8_t*>(a.out);
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; k++) {
+    const int r = k * RPI + rr;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + r * STRIDE + cb);
+    if (r < nrows) *reinterpret_cast<uint4*>(out + (row0 + r) * (2 * D) + cb) = v;
   }
 }
 
@@ -289,7 +304,7 @@ __device__ __forceinline__ v16f mfma_fp4_sel(const uint4& a, const uint4& b, con
 //
 // Staging.  K and V tiles go from memory straight into LDS (buffer loads
 // with the LDS destination: no registers, no LDS store instructions) through
-// rings of three buffers.  Step kt reads K tile kt+1 and V tile kt and issues
+// rings of four buffers.  Step kt reads K tile kt+1 and V tile kt and issues
 // the loads of K tile kt+3 and V tile kt+2 into the buffers the previous
 // step finished with; before its closing barrier it waits only for the loads
 // issued one step earlier (K tile kt+2, V tile kt+1), so every load has two
@@ -333,6 +348,18 @@ struct PrefillTile {
   static constexpr int VC_I = (VC_W + 63) / 64;
   static constexpr int N_LOADS = KC_I + VC_I + 2;  // per wave and step
   static constexpr int STAGES = 4;                 // ring depth (K and V)
+  // Output staging after the last step: a wave's 32 x D tile, rows padded by
+  // 16 bytes (row r starts 4 banks after row r - 1, so the 16-byte writes of
+  // 16 consecutive rows fall in distinct banks).  For d <= 128 each wave has
+  // a region of its own (two workgroups per CU still fit: 2 x 68 KB at
+  // d = 128), written and read by that wave alone; at d = 256 there is no
+  // room beside the rings, so after a workgroup barrier waves 0, 1 use the
+  // K ring and waves 2, 3 the V ring.
+  static constexpr int OUT_STRIDE = 2 * D + 16;
+  static constexpr int OUT_TILE = 32 * OUT_STRIDE;
+  static constexpr bool OUT_OWN = D <= 128;
+  static constexpr int K_RING = OUT_OWN || STAGES * K_BYTES >= 2 * OUT_TILE ? STAGES * K_BYTES : 2 * OUT_TILE;
+  static constexpr int V_RING = OUT_OWN || STAGES * V_BYTES >= 2 * OUT_TILE ? STAGES * V_BYTES : 2 * OUT_TILE;
   static_assert(N_LOADS < 16, "vmcnt encoding below assumes fewer than 16");
 };
 
@@ -526,39 +553,55 @@ constexpr bool prefill_two_phase() { return D == 256; }
 // convert), so the codes are bit-identical.  The scale byte of block 2j + h
 // goes to byte h + 2 (j % 2) of word j / 2, the quantise kernel's row layout
 // as the lane reads it.
-template <int D, bool kBf16, uint32_t kQBias>
+//
+// Every load (the lane's raw blocks and their smoothing factors) is issued
+// before the first one is used, so the section costs one memory round trip;
+// with the smoothing test inside the block loop, the compiler had split it
+// into four dependent ones (3.0 -> ~1 us per work item on the Qwen3-8B shape).
+template <int D, bool kBf16, bool kSmooth, uint32_t kQBias>
 __device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, int hs, int h,
                                                 uint4 (&qa)[D / 64],
                                                 uint32_t (&qsw_raw)[(D / 64 + 1) / 2]) {
   constexpr int NJ = D / 64;
-#pragma unroll
-  for (int j = 0; j < (NJ + 1) / 2; j++) qsw_raw[j] = 0;
   const uint16_t* src = a.q_raw + row * D;
-  const float* sm = a.smooth ? a.smooth + (int64_t)hs * D : nullptr;
+  const float* sm = a.smooth + (int64_t)hs * D;
+  uint4 raw[NJ][4];
 #pragma unroll
   for (int j = 0; j < NJ; j++) {
-    const int kb = 2 * j + h;  // 32-element block along d
-    const uint4* p = reinterpret_cast<const uint4*>(src + 32 * kb);
+    const uint4* p = reinterpret_cast<const uint4*>(src + 32 * (2 * j + h));
+#pragma unroll
+    for (int i = 0; i < 4; i++) raw[j][i] = p[i];
+  }
+  float4 sf[kSmooth ? NJ : 1][8];
+  if constexpr (kSmooth) {
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const float4* sp = reinterpret_cast<const float4*>(sm + 32 * (2 * j + h));
+#pragma unroll
+      for (int i = 0; i < 8; i++) sf[j][i] = sp[i];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < (NJ + 1) / 2; j++) qsw_raw[j] = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
     float v[32];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint4 w = p[i];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      const uint32_t ws[4] = {raw[j][i].x, raw[j][i].y, raw[j][i].z, raw[j][i].w};
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         v[8 * i + 2 * e] = elem<kBf16>(ws[e] & 0xFFFFu);
         v[8 * i + 2 * e + 1] = elem<kBf16>(ws[e] >> 16);
       }
     }
-    if (sm != nullptr) {
-      const float4* sp = reinterpret_cast<const float4*>(sm + 32 * kb);
+    if constexpr (kSmooth) {
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const float4 f = sp[i];
-        v[4 * i] = v[4 * i] * f.x;
-        v[4 * i + 1] = v[4 * i + 1] * f.y;
-        v[4 * i + 2] = v[4 * i + 2] * f.z;
-        v[4 * i + 3] = v[4 * i + 3] * f.w;
+        v[4 * i] = v[4 * i] * sf[j][i].x;
+        v[4 * i + 1] = v[4 * i + 1] * sf[j][i].y;
+        v[4 * i + 2] = v[4 * i + 2] * sf[j][i].z;
+        v[4 * i + 3] = v[4 * i + 3] * sf[j][i].w;
       }
     }
     float amax = 0.0f;
@@ -588,8 +631,8 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   constexpr int DB = T::DB, DS = T::DS;
   constexpr int NJ = D / 64;  // QK MFMAs per 32-key tile
   constexpr int NC = D / 32;  // P V channel tiles
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[T::STAGES * T::K_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[T::STAGES * T::V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[T::K_RING];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[T::V_RING];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -658,12 +701,19 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   uint32_t qsw_raw[(NJ + 1) / 2];
   if (q < a.Sq && a.q_raw) {
     // Q from the activations: smoothed and quantised here
-    if (a.q_raw_bf16)
-      quantise_q_lane<D, true, kQNoClip ? kScaleBiasNoClip : kScaleBiasOcp>(a, bhq * a.Sq + q, g,
-                                                                           h, qa, qsw_raw);
-    else
-      quantise_q_lane<D, false, kQNoClip ? kScaleBiasNoClip : kScaleBiasOcp>(a, bhq * a.Sq + q, g,
-                                                                            h, qa, qsw_raw);
+    constexpr uint32_t kQB = kQNoClip ? kScaleBiasNoClip : kScaleBiasOcp;
+    const int64_t qrow = bhq * a.Sq + q;
+    if (a.q_raw_bf16) {
+      if (a.smooth)
+        quantise_q_lane<D, true, true, kQB>(a, qrow, g, h, qa, qsw_raw);
+      else
+        quantise_q_lane<D, true, false, kQB>(a, qrow, g, h, qa, qsw_raw);
+    } else {
+      if (a.smooth)
+        quantise_q_lane<D, false, true, kQB>(a, qrow, g, h, qa, qsw_raw);
+      else
+        quantise_q_lane<D, false, false, kQB>(a, qrow, g, h, qa, qsw_raw);
+    }
   } else if (q < a.Sq) {
     const uint8_t* qc = a.q_codes + (bhq * a.Sq + q) * DB;
     const uint8_t* qsc = a.q_scales + (bhq * a.Sq + q) * DS;
@@ -910,6 +960,13 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   } else {
     (void)step2;
     for (int kt = 0; kt < n_tiles; kt += 4) {
+      // The loop header is 64-byte aligned (build flags); three 4-byte nops
+      // put the body at byte 12 of its line.  Measured over the 16 positions
+      // 0, 4, .., 60 (Qwen3-8B / Llama-3.1-8B-shaped layers at d = 128): bodies
+      // starting at 12 mod 16 ran at 69-71 / 163-165 us, at 0 mod 16 at
+      // 75-82 / 167-170 us, for the same instructions.  The d = 256 loop
+      // showed no such dependence (209-212 us over all 16 positions).
+      asm volatile("s_nop 0\n\ts_nop 0\n\ts_nop 0");
       step(R0{}, kt, sa0, sa1, sb0, sb1);
       if (kt + 1 >= n_tiles) break;
       step(R1{}, kt + 1, sb0, sb1, sa0, sa1);
@@ -925,8 +982,11 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
       pv_mfma(vo, pend_p, pend_s);
     }
   }
-  // No load may still be writing this workgroup's LDS when it exits.
+  // No load may still be writing this workgroup's LDS when it exits; at
+  // d = 256 the rings take the output tiles once every wave is past its last
+  // ring read.
   HIFA4_WAIT_VMCNT(0);
+  if constexpr (!T::OUT_OWN) __syncthreads();
 
   // Wave priority 2 for the epilogue: a finishing item frees its slot sooner when
   // the other workgroup on the SIMD is in its priority-1 product block (measured:
@@ -934,16 +994,28 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   __builtin_amdgcn_s_setprio(2);
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
   const float lsum = kDirect ? l_direct : __shfl(prefill_two_phase<D>() ? l2 : accl[0], n);
-  if (q < a.Sq) {
-    const int64_t row = bhq * a.Sq + q;
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  // rows of this wave inside the sequence; the lane's row is row0 + n (written
+  // without q, which would otherwise stay live across the loop and spill at
+  // d = 256)
+  const int nrows = min(32, a.Sq - q_wave0);
+  const int64_t row0 = bhq * a.Sq + q_wave0;
+  if (nrows > 0) {
+    const float inv = n < nrows && lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    uint8_t* stage;
+    if constexpr (T::OUT_OWN) {
+      __shared__ __attribute__((aligned(16))) uint8_t lds_o[4 * T::OUT_TILE];
+      stage = lds_o + w * T::OUT_TILE;
+    } else {
+      stage = (w < 2 ? lds_k : lds_v) + (w & 1) * T::OUT_TILE;
+    }
     // the output type is chosen once per wave, not per element
     if (a.out_fp16)
-      write_out<NC, true>(a, row, h, acc, inv);
+      write_out<NC, true>(a, row0, nrows, n, h, lane, acc, inv, stage);
     else
-      write_out<NC, false>(a, row, h, acc, inv);
-    if (a.lse && h == 0) a.lse[row] = lsum > 0.0f ? m_run * kLn2 + logf(lsum) : -INFINITY;
+      write_out<NC, false>(a, row0, nrows, n, h, lane, acc, inv, stage);
   }
+  if (n < nrows && a.lse && h == 0)
+    a.lse[row0 + n] = lsum > 0.0f ? m_run * kLn2 + logf(lsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
