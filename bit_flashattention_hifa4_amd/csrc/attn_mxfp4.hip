@@ -557,7 +557,8 @@ constexpr bool prefill_two_phase() { return D == 256; }
 // Every load (the lane's raw blocks and their smoothing factors) is issued
 // before the first one is used, so the section costs one memory round trip;
 // with the smoothing test inside the block loop, the compiler had split it
-// into four dependent ones (3.0 -> ~1 us per work item on the Qwen3-8B shape).
+// into four dependent ones (3.0 -> ~2 us per work item on the Qwen3-8B shape).
+// Used for d <= 128; d = 256 reads the rows as whole runs (below).
 template <int D, bool kBf16, bool kSmooth, uint32_t kQBias>
 __device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, int hs, int h,
                                                 uint4 (&qa)[D / 64],
@@ -621,6 +622,105 @@ __device__ __forceinline__ void quantise_q_lane(const AttnArgs& a, int64_t row, 
   }
 }
 
+// Q from the bf16 / fp16 activations, smoothed (Q * s in fp32) and quantised
+// to MXFP4 in the prologue, with the quantise kernel's arithmetic and lane
+// decomposition (products, exact block max, E8M0 exponent, packed convert), so
+// the codes are bit-identical to quantise-then-attend.
+//
+// A wave's 32 rows are contiguous in memory and are read as whole 1 KB runs:
+// lane l holds bytes 16 l .. 16 l + 15 of each run, 8 elements whose channel
+// offset 8 l mod d is the same in every run, so the lane loads its 8 smoothing
+// factors once.  Four consecutive lanes hold a 32-element block: two quad
+// swaps give the block max, and each lane encodes its 8 elements to 4 code
+// bytes.  Codes and scale bytes go to a per-wave staging area in LDS in the
+// row layout of the quantised tensors, from which each lane reads its MFMA
+// operand (row n, blocks 2j + h) and scale words as the codes path reads
+// them from memory.  Used at d = 256, where the per-lane form (each lane
+// loading its own blocks' 64-byte pieces and 32 smoothing factors per block)
+// spent ~6 us per work item in this section; the whole launch on the
+// Gemma2-9B-shaped layer: 212.5 -> 207.1 us.  At d = 128 the LDS round trip
+// costs more than the coalescing saves (Llama-3.1-8B-shaped layer 164.8 ->
+// 170.1 us), so d <= 128 keeps the per-lane form.
+template <int D>
+struct QRaw {
+  static constexpr int NI = D / 16;           // 1 KB runs in a wave's 32 rows
+  static constexpr int RPI = 512 / D;         // rows per run
+  static constexpr int DBQ = D / 2;           // code bytes per row
+  static constexpr int SSQ = D / 32 < 4 ? 4 : D / 32;  // staged scale bytes per row
+  static constexpr int STAGE = 32 * (DBQ + SSQ);       // staging bytes per wave
+  uint4 raw[NI];
+  float4 f0, f1;
+};
+
+template <int D>
+__device__ __forceinline__ void q_raw_load(const AttnArgs& a, int64_t row0, int nrows, int hs,
+                                           int lane, QRaw<D>& qr) {
+  using R = QRaw<D>;
+  // the factors first: the first run's products then wait only for it
+  if (a.smooth) {
+    const float4* sp = reinterpret_cast<const float4*>(a.smooth + (int64_t)hs * D + (8 * lane) % D);
+    qr.f0 = sp[0];
+    qr.f1 = sp[1];
+  }
+  // rows past the sequence read its last row (no branch between the loads)
+  // and are zeroed in q_raw_quantise
+  const uint4* src = reinterpret_cast<const uint4*>(a.q_raw + row0 * D) + (8 * lane) % D / 8;
+  const int rl = (8 * lane) / D;  // the lane's row within a run
+#pragma unroll
+  for (int k = 0; k < R::NI; k++) qr.raw[k] = src[min(k * R::RPI + rl, nrows - 1) * (D / 8)];
+}
+
+__device__ __forceinline__ float quad_max(float x) {
+  // lanes 1,0,3,2 then 2,3,0,1 of each quad (DPP quad_perm)
+  x = fmaxf(x, __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(x, __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x4E, 0xF, 0xF, false)));
+}
+
+template <int D, bool kBf16, bool kSmooth, uint32_t kQBias>
+__device__ __forceinline__ void q_raw_quantise(const QRaw<D>& qr, int nrows, int lane, int n, int h,
+                                               uint8_t* stg, uint4 (&qa)[D / 64],
+                                               uint32_t (&qsw_raw)[(D / 64 + 1) / 2]) {
+  using R = QRaw<D>;
+  constexpr int NJ = D / 64;
+  uint8_t* sc = stg + 32 * R::DBQ;  // scale rows after the code rows
+  const int j0 = (8 * lane) % D, rl = (8 * lane) / D;
+  const float ff[8] = {qr.f0.x, qr.f0.y, qr.f0.z, qr.f0.w, qr.f1.x, qr.f1.y, qr.f1.z, qr.f1.w};
+#pragma unroll
+  for (int k = 0; k < R::NI; k++) {
+    const int r = k * R::RPI + rl;
+    const bool in = r < nrows;
+    const uint32_t ws[4] = {in ? qr.raw[k].x : 0u, in ? qr.raw[k].y : 0u, in ? qr.raw[k].z : 0u,
+                            in ? qr.raw[k].w : 0u};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = elem<kBf16>(ws[i] & 0xFFFFu);
+      v[2 * i + 1] = elem<kBf16>(ws[i] >> 16);
+    }
+    if constexpr (kSmooth) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = v[i] * ff[i];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(v[i]));
+    amax = quad_max(amax);
+    const uint32_t sb = e8m0_from_amax(amax, kQBias);
+    *reinterpret_cast<uint32_t*>(stg + r * R::DBQ + j0 / 2) = encode8(v, e8m0_to_float(sb));
+    if ((lane & 3) == 0) sc[r * R::SSQ + j0 / 32] = (uint8_t)sb;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; j++)
+    qa[j] = *reinterpret_cast<const uint4*>(stg + n * R::DBQ + (2 * j + h) * 16);
+#pragma unroll
+  for (int j = 0; j < NJ; j += 2) {
+    if constexpr (D == 64)  // two scale bytes per row, as the codes path reads them
+      qsw_raw[j / 2] = *reinterpret_cast<const uint16_t*>(sc + n * R::SSQ);
+    else
+      qsw_raw[j / 2] = reinterpret_cast<const uint32_t*>(sc + n * R::SSQ)[j >> 1];
+  }
+}
+
 // kQNoClip: the block-scale rule of Q quantised in the prologue, a template
 // parameter rather than a kernel argument (reading the rule there at run time
 // cost about 3% of the whole kernel's time on the Qwen3-8B-shaped layer).
@@ -680,6 +780,13 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // state).  They are issued back to back, so waiting for all of them (and
   // the Q operand) costs little over waiting for K0, V0, K1, and it tells
   // the compiler that no load it knows of is still in flight in the loop.
+  // At d = 256, Q rows from the activations are requested first (their
+  // quantisation then overlaps the tile loads).
+  constexpr bool kQWave = D == 256;
+  const bool q_from_raw = a.q_raw != nullptr && q_wave0 < a.Sq;  // uniform
+  const int q_nrows = min(32, a.Sq - q_wave0);
+  QRaw<D> qr;
+  if (kQWave && q_from_raw) q_raw_load<D>(a, bhq * a.Sq + q_wave0, q_nrows, g, lane, qr);
   const TileLanes<D> tl = tile_lanes<D>(w, lane);
   const HeadDescs hd = head_descs<D>(a, bkv, L, nblk_valid, nblk_cap);
   const WaveDst wd = wave_dst<D>(lds_addr(lds_k), lds_addr(lds_v), w);
@@ -699,8 +806,25 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // here, shifted for the lane's half once the loads have landed).
   uint4 qa[NJ];
   uint32_t qsw_raw[(NJ + 1) / 2];
-  if (q < a.Sq && a.q_raw) {
-    // Q from the activations: smoothed and quantised here
+  if (kQWave && q_from_raw) {
+    // staging: K stage 3 (waves 0, 1) and V stage 2 (waves 2, 3), which no
+    // load writes before the first step
+    static_assert(2 * QRaw<D>::STAGE <= T::K_BYTES, "Q staging: K stage 3");
+    static_assert(2 * QRaw<D>::STAGE <= T::V_BYTES + T::VS_OFF, "Q staging: V stage 2");
+    uint8_t* stg = (w < 2 ? lds_k + 3 * T::K_BYTES : lds_v + 2 * T::V_BYTES) + (w & 1) * QRaw<D>::STAGE;
+    constexpr uint32_t kQB = kQNoClip ? kScaleBiasNoClip : kScaleBiasOcp;
+    if (a.q_raw_bf16) {
+      if (a.smooth)
+        q_raw_quantise<D, true, true, kQB>(qr, q_nrows, lane, n, h, stg, qa, qsw_raw);
+      else
+        q_raw_quantise<D, true, false, kQB>(qr, q_nrows, lane, n, h, stg, qa, qsw_raw);
+    } else {
+      if (a.smooth)
+        q_raw_quantise<D, false, true, kQB>(qr, q_nrows, lane, n, h, stg, qa, qsw_raw);
+      else
+        q_raw_quantise<D, false, false, kQB>(qr, q_nrows, lane, n, h, stg, qa, qsw_raw);
+    }
+  } else if (!kQWave && q < a.Sq && a.q_raw) {
     constexpr uint32_t kQB = kQNoClip ? kScaleBiasNoClip : kScaleBiasOcp;
     const int64_t qrow = bhq * a.Sq + q;
     if (a.q_raw_bf16) {
