@@ -154,6 +154,62 @@ __global__ __launch_bounds__(256) void mfma16_rate_kernel(float* out, int iters)
   out[blockIdx.x * blockDim.x + l] = t;
 }
 
+// Issue cost of vector instructions, two waves per SIMD, 8 independent chains
+// per wave, 32 instructions per wave and iteration (modes as in the header).
+template <int MODE>
+__global__ __launch_bounds__(512) void valu_rate_kernel(float* out, int iters) {
+  const int w = threadIdx.x >> 6;
+  float x[8], y[8];
+  uint32_t pk[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    x[j] = 0.001f * (threadIdx.x + j) - 0.5f;
+    y[j] = 0.3f + 0.01f * j;
+    pk[j] = 0;
+  }
+  auto fma1 = [](float v) { return __builtin_fmaf(v, 0.999f, -0.001f); };
+  auto cvt1 = [](uint32_t p, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, a, b, 1.0f, 0);
+  };
+  if constexpr (MODE == 6) {
+    if (w < 4) {
+      for (int it = 0; it < iters; it++)
+#pragma unroll
+        for (int r = 0; r < 32; r++) x[r & 7] = __builtin_amdgcn_exp2f(x[r & 7]);
+    } else {
+      for (int it = 0; it < iters; it++)
+#pragma unroll
+        for (int r = 0; r < 32; r++) x[r & 7] = fma1(x[r & 7]);
+    }
+  } else {
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int r = 0; r < 32; r++) {
+        const int j = r & 7;
+        const bool odd = r & 1;
+        if constexpr (MODE == 0) x[j] = fma1(x[j]);
+        if constexpr (MODE == 1) x[j] = __builtin_amdgcn_exp2f(x[j]);
+        if constexpr (MODE == 2) x[j] = odd ? __builtin_amdgcn_exp2f(x[j]) : fma1(x[j]);
+        if constexpr (MODE == 3) {
+          if (odd) pk[j] = cvt1(pk[j], x[j], y[j]);
+          else x[j] = fma1(x[j]);
+        }
+        if constexpr (MODE == 4)
+          x[j] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[j], y[j]),
+                                               x[(j + 1) & 7]);
+        if constexpr (MODE == 5) {
+          if (odd) pk[j] = cvt1(pk[j], x[j], y[j]);
+          else x[j] = __builtin_amdgcn_exp2f(x[j]);
+        }
+      }
+    }
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) t += x[j] + (float)pk[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = t;
+}
+
 // Co-execution of the matrix core and the vector ALU: 512-thread blocks (two
 // waves per SIMD), per iteration 16 FP4 32x32x64 MFMAs (four independent
 // chains) and 32 exp2(fma) pairs (eight independent chains).  mode 0: MFMAs
@@ -391,6 +447,23 @@ int probe_coexec(float* out, int mode, int n_blocks, int iters, void* stream) {
   if (n_blocks <= 0 || iters <= 0 || mode < 0 || mode > 3) return -1;
   hipLaunchKernelGGL(coexec_kernel, dim3(n_blocks), dim3(512), 0, (hipStream_t)stream, out, mode,
                      iters);
+  return status(hipGetLastError());
+}
+
+int probe_valu_rate(float* out, int mode, int n_blocks, int iters, void* stream) {
+  if (n_blocks <= 0 || iters <= 0) return -1;
+  const dim3 g(n_blocks), b(512);
+  hipStream_t st = (hipStream_t)stream;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(valu_rate_kernel<0>, g, b, 0, st, out, iters); break;
+    case 1: hipLaunchKernelGGL(valu_rate_kernel<1>, g, b, 0, st, out, iters); break;
+    case 2: hipLaunchKernelGGL(valu_rate_kernel<2>, g, b, 0, st, out, iters); break;
+    case 3: hipLaunchKernelGGL(valu_rate_kernel<3>, g, b, 0, st, out, iters); break;
+    case 4: hipLaunchKernelGGL(valu_rate_kernel<4>, g, b, 0, st, out, iters); break;
+    case 5: hipLaunchKernelGGL(valu_rate_kernel<5>, g, b, 0, st, out, iters); break;
+    case 6: hipLaunchKernelGGL(valu_rate_kernel<6>, g, b, 0, st, out, iters); break;
+    default: return -1;
+  }
   return status(hipGetLastError());
 }
 

@@ -70,6 +70,15 @@ HIFA4_PROBE_API int probe_mfma16_rate(float* out, int n_blocks, int iters, void*
  * argument. */
 HIFA4_PROBE_API int probe_coexec(float* out, int mode, int n_blocks, int iters, void* stream);
 
+/* Issue cost of the softmax step's vector instructions: n_blocks x 512 threads
+ * (two waves per SIMD), each wave runs iters iterations of 32 instructions on 8
+ * independent chains.  mode 0: fma; 1: v_exp_f32; 2: exp and fma alternating;
+ * 3: the 2-value FP4 convert (v_cvt_scalef32_pk_fp4_f32) and fma alternating;
+ * 4: v_maximum3_f32; 5: convert and exp alternating; 6: waves 0-3 exp only,
+ * waves 4-7 fma only (one wave of each kind per SIMD).  out: [n_blocks * 512]
+ * floats (keeps the work alive).  Returns -1 on a bad argument. */
+HIFA4_PROBE_API int probe_valu_rate(float* out, int mode, int n_blocks, int iters, void* stream);
+
 /* The LDS transpose read of 16-bit elements (ds_read_b64_tr_b16): LDS holds
  * element i = i over 4096 16-bit elements; lane l (one wave) reads at element
  * offset addr[l] (device, 64 ints, each a multiple of 4 and at most 4092) and

@@ -51,6 +51,8 @@ def lib():
     l.probe_mfma16_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     l.probe_coexec.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_void_p]
+    l.probe_valu_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
     l.probe_lds_read_tr16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     l.probe_lds_dma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     l.probe_buffer_range.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
@@ -348,6 +350,31 @@ def test_mfma_and_vector_co_execution_report(lib):
     print("one of each kind: %.0f cycles against %.0f for the slower kind alone"
           % (cyc[3], max(cyc[0], cyc[1]) / 2))
     assert cyc[3] < one * 1.2
+
+
+def test_vector_issue_cost_report(lib):
+    """SIMD cycles per wave64 instruction of the softmax step's vector work (two waves
+    per SIMD, 8 independent chains each).  The exponential and the FP4 convert take
+    several fma slots, and pairing an exponential with an fma costs their sum whether
+    both are in each wave or one wave issues each kind: the transcendental does not run
+    beside the other vector work."""
+    n_blocks, iters = 256, 4000
+    out = torch.zeros(n_blocks * 512, device="cuda")
+    names = {0: "fma", 1: "v_exp_f32", 2: "exp / fma alternating", 3: "FP4 convert / fma alternating",
+             4: "v_maximum3_f32", 5: "FP4 convert / exp alternating",
+             6: "exp-only wave beside fma-only wave"}
+    cyc = {}
+    for mode, name in names.items():
+        t = _time(lambda: lib.probe_valu_rate(out.data_ptr(), mode, n_blocks, iters, _stream()))
+        # 1024 SIMDs, two waves each, 32 instructions per wave and iteration
+        cyc[mode] = t * 2.4e9 / iters / 64
+        print("vector issue cost, %s: %.2f SIMD cycles per instruction" % (name, cyc[mode]))
+    assert lib.probe_valu_rate(out.data_ptr(), 7, n_blocks, iters, _stream()) == -1
+    cvt = 2 * cyc[3] - cyc[0]
+    print("derived: FP4 convert %.2f, exp / fma ratio %.2f" % (cvt, cyc[1] / cyc[0]))
+    assert cyc[1] > 2 * cyc[0] and cvt > 2 * cyc[0]
+    # no overlap of the exponential with fma: the pair costs about the sum
+    assert cyc[2] > 0.85 * (cyc[0] + cyc[1]) / 2 and cyc[6] > 0.85 * (cyc[0] + cyc[1]) / 2
 
 
 @pytest.mark.parametrize("size", [1, 2, 4, 16])
