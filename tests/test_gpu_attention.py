@@ -460,7 +460,16 @@ def test_bf16_baseline_full_size_sampled_rows(cfg):
     assert err <= BF16_TOL * vmax and lerr < 1e-2
 
 
-@pytest.mark.parametrize("case", SMALL + [(1, 32, 8, 640, 640, 128, True, "bf16", True, 0)],
+# d = 256 reads Q rows as whole runs (another code path): fp16 / bf16, with and without
+# smoothing, a partial last wave (77 rows: 13 in the third wave, none in the fourth)
+QRAW_D256 = [
+    (1, 4, 2, 77, 300, 256, False, "fp16", False, 0),
+    (2, 2, 1, 40, 40, 256, True, "bf16", False, 0),
+    (1, 2, 1, 64, 128, 256, True, "fp16", True, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL + QRAW_D256 + [(1, 32, 8, 640, 640, 128, True, "bf16", True, 0)],
                          ids=lambda c: "x".join(str(v) for v in c))
 def test_prefill_with_q_from_activations_is_bit_identical(case):
     """hifa4_attn_fwd_qraw quantises Q inside the kernel with the arithmetic of
