@@ -136,6 +136,7 @@ SMALL = [
     (1, 3, 1, 33, 161, 64, True, "fp16", True, 0),
     (2, 4, 4, 64, 64, 128, False, "bf16", True, 0),
     (1, 1, 1, 5, 1, 128, False, "bf16", False, 0),
+    (1, 2, 1, 70, 90, 128, False, "fp16", True, 0),   # fp16 output through the staged epilogue
 ]
 
 
