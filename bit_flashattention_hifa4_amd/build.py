@@ -41,12 +41,13 @@ def flags() -> list[str]:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # IEEE fp32 division (the key smoothing divides)
         "-fhip-fp32-correctly-rounded-divide-sqrt",
-        # Code placement.  The d = 128 prefill loop's speed depends on where its
-        # instructions sit relative to 16-byte boundaries (69 to 82 us on the
-        # Qwen3-8B-shaped layer for the same instructions).  Branch targets that
-        # are never fallen into start on a 16-byte boundary, and every loop
-        # header on a 64-byte one; the loop itself then places its body (see
-        # the prefill kernel), independent of the code before it.
+        # Code placement.  The interleaved prefill step's loop ran at speeds
+        # that depended on where its instructions sat relative to 16-byte
+        # boundaries (69 to 82 us on a Qwen3-8B-shaped d = 128 layer for the
+        # same instructions).  Branch targets that are never fallen into start
+        # on a 16-byte boundary, and every loop header on a 64-byte one; the
+        # loop itself then places its body (see the prefill kernel),
+        # independent of the code before it.
         "-mllvm", "-align-all-nofallthru-blocks=4",
         "-falign-loops=64",
         "-Wall", "-Wno-unused-function",

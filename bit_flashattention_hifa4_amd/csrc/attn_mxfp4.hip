@@ -350,14 +350,14 @@ struct PrefillTile {
   static constexpr int STAGES = 4;                 // ring depth (K and V)
   // Output staging after the last step: a wave's 32 x D tile, rows padded by
   // 16 bytes (row r starts 4 banks after row r - 1, so the 16-byte writes of
-  // 16 consecutive rows fall in distinct banks).  For d <= 128 each wave has
-  // a region of its own (two workgroups per CU still fit: 2 x 68 KB at
-  // d = 128), written and read by that wave alone; at d = 256 there is no
-  // room beside the rings, so after a workgroup barrier waves 0, 1 use the
-  // K ring and waves 2, 3 the V ring.
+  // 16 consecutive rows fall in distinct banks).  At d = 64 each wave has a
+  // region of its own, written and read by that wave alone; at d = 128 (three
+  // workgroups per CU) and d = 256 there is no room beside the rings, so
+  // after a workgroup barrier waves 0, 1 use the K ring and waves 2, 3 the V
+  // ring.
   static constexpr int OUT_STRIDE = 2 * D + 16;
   static constexpr int OUT_TILE = 32 * OUT_STRIDE;
-  static constexpr bool OUT_OWN = D <= 128;
+  static constexpr bool OUT_OWN = D <= 64;
   static constexpr int K_RING = OUT_OWN || STAGES * K_BYTES >= 2 * OUT_TILE ? STAGES * K_BYTES : 2 * OUT_TILE;
   static constexpr int V_RING = OUT_OWN || STAGES * V_BYTES >= 2 * OUT_TILE ? STAGES * V_BYTES : 2 * OUT_TILE;
   static_assert(N_LOADS < 16, "vmcnt encoding below assumes fewer than 16");
@@ -533,19 +533,22 @@ __device__ __forceinline__ void v_load(const uint8_t* vbuf, int n, int h, VOps<D
   }
 }
 
-// Two workgroups (eight waves) per compute unit, two waves per SIMD, for every
-// head dim: d = 256 fits by running its step as two phases (below), so that
-// its 32 x 256 accumulator tile can sit in the accumulation registers.
+// Workgroups per compute unit (= waves per SIMD): three at d = 128 (158
+// VGPRs, 34 KB of LDS each), two at d = 64 and d = 256 (the 32 x 256
+// accumulator tile alone is 128 registers a lane).
 template <int D>
-constexpr int prefill_min_blocks() { return 2; }
+constexpr int prefill_min_blocks() { return D == 128 ? 3 : 2; }
 
-// d = 256 runs the step in two phases, softmax then products, instead of
-// interleaving the next tile's Q K^T with the current softmax in one wave:
-// one S tile per wave instead of two, operands read from LDS just before their
-// MFMA.  The two waves sharing a SIMD take turns, one in its softmax while the
-// other keeps the matrix core busy.
+// d = 128 and d = 256 run the step in two phases, softmax then products,
+// instead of interleaving the next tile's Q K^T with the current softmax in
+// one wave: one S tile per wave instead of two, operands read from LDS just
+// before their MFMA.  The waves sharing a SIMD take turns, one in its softmax
+// while another keeps the matrix core busy.  At d = 256 this is what lets two
+// waves fit a SIMD; at d = 128 it lets three fit (the interleaved step needs
+// 221 registers): Llama-3.1-8B-shaped layer 163.0 -> 148.2 us, Qwen3-8B 71.4
+// -> 70.4.  d = 64 keeps the interleaved step.
 template <int D>
-constexpr bool prefill_two_phase() { return D == 256; }
+constexpr bool prefill_two_phase() { return D >= 128; }
 
 // Smooth-QK (Q * s in fp32) and MXFP4 of the lane's blocks 2j + h (j < D/64)
 // of query row `row`, from the bf16 / fp16 activations: the same arithmetic as
@@ -1085,11 +1088,12 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     (void)step2;
     for (int kt = 0; kt < n_tiles; kt += 4) {
       // The loop header is 64-byte aligned (build flags); three 4-byte nops
-      // put the body at byte 12 of its line.  Measured over the 16 positions
-      // 0, 4, .., 60 (Qwen3-8B / Llama-3.1-8B-shaped layers at d = 128): bodies
-      // starting at 12 mod 16 ran at 69-71 / 163-165 us, at 0 mod 16 at
-      // 75-82 / 167-170 us, for the same instructions.  The d = 256 loop
-      // showed no such dependence (209-212 us over all 16 positions).
+      // put the body at byte 12 of its line.  This step's speed depended on
+      // that position when d = 128 still ran it (16 positions 0, 4, .., 60 on
+      // the Qwen3-8B / Llama-3.1-8B-shaped layers: bodies starting at 12 mod 16
+      // ran at 69-71 / 163-165 us, at 0 mod 16 at 75-82 / 167-170 us, for the
+      // same instructions); the two-phase loop showed no such dependence at
+      // d = 256 (209-212 us over all 16 positions).
       asm volatile("s_nop 0\n\ts_nop 0\n\ts_nop 0");
       step(R0{}, kt, sa0, sa1, sb0, sb1);
       if (kt + 1 >= n_tiles) break;
