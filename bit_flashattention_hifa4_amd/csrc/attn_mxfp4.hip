@@ -1128,14 +1128,20 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // 1.4 % faster on the Qwen3-8B shape, 0.2-0.4 % on the Llama and Gemma2 shapes).
   __builtin_amdgcn_s_setprio(2);
   // ---- epilogue: O = acc / l, LSE = m ln2 + ln l
-  const float lsum = kDirect ? l_direct : __shfl(prefill_two_phase<D>() ? l2 : accl[0], n);
+  // The lane index again, from the lane-count instruction rather than from
+  // threadIdx: the thread id would otherwise stay live across the loop only for
+  // these uses, and at d = 256 it was the one register spilled (a 4-byte store
+  // per lane, 2 MiB of the Gemma2-shaped launch's writes).
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int n_e = lane_e & 31, h_e = lane_e >> 5;
+  const float lsum = kDirect ? l_direct : __shfl(prefill_two_phase<D>() ? l2 : accl[0], n_e);
   // rows of this wave inside the sequence; the lane's row is row0 + n (written
   // without q, which would otherwise stay live across the loop and spill at
   // d = 256)
   const int nrows = min(32, a.Sq - q_wave0);
   const int64_t row0 = bhq * a.Sq + q_wave0;
   if (nrows > 0) {
-    const float inv = n < nrows && lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    const float inv = n_e < nrows && lsum > 0.0f ? 1.0f / lsum : 0.0f;
     uint8_t* stage;
     if constexpr (T::OUT_OWN) {
       __shared__ __attribute__((aligned(16))) uint8_t lds_o[4 * T::OUT_TILE];
@@ -1145,12 +1151,12 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     }
     // the output type is chosen once per wave, not per element
     if (a.out_fp16)
-      write_out<NC, true>(a, row0, nrows, n, h, lane, acc, inv, stage);
+      write_out<NC, true>(a, row0, nrows, n_e, h_e, lane_e, acc, inv, stage);
     else
-      write_out<NC, false>(a, row0, nrows, n, h, lane, acc, inv, stage);
+      write_out<NC, false>(a, row0, nrows, n_e, h_e, lane_e, acc, inv, stage);
   }
-  if (n < nrows && a.lse && h == 0)
-    a.lse[row0 + n] = lsum > 0.0f ? m_run * kLn2 + logf(lsum) : -INFINITY;
+  if (n_e < nrows && a.lse && h_e == 0)
+    a.lse[row0 + n_e] = lsum > 0.0f ? m_run * kLn2 + logf(lsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
