@@ -45,11 +45,15 @@ constexpr int kThreads = 256;
 
 // Row blocks (blocks of 32 along the head dim): four lanes share a block,
 // lane `lane4` handling elements 8*lane4 .. 8*lane4+7.  A lane may process
-// kRowParts blocks, kThreads parts apart, with every load issued before any
-// use.  One part per lane is fastest: the launch is a single round of
-// workgroups, and more, shorter workgroups finish it sooner (K, V of the
-// Qwen3-8B layer: 6.7 us with 1 part, 7.0 with 2, 7.5 with 4, 9.0 with 8).
-constexpr int kRowParts = 1;
+// kRowParts blocks, kThreads parts apart (the same 8 channels of rows that
+// far apart), with every load issued before any use.  Without smoothing one
+// part per lane was fastest (K, V of the Qwen3-8B layer: 6.7 us with 1 part,
+// 7.0 with 2, 7.5 with 4, 9.0 with 8: more, shorter workgroups finish a single
+// round sooner).  Since K / s goes through a per-workgroup table of double
+// reciprocals, two parts halve the table builds per element: K, V of the
+// Gemma2-9B-shaped layer between attention launches 43.7 -> 37.8 us (4 parts:
+// 38.0), the Qwen3- and Llama-shaped layers unchanged within noise.
+constexpr int kRowParts = 2;
 
 struct RowPart {
   uint32_t orow;  // output row (b, h, t) with the token capacity applied
