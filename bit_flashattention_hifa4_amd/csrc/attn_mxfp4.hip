@@ -130,8 +130,15 @@ struct SoftmaxMax {
   float m_use;  // the frame P is taken in (0 while the row has seen no key)
   float bmc;    // fl(block max of S * c)
   float alpha;  // rescale factor of the accumulators
+  bool moved;   // kLazyAlpha: some row of the wave moved its frame (uniform)
 };
 
+// kLazyAlpha: alpha = 1 without its exponential unless some row of the wave
+// moved its frame (a uniform branch; with the lazy threshold most steps move
+// none).  Where it is computed it is the same exp2(m_run - m_use); a row that
+// has seen no key keeps alpha = 1 instead of 0, which scales its still-zero
+// accumulators the same way.
+template <bool kLazyAlpha = false>
 __device__ __forceinline__ SoftmaxMax softmax_max(const v16f& s0, const v16f& s1, float& m_run,
                                                   float c, float tau) {
   // max3 tree over the 32 scores (32 -> 11 -> 4 -> 1): depth 4 instead of
@@ -154,7 +161,14 @@ __device__ __forceinline__ SoftmaxMax softmax_max(const v16f& s0, const v16f& s1
   const float rmc = max_with_half_swap(x.bmc);
   const float m_new = rmc > m_run + tau ? rmc : m_run;
   x.m_use = m_new == -INFINITY ? 0.0f : m_new;
-  x.alpha = fast_exp2(m_run - x.m_use);
+  if constexpr (kLazyAlpha) {
+    x.moved = __any(m_new != m_run);
+    x.alpha = 1.0f;
+    if (x.moved) x.alpha = fast_exp2(m_run - x.m_use);
+  } else {
+    x.moved = true;
+    x.alpha = fast_exp2(m_run - x.m_use);
+  }
   m_run = m_new;
   return x;
 }
@@ -991,6 +1005,14 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
   // product itself starting from zero every step: the live state fits two
   // waves per SIMD without spills.
   float l2 = 0.0f;
+  // The lane's V operand and V scale bytes in ring stage 0 (channel tile 0):
+  // every other stage and channel tile is a compile-time offset from them,
+  // which the LDS reads take as immediates (the V ring lies above 64 KB of LDS
+  // at d = 256, out of reach of an immediate offset from address 0; written
+  // as one expression per read, the compiler had kept one address register
+  // per channel tile and added the stage base each step).
+  const uint8_t* v_op0 = lds_v + (h * D + n) * 16;
+  const uint8_t* v_sc0 = lds_v + T::VS_OFF + h * D + n;
   auto step2 = [&](auto ring, int kt, v16f& s0, v16f& s1) {
     // row 32 + n's chunk swizzle is row n's XOR 4 at d = 256 and the same at
     // d = 64 / 128 (k_swz), so its chunk 2j + h is row n's chunk 2 (j ^ KX) + h
@@ -1010,23 +1032,24 @@ __global__ __launch_bounds__(256, prefill_min_blocks<D>()) void attn_prefill_ker
     // Llama-3.1-8B-shaped layers 211.8 / 150.8 -> 208.1 / 147.2 us).
     if (do_sm) {
       if (n0 + kBN > wave_full) mask_scores(s0, s1, n0 + 32 * h, row_lim);
-      const SoftmaxMax sx = softmax_max(s0, s1, m_run, c, a.tau);
-      uint4 pz = make_uint4(0, 0, 0, 0);
+      const SoftmaxMax sx = softmax_max<true>(s0, s1, m_run, c, a.tau);
+      // the packing register: the converts overwrite every byte of it, so it
+      // starts from whatever the registers hold (no zeroing moves)
+      uint4 pz;
+      asm volatile("" : "=v"(pz.x), "=v"(pz.y), "=v"(pz.z), "=v"(pz.w));
       const SoftmaxStep st = softmax_exp(s0, s1, sx, c, a.p_bias, pz);
       if constexpr (kDirect) l_direct = __builtin_fmaf(l_direct, st.alpha, row_sum_p(s0, s1));
-      if (kt != 0 && __any(st.alpha != 1.0f)) {
+      if (kt != 0 && sx.moved) {
 #pragma unroll
         for (int cc = 0; cc < NC; cc++) acc[cc] *= st.alpha;
         l2 *= st.alpha;
       }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
-      const uint8_t* vbuf = lds_v + RP * T::V_BYTES;
 #pragma unroll
       for (int cc = 0; cc < NC; cc++) {
-        const int ch = 32 * cc + n;
-        const uint4 va = *reinterpret_cast<const uint4*>(vbuf + (h * D + ch) * 16);
-        const int vs = vbuf[T::VS_OFF + h * D + ch];
+        const uint4 va = *reinterpret_cast<const uint4*>(v_op0 + RP * T::V_BYTES + cc * 512);
+        const int vs = v_sc0[RP * T::V_BYTES + cc * 32];
         acc[cc] = mfma_fp4_32x32x64(va, st.p_codes, acc[cc], vs, st.p_scale);
       }
       if constexpr (!kDirect) {
