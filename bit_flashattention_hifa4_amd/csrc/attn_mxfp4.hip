@@ -547,7 +547,7 @@ __device__ __forceinline__ void v_load(const uint8_t* vbuf, int n, int h, VOps<D
   }
 }
 
-// Workgroups per compute unit (= waves per SIMD): three at d = 128 (158
+// Workgroups per compute unit (= waves per SIMD): three at d = 128 (154
 // VGPRs, 34 KB of LDS each), two at d = 64 and d = 256 (the 32 x 256
 // accumulator tile alone is 128 registers a lane).
 template <int D>
