@@ -646,6 +646,10 @@ def main():
         "quantize_kv_gbs": P.q_bytes / (q_ms.mean() * 1e-3) / 1e9,
         "flops_per_step": P.flops,
         "mfma_fp4_measured_tflops": mfma_tf,
+        # the clock at which a full-rate FP4 MFMA stream gives the measured rate (the
+        # probe issues independent chains only): the headline fraction against the
+        # observed clock is attention_fraction_of_measured_mfma_rate
+        "clock_implied_by_mfma_probe_ghz": 2.4 * mfma_tf / MXFP4_PEAK_TFLOPS,
         "kernel_source_sha256_16": kernel_source_sha(),
     }
     if not args.no_variants:
